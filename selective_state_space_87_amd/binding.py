@@ -1,0 +1,210 @@
+"""ctypes binding of the C ABI in include/ssm_scan.h.
+
+Argument marshalling only: checks that tensors live on the current HIP device
+with the dtype and layout the ABI documents, allocates outputs and workspace
+with torch, and passes raw device pointers plus torch's current stream to the
+library. Every arithmetic step runs in the library's HIP kernels; there is no
+fallback. A missing library, a CPU tensor or a non-zero status raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libssm_scan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: SSM_F32, torch.bfloat16: SSM_BF16}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class SSMError(RuntimeError):
+    """Non-zero status from the library."""
+
+    def __init__(self, fn, status, message):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library not found at {LIB_PATH}; build it first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        lib.ssm_abi_version.restype = i32
+        lib.ssm_abi_version.argtypes = []
+        lib.ssm_status_string.restype = ctypes.c_char_p
+        lib.ssm_status_string.argtypes = [i32]
+        lib.ssm_scan_workspace_bytes.restype = sz
+        lib.ssm_scan_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        lib.ssm_selective_scan_fwd.restype = i32
+        lib.ssm_selective_scan_fwd.argtypes = [i64, i64, i64, i64, i32, i32, i32,
+                                               vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, vp, vp, sz, vp]
+        lib.ssm_selective_state_update.restype = i32
+        lib.ssm_selective_state_update.argtypes = [i64, i64, i64, i32, i32, i32,
+                                                   vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                   vp, vp]
+        _lib = lib
+        return lib
+
+
+def library():
+    """The loaded ctypes library (loads it on first call)."""
+    return _load()
+
+
+def _check(fn, status):
+    if status != 0:
+        msg = _load().ssm_status_string(status).decode()
+        raise SSMError(fn, status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_tensor(name, t, shape, dtypes, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device}); there is no CPU path")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (dense row-major)")
+    return t
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def ssm_abi_version() -> int:
+    return int(_load().ssm_abi_version())
+
+
+def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate) -> int:
+    return int(_load().ssm_scan_workspace_bytes(batch, seqlen, dim, dstate))
+
+
+def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                           delta_softplus=False, h0=None, out_dtype=None,
+                           return_final_state=False, y=None, h_final=None,
+                           workspace=None, stream=None):
+    """Selective scan forward; see ssm_selective_scan_fwd in include/ssm_scan.h.
+
+    u, delta, z: [B, L, d]; B, C: [B, L, N] (all float32 or all bfloat16);
+    A: [d, N], D, delta_bias: [d], h0: [B, d, N] (float32).
+    Returns y ([B, L, d], ``out_dtype`` or the input dtype) or (y, h_final).
+    """
+    lib = _load()
+    if not isinstance(u, torch.Tensor) or u.dim() != 3:
+        raise ValueError("u must be a 3-d tensor [B, L, d]")
+    dev = u.device
+    Bt, L, d = u.shape
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be a 2-d tensor [d, N]")
+    N = A.shape[1]
+    ind = (u.dtype,)
+    if u.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported input dtype {u.dtype}")
+    _dev_tensor("u", u, (Bt, L, d), ind, dev)
+    _dev_tensor("delta", delta, (Bt, L, d), ind, dev)
+    _dev_tensor("A", A, (d, N), (torch.float32,), dev)
+    _dev_tensor("B", B, (Bt, L, N), ind, dev)
+    _dev_tensor("C", C, (Bt, L, N), ind, dev)
+    _dev_tensor("D", D, (d,), (torch.float32,), dev)
+    _dev_tensor("z", z, (Bt, L, d), ind, dev)
+    _dev_tensor("delta_bias", delta_bias, (d,), (torch.float32,), dev)
+    _dev_tensor("h0", h0, (Bt, d, N), (torch.float32,), dev)
+    out_dtype = u.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    if y is None:
+        y = torch.empty((Bt, L, d), dtype=out_dtype, device=dev)
+    _dev_tensor("y", y, (Bt, L, d), (out_dtype,), dev)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((Bt, d, N), dtype=torch.float32, device=dev)
+    _dev_tensor("h_final", h_final, (Bt, d, N), (torch.float32,), dev)
+    ws_bytes = int(lib.ssm_scan_workspace_bytes(Bt, L, d, N))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+        ws_size = workspace.numel() * workspace.element_size()
+    else:
+        ws_size = 0
+    with torch.cuda.device(dev):
+        st = lib.ssm_selective_scan_fwd(
+            Bt, L, d, N, _DTYPE_CODE[u.dtype], _DTYPE_CODE[out_dtype], int(bool(delta_softplus)),
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), ws_size, _stream_handle(stream, dev))
+    _check("ssm_selective_scan_fwd", st)
+    if return_final_state or h_final is not None:
+        return y, h_final
+    return y
+
+
+def ssm_selective_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                               delta_softplus=False, out_dtype=None, y=None, stream=None):
+    """One decode step in place on ``state``; see ssm_selective_state_update in include/ssm_scan.h.
+
+    state: [B, d, N] float32 (updated in place); x, delta, z: [B, d]; B, C: [B, N]
+    (all float32 or all bfloat16); A: [d, N], D, delta_bias: [d] float32.
+    Returns y [B, d].
+    """
+    lib = _load()
+    if not isinstance(state, torch.Tensor) or state.dim() != 3:
+        raise ValueError("state must be a 3-d tensor [B, d, N]")
+    dev = state.device
+    Bt, d, N = state.shape
+    if not isinstance(x, torch.Tensor) or x.dtype not in _DTYPE_CODE:
+        raise ValueError("x must be a float32 or bfloat16 tensor")
+    ind = (x.dtype,)
+    _dev_tensor("state", state, (Bt, d, N), (torch.float32,), dev)
+    _dev_tensor("x", x, (Bt, d), ind, dev)
+    _dev_tensor("delta", delta, (Bt, d), ind, dev)
+    _dev_tensor("A", A, (d, N), (torch.float32,), dev)
+    _dev_tensor("B", B, (Bt, N), ind, dev)
+    _dev_tensor("C", C, (Bt, N), ind, dev)
+    _dev_tensor("D", D, (d,), (torch.float32,), dev)
+    _dev_tensor("z", z, (Bt, d), ind, dev)
+    _dev_tensor("delta_bias", delta_bias, (d,), (torch.float32,), dev)
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    if y is None:
+        y = torch.empty((Bt, d), dtype=out_dtype, device=dev)
+    _dev_tensor("y", y, (Bt, d), (out_dtype,), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssm_selective_state_update(
+            Bt, d, N, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype], int(bool(delta_softplus)),
+            _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), _ptr(y), _stream_handle(stream, dev))
+    _check("ssm_selective_state_update", st)
+    return y
