@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark: selective scan throughput on one MI355X, plus the decode state update.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one selective scan (all of: load/convert, softplus step size,
+discretise, recurrence, readout, D skip, silu gate, bf16 store, final state)
+over the Mamba-1.4B-shaped layer: B=4, L=8192, d_inner=4096, N=16, bf16
+u/delta/B/C/z, float32 A/D/state, bf16 y, h_final exported. Inputs are
+synthetic (seeded, see selective_state_space_87_amd/synth.py) and resident in
+HBM before the timed region. Prints one JSON line.
+
+Also reported in the same line: the scan kernel's roofline (VALU-bound: the
+transition needs one transcendental per state update), the float64 CPU
+oracle timed on a bounded sample of the same workload, and the decode state
+update (128 x 4096 x 128 float32 state, 1000 chained steps).
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scan G state-updates/s (B·L·d·N) + % HBM/VALU roofline, 1 MI355X"
+UNIT = "G state-updates/s"
+
+# MI355X constants (vendor figures): 256 CUs at 2.4 GHz, 8.0 TB/s HBM3E.
+CUS, CLOCK_HZ, HBM_BPS = 256, 2.4e9, 8.0e12
+# VALU issue model of gfx950: 4 SIMD x 16 lanes = 64 lane-slots per clock per CU
+# for full-rate fp32 ops; transcendentals (exp, log, rcp) take 2 slots (half rate,
+# no co-issue with FMA-pipe ops). Packed fp32 is not used.
+SLOTS_PER_CLK_CU = 64
+VALU_PEAK_SLOTS = CUS * SLOTS_PER_CLK_CU * CLOCK_HZ          # 3.93e13 lane-slots/s
+TRANS_SLOTS = 2
+# Algorithmic VALU work of the method (not of any implementation):
+#   per state update (b,l,d,n): exp(dt*A) [trans], dt*A, (dt*u)*B, Abar*h + .., C*h + ..
+#   per (b,l,d): softplus = exp, log [2 trans] + 2 adds; dt*u; D*u + y;
+#                silu gate = exp, rcp [2 trans] + add, mul z, mul y.
+SLOTS_PER_UPDATE = TRANS_SLOTS + 4
+SLOTS_PER_BLD = 4 * TRANS_SLOTS + 2 + 1 + 1 + 3
+
+
+def scan_alg_bytes(B, L, d, N, in_bytes, out_bytes, final_state):
+    """Algorithmic HBM bytes of one scan: each input read once, each output written once."""
+    b = B * L * d * in_bytes * 3            # u, delta, z
+    b += B * L * N * in_bytes * 2           # B, C
+    b += d * N * 4 + d * 4 * 2              # A, D, delta_bias
+    b += B * L * d * out_bytes              # y
+    if final_state:
+        b += B * d * N * 4                  # h_final
+    return b
+
+
+def decode_alg_bytes(B, d, N, in_bytes=4, out_bytes=4):
+    state = 2 * B * d * N * 4
+    return state, state + B * d * in_bytes * 3 + B * d * out_bytes + 2 * B * N * in_bytes + d * N * 4 + 2 * d * 4
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_87_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(profile_name, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (same source hash); else None."""
+    p = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m_hash and m_b) or m_hash.group(1) != src_hash:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(inp, sample_steps):
+    """The float64 oracle, as it stands, on the first `sample_steps` time steps
+    of the same workload (all batches, channels and states)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from selective_state_space_87_amd import synth
+
+    dt = inp["in_dtype"]
+    S = min(sample_steps, inp["u"].shape[1])
+    sl = {k: synth.to_float64(np.ascontiguousarray(inp[k][:, :S]), dt) for k in ("u", "delta", "B", "C", "z")}
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.selective_scan(sl["u"], sl["delta"], inp["A"].astype(np.float64), sl["B"], sl["C"],
+                              D=inp["D"].astype(np.float64), z=sl["z"],
+                              delta_bias=inp["delta_bias"].astype(np.float64), delta_softplus=True)
+        t = time.perf_counter() - t0
+    Bt, _, d = inp["u"].shape
+    N = inp["A"].shape[1]
+    ups = Bt * S * d * N
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": ups / t / 1e9, "unit": UNIT, "cores": 1, "kind": "oracle",
+            "sample": f"float64 NumPy oracle, first {S} of {inp['u'].shape[1]} time steps of the same "
+                      f"workload (B={Bt}, d={d}, N={N}; {ups:.3e} state updates) in {t:.1f} s on one "
+                      f"thread of {cpu}"}
+
+
+def bench_scan(args, torch, binding, synth):
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.workload_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    dt = inp["in_dtype"]
+
+    def up(a, kind):
+        import numpy as np
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t = {k: up(inp[k], dt) for k in ("u", "delta", "B", "C", "z")}
+    for k in ("A", "D", "delta_bias"):
+        t[k] = up(inp[k], "f32")
+    out_dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    y = torch.empty(w.batch, w.seqlen, w.dim, dtype=out_dtype, device=dev)
+    hf = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
+
+    def step():
+        binding.ssm_selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                       delta_bias=t["delta_bias"], delta_softplus=True, y=y,
+                                       h_final=hf if w.final_state else None, out_dtype=out_dtype)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Cold-cache kernel time: flush the 256 MB MALL and the L2s before each launch.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(3):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    return w, inp, wall_ms, kern_ms, sorted(cold)[1]
+
+
+def bench_decode(args, torch, binding, synth):
+    w = synth.WORKLOADS[4]
+    d = synth.workload_inputs(4)
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(d[k]).to(dev) for k in ("state", "x", "delta", "B", "C", "z", "A", "D", "delta_bias")}
+    y = torch.empty(w.batch, w.dim, dtype=torch.float32, device=dev)
+
+    def step():
+        binding.ssm_selective_state_update(t["state"], t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"],
+                                           z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True, y=y)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.decode_steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+    state_b, alg_b = decode_alg_bytes(w.batch, w.dim, w.dstate)
+    gbs = alg_b / (us * 1e-6) / 1e9
+    return {
+        "workload": f"{w.name} (batch={w.batch}, d_inner={w.dim}, N={w.dstate}, f32, "
+                    f"{args.decode_steps} chained steps, same token)",
+        "us_per_step": us,
+        "state_GBps": state_b / (us * 1e-6) / 1e9,
+        "G_updates_per_s": w.batch * w.dim * w.dstate / (us * 1e-6) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_BPS / 1e9, "unit": "GB/s",
+                     "frac": gbs / (HBM_BPS / 1e9), "traffic": None,
+                     "alg_bytes_per_launch": alg_b},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3])
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-steps", type=int, default=8192)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world > 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+                  "the scan shards channels with no communication, so only the one-GPU figure is measured.",
+                  flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_87_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+
+    w, inp, wall_ms, kern_ms, cold_ms = bench_scan(args, torch, binding, synth)
+    ups = w.updates
+    value = ups / (wall_ms * 1e-3) / 1e9
+    in_b = 2 if w.in_dtype == "bf16" else 4
+    alg_bytes = scan_alg_bytes(w.batch, w.seqlen, w.dim, w.dstate, in_b, in_b, w.final_state)
+    bld = w.batch * w.seqlen * w.dim
+    alg_slots = ups * SLOTS_PER_UPDATE + bld * SLOTS_PER_BLD
+    achieved = alg_slots / (kern_ms * 1e-3) / 1e12
+    peak = VALU_PEAK_SLOTS / 1e12
+    src_hash = kernel_source_hash()
+    traffic = counter_traffic("scan_fwd_mamba14b_counters.md", src_hash)
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "d_inner": w.dim,
+                   "d_state": w.dstate, "storage_dtype": w.in_dtype, "state_dtype": "f32",
+                   "out_dtype": w.in_dtype, "delta_softplus": True, "gate": w.gate,
+                   "final_state": w.final_state},
+        "kernel_ms": kern_ms,
+        "cold_kernel_ms": cold_ms,
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "Tslot/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "alg_slots_per_launch": alg_slots, "alg_bytes_per_launch": alg_bytes,
+                     "hbm_GBps": alg_bytes / (kern_ms * 1e-3) / 1e9,
+                     "hbm_frac": alg_bytes / (kern_ms * 1e-3) / HBM_BPS,
+                     "source_hash": src_hash},
+    }
+    if not args.no_decode:
+        result["decode"] = bench_decode(args, torch, binding, synth)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_steps)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * ssm_scan.h — C ABI of the MI355X (gfx950) selective state-space scan library
+ * (libssm_scan.so).
+ *
+ * What it computes, per batch b, channel d (of `dim`), state n (of `dstate`),
+ * time step l (of `seqlen`):
+ *
+ *   dt      = softplus(delta[b,l,d] + delta_bias[d])   (or no softplus)
+ *   h[n]    = exp(dt * A[d,n]) * h[n] + dt * B[b,l,n] * u[b,l,d]
+ *   y[b,l,d] = (sum_n C[b,l,n] * h[n] + D[d] * u[b,l,d]) * silu(z[b,l,d])
+ *
+ * Sources (page title and section; the same pages throughout this library):
+ *   - "从 Transformer 到 Mamba：状态空间模型如何重塑序列计算的效率边界" (ybb.press):
+ *     section 2 (discrete recurrence), section 3 (input-dependent delta, B, C;
+ *     softplus), section 3.1 (the selective_scan(u, delta, A, B, C, D)
+ *     statement, shapes and discretisation), section 5 (SelectiveScan loop,
+ *     step-size bias before softplus, D skip, MambaBlock gate), section 6.3
+ *     (decode: fixed work per token, state in, new state out).
+ *   - "Mamba" study notes (lyirs.cc): "Selective State Space" (y_t = C_t h_t +
+ *     D x_t), "block structure" (gate branch), and the fixed-size ssm_state
+ *     kept between tokens.
+ *   - "Mamba架构：突破Transformer瓶颈的序列建模新范式" (intelliparadigm.com),
+ *     section 6.2: very long sequences are processed in chunks with the state
+ *     carried from chunk to chunk (h0 in, h_final out).
+ *
+ * Readings where the pages disagree: the transition is exp(dt * A) with A <= 0
+ * passed in directly (not A_log, and no extra minus sign); the input term is
+ * dt * B * u; the gate multiplies after the D skip.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     dense row-major with the shapes given. The caller owns every buffer; the
+ *     library never allocates, frees or synchronises, and keeps no mutable
+ *     global state.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work
+ *     and return at once; a status of 0 means the launch was accepted.
+ *   - dtype codes: 0 = float32, 1 = bfloat16. u, delta, B, C and z share
+ *     `in_dtype`; y has `out_dtype`; A, D, delta_bias, h0, h_final and the
+ *     decode state are always float32. bfloat16 outputs round to nearest even.
+ *   - Optional pointers may be NULL: D (= 0), z (no gate), delta_bias (= 0),
+ *     h0 (= zero state), h_final (not written).
+ *   - Errors: arguments are validated on the host before anything is launched.
+ *     A failed check returns its status and touches no memory. A launch error
+ *     returns SSM_E_HIP. Nothing throws across the ABI.
+ *   - Alignment: u, delta, z, y, B, C must be 16-byte aligned (SSM_E_ALIGN);
+ *     float32 arrays 4-byte aligned.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+/* Status codes. */
+#define SSM_OK 0
+#define SSM_E_NULLPTR 1     /* a required pointer is NULL                        */
+#define SSM_E_SHAPE 2       /* negative or inconsistent size                     */
+#define SSM_E_DTYPE 3       /* dtype code other than 0 or 1                      */
+#define SSM_E_ALIGN 4       /* pointer not aligned as documented                 */
+#define SSM_E_WORKSPACE 5   /* workspace missing or smaller than required        */
+#define SSM_E_ALIAS 6       /* an output overlaps an input it may not overlap    */
+#define SSM_E_UNSUPPORTED 7 /* dstate outside the supported range                */
+#define SSM_E_HIP 8         /* the HIP runtime reported an error at launch       */
+
+/* Version of this ABI (SSM_ABI_VERSION of the header the library was built from). */
+int ssm_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* ssm_status_string(int status);
+
+/*
+ * Bytes of device workspace ssm_selective_scan_fwd needs for this shape
+ * (0 when the shape runs without one). The workspace holds, per time chunk,
+ * the chunk's transition product exp(A * sum(dt)) and its zero-start end
+ * state, both [B, d, N] float32, so chunks can run in parallel and be joined
+ * with the associative operator (A_i, b_i) (+) (A_j, b_j) = (A_j A_i,
+ * A_j b_i + b_j) of "Mamba的隐藏代价" (kongchang.com), section on sequential
+ * gradients. It depends only on the four sizes. Returns 0 for invalid sizes.
+ */
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * Selective scan forward (the selective_scan(u, delta, A, B, C, D) statement
+ * of ybb.press section 3.1 with the loop of section 5; gate from section 5's
+ * MambaBlock; h0/h_final per intelliparadigm.com section 6.2).
+ *
+ *   batch, seqlen, dim, dstate : B >= 0, L >= 0, d >= 0, 1 <= N <= 64.
+ *   in_dtype, out_dtype        : 0 float32, 1 bfloat16.
+ *   delta_softplus             : nonzero -> dt = softplus(delta + bias).
+ *   u, delta  [B, L, d]  in_dtype   input and raw step size
+ *   A         [d, N]     float32    diagonal state matrix (expected <= 0)
+ *   B, C      [B, L, N]  in_dtype   input and output projections
+ *   D         [d]        float32    skip (optional)
+ *   z         [B, L, d]  in_dtype   gate branch (optional)
+ *   delta_bias[d]        float32    step-size bias (optional)
+ *   h0        [B, d, N]  float32    initial state (optional)
+ *   y         [B, L, d]  out_dtype  output; must not overlap any input
+ *   h_final   [B, d, N]  float32    final state (optional); may equal h0
+ *   workspace, workspace_bytes      device scratch of at least
+ *                                   ssm_scan_workspace_bytes() bytes (may be
+ *                                   NULL when that is 0)
+ *   stream                          hipStream_t
+ *
+ * L = 0 writes h_final = h0 (or zeros) and nothing else. Results are
+ * bitwise deterministic from run to run (fixed combine order, no atomics on
+ * floating-point data). NaN/Inf propagate without clamping.
+ */
+int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           int in_dtype, int out_dtype, int delta_softplus,
+                           const void* u, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, const float* h0,
+                           void* y, float* h_final,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode: one token's state update in place (ybb.press section 6.3; the
+ * fixed-size ssm_state of the lyirs.cc notes). The step is the scan's step
+ * for L = 1 with h0 = state and h_final = state:
+ *
+ *   batch, dim, dstate         : B >= 0, d >= 0, 1 <= N <= 256.
+ *   state     [B, d, N]  float32    read, then overwritten with the new state
+ *   x, delta  [B, d]     in_dtype   token input and raw step size
+ *   A         [d, N]     float32
+ *   B, C      [B, N]     in_dtype
+ *   D         [d]        float32    (optional)
+ *   z         [B, d]     in_dtype   gate branch (optional)
+ *   delta_bias[d]        float32    (optional)
+ *   y         [B, d]     out_dtype  output; must not overlap state or inputs
+ *   stream                          hipStream_t
+ */
+int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
+                               int in_dtype, int out_dtype, int delta_softplus,
+                               float* state, const void* x, const void* delta,
+                               const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias,
+                               void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

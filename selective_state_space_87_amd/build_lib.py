@@ -1,0 +1,67 @@
+"""Build libssm_scan.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m selective_state_space_87_amd.build_lib
+
+Objects go to _build/ at the repository root; the library to
+selective_state_space_87_amd/lib/libssm_scan.so. Always recompiles.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIBDIR = os.path.join(PKG, "lib")
+LIB = os.path.join(LIBDIR, "libssm_scan.so")
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Packed FP32 (v_pk_*_f32) is switched off for all device code.
+DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-I", os.path.join(ROOT, "include")]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
+
+DEVICE_SOURCES = ["scan_fwd.hip", "state_update.hip"]
+HOST_SOURCES = ["api.cpp"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops" not in l and "not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    jobs = []
+    for s in DEVICE_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        jobs.append(([HIPCC] + DEVICE_FLAGS + ["-c", os.path.join(CSRC, s), "-o", o], o))
+    for s in HOST_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        jobs.append(([HIPCC] + HOST_FLAGS + ["-c", os.path.join(CSRC, s), "-o", o], o))
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + [o for _, o in jobs]
+         + ["-Wl,-soname,libssm_scan.so"], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

@@ -1,0 +1,208 @@
+// C-ABI front end of libssm_scan.so: host-side validation, then dispatch to
+// the kernel launchers. Every check runs before anything touches the device,
+// so an invalid call returns a status without side effects (and without a
+// HIP device being present at all).
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <limits>
+
+#include "../../include/ssm_scan.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxScanState = 64;
+constexpr int64_t kMaxDecodeState = 256;
+constexpr int64_t kMaxElems = int64_t(1) << 52;
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Range span(const void* p, int64_t elems, int64_t elem_bytes) {
+  Range r;
+  if (p == nullptr || elems <= 0) return r;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + static_cast<uintptr_t>(elems * elem_bytes);
+  return r;
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool safe_mul(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > kMaxElems / a) return false;
+  *out = a * b;
+  return *out <= kMaxElems;
+}
+
+int map_hip(int err) { return err == 0 ? SSM_OK : SSM_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(int status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_E_NULLPTR: return "a required pointer is NULL";
+    case SSM_E_SHAPE: return "negative, overflowing or inconsistent size";
+    case SSM_E_DTYPE: return "dtype code must be 0 (float32) or 1 (bfloat16)";
+    case SSM_E_ALIGN: return "pointer not aligned as documented";
+    case SSM_E_WORKSPACE: return "workspace missing or smaller than ssm_scan_workspace_bytes()";
+    case SSM_E_ALIAS: return "an output overlaps an input it may not overlap";
+    case SSM_E_UNSUPPORTED: return "dstate outside the supported range";
+    case SSM_E_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > kMaxScanState) return 0;
+  int64_t t;
+  if (!safe_mul(batch, seqlen, &t) || !safe_mul(t, dim, &t)) return 0;
+  return ssm::scan_workspace_bytes(batch, seqlen, dim, dstate);
+}
+
+int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           int in_dtype, int out_dtype, int delta_softplus,
+                           const void* u, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, const float* h0,
+                           void* y, float* h_final,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
+  if (dstate > kMaxScanState) return SSM_E_UNSUPPORTED;
+  if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return SSM_E_DTYPE;
+  int64_t bl, bld, bln, bdn, dn;
+  if (!safe_mul(batch, seqlen, &bl) || !safe_mul(bl, dim, &bld) || !safe_mul(bl, dstate, &bln) ||
+      !safe_mul(batch, dim, &bdn) || !safe_mul(bdn, dstate, &bdn) || !safe_mul(dim, dstate, &dn)) {
+    return SSM_E_SHAPE;
+  }
+  if (batch == 0 || dim == 0) return SSM_OK;  // no channel: nothing to compute or write
+  const int64_t isz = in_dtype == 1 ? 2 : 4, osz = out_dtype == 1 ? 2 : 4;
+  if (A == nullptr) return SSM_E_NULLPTR;
+  if (seqlen > 0 && (u == nullptr || delta == nullptr || B == nullptr || C == nullptr || y == nullptr)) {
+    return SSM_E_NULLPTR;
+  }
+  const void* vec_ptrs[] = {u, delta, B, C, z, y};
+  for (const void* p : vec_ptrs) {
+    if (p && !aligned(p, 16)) return SSM_E_ALIGN;
+  }
+  const void* f32_ptrs[] = {A, D, delta_bias, h0, h_final};
+  for (const void* p : f32_ptrs) {
+    if (p && !aligned(p, 4)) return SSM_E_ALIGN;
+  }
+  const size_t need = ssm::scan_workspace_bytes(batch, seqlen, dim, dstate);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SSM_E_WORKSPACE;
+
+  const Range ry = span(y, seqlen > 0 ? bld : 0, osz);
+  const Range rhf = span(h_final, bdn, 4);
+  const Range rh0 = span(h0, bdn, 4);
+  const Range inputs[] = {span(u, bld, isz), span(delta, bld, isz), span(z, bld, isz),
+                          span(B, bln, isz), span(C, bln, isz), span(A, dn, 4),
+                          span(D, dim, 4), span(delta_bias, dim, 4), rh0};
+  for (const Range& r : inputs) {
+    if (overlaps(ry, r)) return SSM_E_ALIAS;
+  }
+  if (overlaps(ry, rhf)) return SSM_E_ALIAS;
+  for (int i = 0; i < 8; ++i) {  // h_final may equal h0 exactly, nothing else
+    if (overlaps(rhf, inputs[i])) return SSM_E_ALIAS;
+  }
+  if (overlaps(rhf, rh0) && !(rhf.lo == rh0.lo && rhf.hi == rh0.hi)) return SSM_E_ALIAS;
+  const Range rws = span(workspace, need > 0 ? static_cast<int64_t>(need) : 0, 1);
+  for (const Range& r : inputs) {
+    if (overlaps(rws, r)) return SSM_E_ALIAS;
+  }
+  if (overlaps(rws, ry) || overlaps(rws, rhf)) return SSM_E_ALIAS;
+
+  ssm::ScanArgs a;
+  a.u = u;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.z = z;
+  a.delta_bias = delta_bias;
+  a.h0 = h0;
+  a.y = y;
+  a.h_final = h_final;
+  a.workspace = workspace;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.dim = dim;
+  a.dstate = dstate;
+  a.in_bf16 = in_dtype;
+  a.out_bf16 = out_dtype;
+  a.delta_softplus = delta_softplus ? 1 : 0;
+  return map_hip(ssm::launch_scan(a, stream));
+}
+
+int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
+                               int in_dtype, int out_dtype, int delta_softplus,
+                               float* state, const void* x, const void* delta,
+                               const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias,
+                               void* y, void* stream) {
+  if (batch < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
+  if (dstate > kMaxDecodeState) return SSM_E_UNSUPPORTED;
+  if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return SSM_E_DTYPE;
+  int64_t bd, bdn, bn, dn;
+  if (!safe_mul(batch, dim, &bd) || !safe_mul(bd, dstate, &bdn) || !safe_mul(batch, dstate, &bn) ||
+      !safe_mul(dim, dstate, &dn)) {
+    return SSM_E_SHAPE;
+  }
+  if (bd == 0) return SSM_OK;
+  if (state == nullptr || x == nullptr || delta == nullptr || A == nullptr || B == nullptr ||
+      C == nullptr || y == nullptr) {
+    return SSM_E_NULLPTR;
+  }
+  const void* vec_ptrs[] = {x, delta, B, C, z, y};
+  for (const void* p : vec_ptrs) {
+    if (p && !aligned(p, 16)) return SSM_E_ALIGN;
+  }
+  const void* f32_ptrs[] = {state, A, D, delta_bias};
+  for (const void* p : f32_ptrs) {
+    if (p && !aligned(p, 4)) return SSM_E_ALIGN;
+  }
+  const int64_t isz = in_dtype == 1 ? 2 : 4, osz = out_dtype == 1 ? 2 : 4;
+  const Range rs = span(state, bdn, 4);
+  const Range ry = span(y, bd, osz);
+  const Range inputs[] = {span(x, bd, isz), span(delta, bd, isz), span(z, bd, isz),
+                          span(B, bn, isz), span(C, bn, isz), span(A, dn, 4),
+                          span(D, dim, 4), span(delta_bias, dim, 4)};
+  for (const Range& r : inputs) {
+    if (overlaps(ry, r) || overlaps(rs, r)) return SSM_E_ALIAS;
+  }
+  if (overlaps(ry, rs)) return SSM_E_ALIAS;
+
+  ssm::UpdateArgs a;
+  a.state = state;
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.z = z;
+  a.delta_bias = delta_bias;
+  a.y = y;
+  a.batch = batch;
+  a.dim = dim;
+  a.dstate = dstate;
+  a.in_bf16 = in_dtype;
+  a.out_bf16 = out_dtype;
+  a.delta_softplus = delta_softplus ? 1 : 0;
+  return map_hip(ssm::launch_state_update(a, stream));
+}
+
+}  // extern "C"

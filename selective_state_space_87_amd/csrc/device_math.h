@@ -1,0 +1,135 @@
+// Device-side helpers shared by the scan and decode kernels (gfx950).
+//
+// Element functions of the selective scan, written for the CDNA4 VALU:
+// exp and log go through the hardware base-2 transcendentals (v_exp_f32,
+// v_log_f32, v_rcp_f32), which issue at half the FMA rate on gfx950.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
+// log1p(v) is taken as v * ln(w) / (w - 1) with w = fl(1 + v): the rounding
+// of w cancels between numerator and denominator, so small v keeps full
+// relative accuracy (a plain log(1 + v) would lose it for v << 1, which is
+// exactly the small-step regime). w - 1 is exact for w in [1, 2].
+__device__ __forceinline__ float softplus_f(float x) {
+  const float v = exp2_hw(-fabsf(x) * kLog2e);
+  const float w = 1.0f + v;
+  const float dw = w - 1.0f;
+  const float lp = (dw == 0.0f) ? v : (log2_hw(w) * kLn2) * (v * rcp_hw(dw));
+  return fmaxf(x, 0.0f) + lp;
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z).
+__device__ __forceinline__ float silu_f(float z) {
+  return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  const __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if constexpr (BF16) {
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+  } else {
+    return static_cast<const float*>(p)[i];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
+  if constexpr (BF16) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
+  } else {
+    static_cast<float*>(p)[i] = v;
+  }
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// ---- cross-lane moves inside groups of 1, 2 or 4 consecutive lanes (DPP quad_perm)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+
+// Value of lane K of this lane's group of G consecutive lanes.
+template <int G, int K>
+__device__ __forceinline__ float group_bcast(float v) {
+  static_assert(G == 1 || G == 2 || G == 4, "group of 1, 2 or 4 lanes");
+  if constexpr (G == 1) {
+    return v;
+  } else if constexpr (G == 2) {
+    return dpp_f<quad_perm(K, K, 2 + K, 2 + K)>(v);
+  } else {
+    return dpp_f<quad_perm(K, K, K, K)>(v);
+  }
+}
+
+template <int MASK>
+__device__ __forceinline__ float quad_xor(float v) {
+  static_assert(MASK == 1 || MASK == 2, "xor 1 or 2 inside a quad");
+  if constexpr (MASK == 1) {
+    return dpp_f<quad_perm(1, 0, 3, 2)>(v);
+  } else {
+    return dpp_f<quad_perm(2, 3, 0, 1)>(v);
+  }
+}
+
+// Transposed reduction over a group of G lanes: on entry lane j of the group
+// holds partial sums p[0..G-1] (one per time step of the group); on exit it
+// returns the group-wide sum of p[j]. Butterfly: at each level a lane keeps
+// the half of its vector whose index bit matches its own lane bit and adds
+// the partner's copy of that half.
+template <int G>
+__device__ __forceinline__ float group_transpose_sum(const float (&p)[G], int j) {
+  if constexpr (G == 1) {
+    return p[0];
+  } else if constexpr (G == 2) {
+    const bool hi = j & 1;
+    const float keep = hi ? p[1] : p[0];
+    const float send = hi ? p[0] : p[1];
+    return keep + quad_xor<1>(send);
+  } else {
+    static_assert(G == 4, "group of 1, 2 or 4 lanes");
+    const bool b1 = j & 2;
+    const float k0 = b1 ? p[2] : p[0], s0 = b1 ? p[0] : p[2];
+    const float k1 = b1 ? p[3] : p[1], s1 = b1 ? p[1] : p[3];
+    const float q0 = k0 + quad_xor<2>(s0);
+    const float q1 = k1 + quad_xor<2>(s1);
+    const bool b0 = j & 1;
+    const float k = b0 ? q1 : q0, s = b0 ? q0 : q1;
+    return k + quad_xor<1>(s);
+  }
+}
+
+}  // namespace ssm

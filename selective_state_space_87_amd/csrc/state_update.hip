@@ -1,0 +1,128 @@
+// Decode: one token's selective state update, in place, for gfx950.
+//
+// Per (b, d, n) ("从 Transformer 到 Mamba", ybb.press, section 6.3: fixed work
+// per token, old state and token in, new state out; the step is the scan's
+// step of section 5 for a single token):
+//   dt = softplus(delta + bias);  s[n] = exp(dt*A[n]) s[n] + dt*B[n]*x
+//   y  = (sum_n C[n] s[n] + D x) * silu(z)
+//
+// The state [B, d, N] float32 is read once and written once: the kernel is a
+// streaming read-modify-write bound by HBM. A row (b, d) is owned by R lanes
+// of one wave, each holding V consecutive states (V = 4 when N % 4 == 0, a
+// 16-byte nontemporal load and store); the row's readout is summed across
+// those lanes with xor shuffles inside the wave.
+#include <hip/hip_runtime.h>
+
+#include "device_math.h"
+#include "kernels.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kThreads = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int V, int R, bool BF16_IN, bool BF16_OUT>
+__global__ __launch_bounds__(kThreads) void state_update_kernel(const UpdateArgs a) {
+  constexpr int RPB = kThreads / R;  // rows per block
+  const int tid = threadIdx.x;
+  const int j = tid % R;
+  const int64_t rows = a.batch * a.dim, N = a.dstate;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + tid / R;
+  const bool ok = row < rows;
+  const int64_t b = ok ? row / a.dim : 0;
+  const int64_t ch = ok ? row % a.dim : 0;
+
+  const float x = ok ? load_elem<BF16_IN>(a.x, row) : 0.0f;
+  const float dr = ok ? load_elem<BF16_IN>(a.delta, row) : 0.0f;
+  const float zz = (ok && a.z) ? load_elem<BF16_IN>(a.z, row) : 0.0f;
+  const float bias = (ok && a.delta_bias) ? a.delta_bias[ch] : 0.0f;
+  float dt = dr + bias;
+  if (a.delta_softplus) dt = softplus_f(dt);
+  dt = ok ? dt : 0.0f;
+  const float du = dt * x;
+
+  float acc = 0.0f;
+  for (int64_t n0 = static_cast<int64_t>(j) * V; n0 < N; n0 += static_cast<int64_t>(R) * V) {
+    if (!ok) continue;
+    if constexpr (V == 4) {
+      f32x4* sp = reinterpret_cast<f32x4*>(a.state + row * N + n0);
+      f32x4 s = __builtin_nontemporal_load(sp);
+      const f32x4 av = *reinterpret_cast<const f32x4*>(a.A + ch * N + n0);
+      float bv[4], cv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        bv[v] = load_elem<BF16_IN>(a.B, b * N + n0 + v);
+        cv[v] = load_elem<BF16_IN>(a.C, b * N + n0 + v);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float abar = exp2_hw(dt * (av[v] * kLog2e));
+        s[v] = fmaf(abar, s[v], du * bv[v]);
+        acc = fmaf(cv[v], s[v], acc);
+      }
+      __builtin_nontemporal_store(s, sp);
+    } else {
+      float* sp = a.state + row * N + n0;
+      const float abar = exp2_hw(dt * (a.A[ch * N + n0] * kLog2e));
+      const float s = fmaf(abar, *sp, du * load_elem<BF16_IN>(a.B, b * N + n0));
+      *sp = s;
+      acc = fmaf(load_elem<BF16_IN>(a.C, b * N + n0), s, acc);
+    }
+  }
+#pragma unroll
+  for (int m = R / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, R);
+  if (ok && j == 0) {
+    float yv = acc;
+    if (a.D) yv = fmaf(a.D[ch], x, yv);
+    if (a.z) yv *= silu_f(zz);
+    store_elem<BF16_OUT>(a.y, row, yv);
+  }
+}
+
+template <int V, int R, bool BI, bool BO>
+int launch_vr(const UpdateArgs& a, hipStream_t st) {
+  constexpr int RPB = kThreads / R;
+  const int64_t rows = a.batch * a.dim;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  UpdateArgs args = a;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&state_update_kernel<V, R, BI, BO>),
+                         dim3(static_cast<unsigned>(blocks)), dim3(kThreads), kargs, 0, st);
+}
+
+// Lanes per row: enough to cover N with V states each, a power of two <= 64.
+template <int V, bool BI, bool BO>
+int launch_v(const UpdateArgs& a, hipStream_t st) {
+  const int64_t need = (a.dstate + V - 1) / V;
+  if (need <= 1) return launch_vr<V, 1, BI, BO>(a, st);
+  if (need <= 2) return launch_vr<V, 2, BI, BO>(a, st);
+  if (need <= 4) return launch_vr<V, 4, BI, BO>(a, st);
+  if (need <= 8) return launch_vr<V, 8, BI, BO>(a, st);
+  if (need <= 16) return launch_vr<V, 16, BI, BO>(a, st);
+  if (need <= 32) return launch_vr<V, 32, BI, BO>(a, st);
+  return launch_vr<V, 64, BI, BO>(a, st);
+}
+
+// 16-byte state/A accesses need N % 4 == 0 and 16-byte aligned bases.
+template <bool BI, bool BO>
+int launch_io(const UpdateArgs& a, hipStream_t st) {
+  const bool vec4 = a.dstate % 4 == 0 && reinterpret_cast<uintptr_t>(a.state) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(a.A) % 16 == 0;
+  return vec4 ? launch_v<4, BI, BO>(a, st) : launch_v<1, BI, BO>(a, st);
+}
+
+}  // namespace
+
+int launch_state_update(const UpdateArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.batch == 0 || a.dim == 0) return 0;
+  if (a.in_bf16) {
+    return a.out_bf16 ? launch_io<true, true>(a, st) : launch_io<true, false>(a, st);
+  }
+  return a.out_bf16 ? launch_io<false, true>(a, st) : launch_io<false, false>(a, st);
+}
+
+}  // namespace ssm

@@ -24,6 +24,8 @@ The values therefore do not depend on how the caller slices the work.
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -72,8 +74,9 @@ WORKLOADS = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); return uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    out = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    b = x.view(np.uint32)
+    # No overflow for non-NaN inputs: the largest pattern, -inf, is 0xFF800000.
+    out = ((b + np.uint32(0x7FFF) + ((b >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = (x.view(np.uint32)[nan] >> 16).astype(np.uint16) | np.uint16(0x0040)
@@ -98,21 +101,30 @@ def _rng(seed, stream, tid, b=0, block=0):
     return np.random.default_rng([seed, stream, tid, b, block])
 
 
-def _normal_blocks(seed, stream, tid, batch, rows, cols, scale=1.0):
-    """[batch, rows, cols] float32 N(0, scale^2), drawn per (batch, 4096-row block)."""
-    out = np.empty((batch, rows, cols), dtype=np.float32)
-    for b in range(batch):
-        for k in range(0, rows, BLOCK):
-            n = min(BLOCK, rows - k)
-            blk = _rng(seed, stream, tid, b, k // BLOCK).standard_normal((n, cols), dtype=np.float32)
-            if scale != 1.0:
-                blk *= np.float32(scale)
-            out[b, k:k + n] = blk
+def _normal_blocks(seed, stream, tid, batch, rows, cols, scale=1.0, dtype="f32"):
+    """[batch, rows, cols] N(0, scale^2) in storage form, drawn per (batch, 4096-row block).
+
+    Blocks are drawn (and rounded) on a thread pool; each block has its own
+    generator, so the values do not depend on the scheduling.
+    """
+    out = np.empty((batch, rows, cols), dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def one(job):
+        b, k = job
+        n = min(BLOCK, rows - k)
+        blk = _rng(seed, stream, tid, b, k // BLOCK).standard_normal((n, cols), dtype=np.float32)
+        if scale != 1.0:
+            blk *= np.float32(scale)
+        out[b, k:k + n] = f32_to_bf16_bits(blk) if dtype == "bf16" else blk
+
+    jobs = [(b, k) for b in range(batch) for k in range(0, rows, BLOCK)]
+    if len(jobs) == 1 or batch * rows * cols < (1 << 20):
+        for jb in jobs:
+            one(jb)
+    else:
+        with ThreadPoolExecutor(max_workers=min(8, len(jobs), os.cpu_count() or 1)) as ex:
+            list(ex.map(one, jobs))
     return out
-
-
-def _store(x: np.ndarray, dtype: str) -> np.ndarray:
-    return f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
 def delta_bias_for(dim, dt_range, seed, stream):
@@ -136,11 +148,11 @@ def make_scan_inputs(batch, seqlen, dim, dstate, in_dtype="f32", dt_range=(1e-3,
     or bf16 bits (``in_dtype``), and A [d, N], D [d], delta_bias [d] as
     float32. It also carries the keys in_dtype and delta_softplus (True).
     """
-    u = _store(_normal_blocks(seed, stream, TID_U, batch, seqlen, dim), in_dtype)
-    dl = _store(_normal_blocks(seed, stream, TID_DELTA, batch, seqlen, dim), in_dtype)
-    Bm = _store(_normal_blocks(seed, stream, TID_B, batch, seqlen, dstate), in_dtype)
-    Cm = _store(_normal_blocks(seed, stream, TID_C, batch, seqlen, dstate), in_dtype)
-    z = _store(_normal_blocks(seed, stream, TID_Z, batch, seqlen, dim), in_dtype) if gate else None
+    u = _normal_blocks(seed, stream, TID_U, batch, seqlen, dim, dtype=in_dtype)
+    dl = _normal_blocks(seed, stream, TID_DELTA, batch, seqlen, dim, dtype=in_dtype)
+    Bm = _normal_blocks(seed, stream, TID_B, batch, seqlen, dstate, dtype=in_dtype)
+    Cm = _normal_blocks(seed, stream, TID_C, batch, seqlen, dstate, dtype=in_dtype)
+    z = _normal_blocks(seed, stream, TID_Z, batch, seqlen, dim, dtype=in_dtype) if gate else None
     return dict(u=u, delta=dl, B=Bm, C=Cm, z=z,
                 A=s4d_real_A(dim, dstate), D=np.ones(dim, dtype=np.float32),
                 delta_bias=delta_bias_for(dim, dt_range, seed, stream),
@@ -152,11 +164,11 @@ def make_decode_inputs(batch, dim, dstate, in_dtype="f32", dt_range=(1e-3, 1e-1)
     """Decode inputs: state [B, d, N] float32 ~ 0.1 N(0,1); one token x, delta,
     z [B, d] and B, C [B, N] in ``in_dtype``; A, D, delta_bias as for the scan."""
     state = _normal_blocks(seed, stream, TID_STATE, batch, dim, dstate, scale=state_scale)
-    x = _store(_normal_blocks(seed, stream, TID_U, 1, batch, dim)[0], in_dtype)
-    dl = _store(_normal_blocks(seed, stream, TID_DELTA, 1, batch, dim)[0], in_dtype)
-    Bm = _store(_normal_blocks(seed, stream, TID_B, 1, batch, dstate)[0], in_dtype)
-    Cm = _store(_normal_blocks(seed, stream, TID_C, 1, batch, dstate)[0], in_dtype)
-    z = _store(_normal_blocks(seed, stream, TID_Z, 1, batch, dim)[0], in_dtype) if gate else None
+    x = _normal_blocks(seed, stream, TID_U, 1, batch, dim, dtype=in_dtype)[0]
+    dl = _normal_blocks(seed, stream, TID_DELTA, 1, batch, dim, dtype=in_dtype)[0]
+    Bm = _normal_blocks(seed, stream, TID_B, 1, batch, dstate, dtype=in_dtype)[0]
+    Cm = _normal_blocks(seed, stream, TID_C, 1, batch, dstate, dtype=in_dtype)[0]
+    z = _normal_blocks(seed, stream, TID_Z, 1, batch, dim, dtype=in_dtype)[0] if gate else None
     return dict(state=state, x=x, delta=dl, B=Bm, C=Cm, z=z,
                 A=s4d_real_A(dim, dstate), D=np.ones(dim, dtype=np.float32),
                 delta_bias=delta_bias_for(dim, dt_range, seed, stream),
