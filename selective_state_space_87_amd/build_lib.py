@@ -26,7 +26,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-I", os.path.join(ROOT, "include")]
-HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", os.path.join(ROOT, "include")]
+CXX = os.environ.get("CXX_HOST", "g++")
 
 DEVICE_SOURCES = ["scan_fwd.hip", "state_update.hip"]
 HOST_SOURCES = ["api.cpp"]
@@ -51,9 +52,9 @@ def build(verbose: bool = True) -> str:
     for s in DEVICE_SOURCES:
         o = os.path.join(BUILD, s + ".o")
         jobs.append(([HIPCC] + DEVICE_FLAGS + ["-c", os.path.join(CSRC, s), "-o", o], o))
-    for s in HOST_SOURCES:
+    for s in HOST_SOURCES:  # HIP-free host code: the C-ABI validation front end
         o = os.path.join(BUILD, s + ".o")
-        jobs.append(([HIPCC] + HOST_FLAGS + ["-c", os.path.join(CSRC, s), "-o", o], o))
+        jobs.append(([CXX] + HOST_FLAGS + ["-c", os.path.join(CSRC, s), "-o", o], o))
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda j: _run(j[0], verbose), jobs))
     tmp = LIB + ".tmp"

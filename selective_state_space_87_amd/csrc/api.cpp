@@ -1,14 +1,11 @@
 // C-ABI front end of libssm_scan.so: host-side validation, then dispatch to
-// the kernel launchers. Every check runs before anything touches the device,
-// so an invalid call returns a status without side effects (and without a
-// HIP device being present at all).
-#include <hip/hip_runtime_api.h>
-
+// the kernel launchers. Plain C++ (no HIP headers): every check runs before
+// anything touches the device, so an invalid call returns a status without
+// side effects (and without a HIP device being present at all).
 #include <cstdint>
-#include <limits>
 
-#include "../../include/ssm_scan.h"
 #include "kernels.h"
+#include "ssm_scan.h"
 
 namespace {
 

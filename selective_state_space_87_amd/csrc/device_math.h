@@ -55,12 +55,71 @@ __device__ __forceinline__ float load_elem(const void* p, int64_t i) {
   }
 }
 
+// Raw storage bits of element i (bf16 zero-extended, or the float32 pattern).
+// Keeping the bits lets a prefetch stay in flight until the value is used.
+template <bool BF16>
+__device__ __forceinline__ uint32_t load_bits(const void* p, int64_t i) {
+  if constexpr (BF16) {
+    return static_cast<const uint16_t*>(p)[i];
+  } else {
+    return static_cast<const uint32_t*>(p)[i];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float bits_to_f32(uint32_t v) {
+  if constexpr (BF16) {
+    return __uint_as_float(v << 16);
+  } else {
+    return __uint_as_float(v);
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
   if constexpr (BF16) {
     static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
   } else {
     static_cast<float*>(p)[i] = v;
+  }
+}
+
+// ---- raw buffer access (gfx9 family, untyped, stride 0)
+//
+// An access whose per-lane byte offset is at or beyond the descriptor's size
+// is out of range: the load returns 0 and the store is dropped by the memory
+// unit. Kernels use this to mask ragged edges without branching. The whole
+// offset is passed per lane (the scalar offset is not range-checked).
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+__device__ __forceinline__ rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kRawBufferFlags);
+}
+
+// Storage bits of one element: uint16_t for bfloat16 (kept 16-bit so that a
+// value carried across a loop needs no zero-extension), uint32_t for float32.
+template <bool BF16>
+using storage_t = std::conditional_t<BF16, uint16_t, uint32_t>;
+
+template <bool BF16>
+__device__ __forceinline__ storage_t<BF16> buffer_load_bits(rsrc_t r, uint32_t off) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void buffer_store_f32(float v, rsrc_t r, uint32_t off) {
+  if constexpr (BF16) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
   }
 }
 

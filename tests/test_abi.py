@@ -59,7 +59,7 @@ def vp(x):
 
 
 def scan(lib, B=2, L=8, d=4, N=4, ind=0, outd=0, sp=1, u=P, delta=2 * P, A=3 * P, Bm=4 * P, Cm=5 * P,
-         D=6 * P, z=7 * P, bias=8 * P, h0=9 * P, y=10 * P, hf=11 * P, ws=None, wsb=0):
+         D=6 * P, z=7 * P, bias=8 * P, h0=9 * P, y=10 * P, hf=11 * P, ws=20 * P, wsb=1 << 20):
     return lib.ssm_selective_scan_fwd(B, L, d, N, ind, outd, sp, vp(u), vp(delta), vp(A), vp(Bm), vp(Cm),
                                       vp(D), vp(z), vp(bias), vp(h0), vp(y), vp(hf), vp(ws), wsb, None)
 
@@ -115,8 +115,8 @@ def test_workspace_query(lib):
     assert lib.ssm_scan_workspace_bytes(1, 8, 4, 65) == 0
     need = lib.ssm_scan_workspace_bytes(1, 262144, 2560, 16)
     if need:
-        assert scan(lib, B=1, L=262144, d=2560, N=16, ws=None) == E_WORKSPACE
-        assert scan(lib, B=1, L=262144, d=2560, N=16, ws=64 * P, wsb=need - 1) == E_WORKSPACE
+        assert scan(lib, B=1, L=262144, d=2560, N=16, ws=None, wsb=0) == E_WORKSPACE
+        assert scan(lib, B=1, L=262144, d=2560, N=16, ws=1 << 40, wsb=need - 1) == E_WORKSPACE
 
 
 def test_python_binding_rejects_cpu_tensors():
