@@ -213,6 +213,18 @@ def bench_decode(args, torch, binding, synth):
     }
 
 
+def copy_calibration(torch, mib):
+    """Three device-to-device copies of `mib` MiB (reads and writes mib MiB each)."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +235,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=8192)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first copy a buffer of this many MiB device to device three times: a kernel "
+                         "of known HBM traffic, against which hardware byte counters are scaled")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -241,6 +256,8 @@ def main():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
 
+    if args.copy_calibration_mib > 0:
+        copy_calibration(torch, args.copy_calibration_mib)
     w, inp, wall_ms, kern_ms, cold_ms = bench_scan(args, torch, binding, synth)
     ups = w.updates
     value = ups / (wall_ms * 1e-3) / 1e9

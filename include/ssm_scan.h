@@ -65,7 +65,7 @@ extern "C" {
 #define SSM_E_ALIGN 4       /* pointer not aligned as documented                 */
 #define SSM_E_WORKSPACE 5   /* workspace missing or smaller than required        */
 #define SSM_E_ALIAS 6       /* an output overlaps an input it may not overlap    */
-#define SSM_E_UNSUPPORTED 7 /* dstate outside the supported range                */
+#define SSM_E_UNSUPPORTED 7 /* dstate, seqlen or dim beyond the supported range  */
 #define SSM_E_HIP 8         /* the HIP runtime reported an error at launch       */
 
 /* Version of this ABI (SSM_ABI_VERSION of the header the library was built from). */
@@ -75,22 +75,38 @@ int ssm_abi_version(void);
 const char* ssm_status_string(int status);
 
 /*
- * Bytes of device workspace ssm_selective_scan_fwd needs for this shape
- * (0 when the shape runs without one). The workspace holds, per time chunk,
- * the chunk's transition product exp(A * sum(dt)) and its zero-start end
- * state, both [B, d, N] float32, so chunks can run in parallel and be joined
- * with the associative operator (A_i, b_i) (+) (A_j, b_j) = (A_j A_i,
- * A_j b_i + b_j) of "Mamba的隐藏代价" (kongchang.com), section on sequential
- * gradients. It depends only on the four sizes. Returns 0 for invalid sizes.
+ * Bytes of device workspace ssm_selective_scan_fwd needs for this shape. It
+ * holds B and C repacked time-major per state (read by the kernels as
+ * wave-uniform rows) and, when the sequence is split into chunks that run in
+ * parallel (see ssm_scan_chunks), each chunk's summary: the sum of its step
+ * sizes, [B, d] float32 (its transition product is exp(A * that sum)), and
+ * its final state from a zero start, [B, d, N] float32. The summaries are
+ * joined in order with the recurrence's own combine rule, the associative
+ * operator (A_i, b_i) (+) (A_j, b_j) = (A_j A_i, A_j b_i + b_j) of
+ * "Mamba的隐藏代价" (kongchang.com), section on sequential gradients, and the
+ * chunked processing with a carried state of intelliparadigm.com section 6.2.
+ * It depends only on the four sizes. Returns 0 for invalid or unsupported
+ * sizes, and for batch, dim or seqlen 0.
  */
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * Number of sequence chunks the scan of this shape runs in (1: one pass over
+ * the whole sequence; 0: invalid or unsupported sizes). Chunking is chosen
+ * when the batch has too few 64-channel blocks to occupy the device
+ * (B * ceil(d / 64) <= 128 with L >= 2048), or when one batch row's [L, d]
+ * plane exceeds 2^30 bytes at 4 bytes per element. Results of a chunked and a
+ * single-pass scan agree to rounding; each is deterministic.
+ */
+int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
 /*
  * Selective scan forward (the selective_scan(u, delta, A, B, C, D) statement
  * of ybb.press section 3.1 with the loop of section 5; gate from section 5's
  * MambaBlock; h0/h_final per intelliparadigm.com section 6.2).
  *
- *   batch, seqlen, dim, dstate : B >= 0, L >= 0, d >= 0, 1 <= N <= 64.
+ *   batch, seqlen, dim, dstate : B >= 0, 0 <= L < 2^30, 0 <= d < 2^24,
+ *                                1 <= N <= 64 (else SSM_E_UNSUPPORTED).
  *   in_dtype, out_dtype        : 0 float32, 1 bfloat16.
  *   delta_softplus             : nonzero -> dt = softplus(delta + bias).
  *   u, delta  [B, L, d]  in_dtype   input and raw step size

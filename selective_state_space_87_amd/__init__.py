@@ -8,6 +8,7 @@ unloadable library raises at once.
 
 from .binding import (  # noqa: F401
     ssm_abi_version,
+    ssm_scan_chunks,
     ssm_scan_workspace_bytes,
     ssm_selective_scan_fwd,
     ssm_selective_state_update,

@@ -52,6 +52,8 @@ def _load():
         lib.ssm_status_string.argtypes = [i32]
         lib.ssm_scan_workspace_bytes.restype = sz
         lib.ssm_scan_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        lib.ssm_scan_chunks.restype = i64
+        lib.ssm_scan_chunks.argtypes = [i64, i64, i64, i64]
         lib.ssm_selective_scan_fwd.restype = i32
         lib.ssm_selective_scan_fwd.argtypes = [i64, i64, i64, i64, i32, i32, i32,
                                                vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -109,6 +111,11 @@ def ssm_abi_version() -> int:
 
 def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate) -> int:
     return int(_load().ssm_scan_workspace_bytes(batch, seqlen, dim, dstate))
+
+
+def ssm_scan_chunks(batch, seqlen, dim, dstate) -> int:
+    """Sequence chunks the scan of this shape runs in (1 = single pass, 0 = unsupported)."""
+    return int(_load().ssm_scan_chunks(batch, seqlen, dim, dstate))
 
 
 def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,

@@ -30,7 +30,7 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", os.path.jo
 CXX = os.environ.get("CXX_HOST", "g++")
 
 DEVICE_SOURCES = ["scan_fwd.hip", "state_update.hip"]
-HOST_SOURCES = ["api.cpp"]
+HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 
 def _run(cmd, verbose):

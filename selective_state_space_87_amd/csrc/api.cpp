@@ -69,6 +69,14 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
   return ssm::scan_workspace_bytes(batch, seqlen, dim, dstate);
 }
 
+int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > kMaxScanState) return 0;
+  int64_t t;
+  if (!safe_mul(batch, seqlen, &t) || !safe_mul(t, dim, &t)) return 0;
+  const ssm::ScanPlan p = ssm::plan_scan(batch, seqlen, dim, dstate);
+  return p.ok ? p.chunks : 0;
+}
+
 int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                            int in_dtype, int out_dtype, int delta_softplus,
                            const void* u, const void* delta, const float* A,
@@ -84,6 +92,8 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
       !safe_mul(batch, dim, &bdn) || !safe_mul(bdn, dstate, &bdn) || !safe_mul(dim, dstate, &dn)) {
     return SSM_E_SHAPE;
   }
+  const ssm::ScanPlan plan = ssm::plan_scan(batch, seqlen, dim, dstate);
+  if (!plan.ok) return SSM_E_UNSUPPORTED;
   if (batch == 0 || dim == 0) return SSM_OK;  // no channel: nothing to compute or write
   const int64_t isz = in_dtype == 1 ? 2 : 4, osz = out_dtype == 1 ? 2 : 4;
   if (A == nullptr) return SSM_E_NULLPTR;
@@ -98,7 +108,7 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   for (const void* p : f32_ptrs) {
     if (p && !aligned(p, 4)) return SSM_E_ALIGN;
   }
-  const size_t need = ssm::scan_workspace_bytes(batch, seqlen, dim, dstate);
+  const size_t need = plan.bytes;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SSM_E_WORKSPACE;
 
   const Range ry = span(y, seqlen > 0 ? bld : 0, osz);

@@ -18,16 +18,16 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
-// log1p(v) is taken as v * ln(w) / (w - 1) with w = fl(1 + v): the rounding
-// of w cancels between numerator and denominator, so small v keeps full
-// relative accuracy (a plain log(1 + v) would lose it for v << 1, which is
-// exactly the small-step regime). w - 1 is exact for w in [1, 2].
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(v), v = e^-|x| in (0, 1].
+// log1p(v) is taken as log(w) + (v - (w - 1)) with w = fl(1 + v): w - 1 is
+// exact, so the second term is the part of v lost when rounding 1 + v, and
+// adding it restores log1p to first order (the term dropped, c * v / w with
+// |c| <= half an ulp of w, is below 2^-24 v). Small v, the small-step regime,
+// thus keeps full relative accuracy at two transcendentals.
 __device__ __forceinline__ float softplus_f(float x) {
   const float v = exp2_hw(-fabsf(x) * kLog2e);
   const float w = 1.0f + v;
-  const float dw = w - 1.0f;
-  const float lp = (dw == 0.0f) ? v : (log2_hw(w) * kLn2) * (v * rcp_hw(dw));
+  const float lp = fmaf(log2_hw(w), kLn2, v - (w - 1.0f));
   return fmaxf(x, 0.0f) + lp;
 }
 

@@ -39,7 +39,32 @@ struct UpdateArgs {
   int in_bf16, out_bf16, delta_softplus;
 };
 
-// Workspace bytes the scan needs for this shape (0: single pass).
+// How a scan of a given shape is run. The sequence is split into `chunks`
+// pieces of `chunk` steps (the last may be shorter) when there are too few
+// channel blocks to fill the device, or when one batch row's [L, d] plane is
+// too large for 32-bit buffer offsets. A chunked scan is three launches after
+// the B/C pre-pass: per-chunk summaries (local final state from zero, and the
+// sum of the step sizes), an in-order fold of the summaries into each chunk's
+// incoming state, and the full scan of every chunk from that state.
+// Pure function of the sizes (not of the device or the dtypes).
+struct ScanPlan {
+  bool ok;                 // false: sizes beyond what the kernels address
+  int NS, W, S;            // padded state count, waves per block, states per lane
+  int64_t Lp;              // sequence length padded to a multiple of kPadSteps
+  int64_t chunk, chunks;   // steps per chunk (multiple of kPadSteps), chunk count
+  int64_t dim_blocks;      // blocks of 64 channels per batch row
+  size_t off_bc, off_hsum, off_ssum, bytes;  // workspace layout
+};
+
+constexpr int64_t kPadSteps = 16;        // tiles never straddle this boundary
+constexpr int64_t kPlaneBytesMax = int64_t(1) << 30;   // per chunk and batch row
+constexpr int64_t kChunkMinSteps = 1024;
+constexpr int64_t kBlockSlots = 512;     // 256 CUs x two resident blocks
+constexpr int64_t kChunkWhenBlocksAtMost = 128;
+
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+// Workspace bytes the scan needs for this shape.
 size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
 // Enqueue the scan / decode kernels on `stream`. Arguments are already

@@ -1,0 +1,74 @@
+// Execution plan of the selective scan (host only, no HIP): state mapping,
+// sequence chunking and workspace layout, as a pure function of the sizes.
+#include "kernels.h"
+
+namespace ssm {
+
+namespace {
+
+int ceil_pow2(int64_t n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  ScanPlan p{};
+  p.ok = batch >= 0 && seqlen >= 0 && dim >= 0 && dstate >= 1 && dstate <= 64 &&
+         seqlen < (int64_t(1) << 30) && dim < (int64_t(1) << 24);
+  if (!p.ok) return p;
+  // States: N padded to a power of two; N = 16 runs two states per lane on
+  // eight waves, other sizes one wave per state up to sixteen waves.
+  p.NS = ceil_pow2(dstate);
+  p.W = p.NS < 16 ? p.NS : (p.NS == 16 ? 8 : 16);
+  p.S = p.NS / p.W;
+  p.Lp = round_up(seqlen, kPadSteps);
+  p.dim_blocks = ceil_div(dim, 64);
+  p.chunks = 1;
+  p.chunk = p.Lp;
+  if (batch > 0 && dim > 0 && p.Lp > 0) {
+    const int64_t blocks = batch * p.dim_blocks;
+    int64_t k = 1;
+    if (blocks <= kChunkWhenBlocksAtMost && p.Lp >= 2 * kChunkMinSteps) {
+      k = kBlockSlots / blocks;
+      if (p.Lp / kChunkMinSteps < k) k = p.Lp / kChunkMinSteps;
+      if (k < 1) k = 1;
+    }
+    // Every chunk's plane (counted at 4 bytes per element, whatever the
+    // dtype) must stay within 32-bit buffer offsets with room for the
+    // out-of-range markers.
+    const int64_t steps_max = kPlaneBytesMax / (dim * 4) / kPadSteps * kPadSteps;
+    if (steps_max < kPadSteps) {
+      p.ok = false;
+      return p;
+    }
+    if (ceil_div(p.Lp, steps_max) > k) k = ceil_div(p.Lp, steps_max);
+    p.chunk = round_up(ceil_div(p.Lp, k), kPadSteps);
+    if (p.chunk > steps_max) p.chunk = steps_max;
+    p.chunks = ceil_div(p.Lp, p.chunk);
+  }
+  // Workspace: packed B/C (one word per (b, n, step) for bfloat16 inputs,
+  // two for float32; sized for float32), then the chunk summaries.
+  size_t off = 0;
+  p.off_bc = off;
+  if (batch > 0 && dim > 0 && p.Lp > 0) off += align256(size_t(2 * batch * p.NS * p.Lp) * 4);
+  p.off_hsum = off;
+  if (p.chunks > 1) off += align256(size_t(p.chunks * batch * dim * dstate) * 4);
+  p.off_ssum = off;
+  if (p.chunks > 1) off += align256(size_t((p.chunks - 1) * batch * dim) * 4);
+  p.bytes = off;
+  return p;
+}
+
+size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  const ScanPlan p = plan_scan(batch, seqlen, dim, dstate);
+  return p.ok ? p.bytes : 0;
+}
+
+}  // namespace ssm

@@ -34,8 +34,6 @@ namespace ssm {
 
 namespace {
 
-constexpr int kPad = 16;  // sequences are padded to a multiple of this many steps
-
 typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
 
 // s_waitcnt immediates (gfx9 encoding); counters not named are left at their
@@ -43,12 +41,6 @@ typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 
-
-int ceil_pow2(int64_t n) {
-  int p = 1;
-  while (p < n) p <<= 1;
-  return p;
-}
 
 // ---------------------------------------------------------------- B/C pre-pass
 // B, C [Bt, L, N] -> one 32-bit word per (b, n, t), time-contiguous, zero
@@ -98,15 +90,27 @@ struct Scan {
   const float* A;
   const float* D;
   const float* bias;
-  const float* h0;
+  const float* h0;     // initial state [B, d, N] of a single-pass scan, or null (zeros)
+  const float* carry;  // chunked: chunk c starts from carry[c] ([chunks][B][d][N])
   const uint32_t* BC;  // packed B/C (see bc_pack_kernel)
   void* y;
   float* h_final;
-  int64_t L, Lp, dim;
-  int N, softplus;
+  float* hsum;         // summary pass: chunk c's final state from zero into slot c + 1
+  float* ssum;         // summary pass: chunk c's sum of step sizes, [chunks-1][B][d]
+  int L, Lp, dim, N, chunk, batch;
 };
 
-template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS>
+// Out-of-range markers of the two parts of a buffer offset: the lane part
+// (channel beyond d) and the wave-uniform step part (step outside the chunk).
+// A chunk's plane is at most 2^30 bytes, so an offset with either marker,
+// or both, is beyond every descriptor's size and the access is masked.
+constexpr uint32_t kLaneOut = 0x80000000u;
+constexpr uint32_t kStepOut = 0x40000000u;
+
+// SUMMARY = false: the scan of one chunk (or of the whole sequence), with
+// readout, gate and store. SUMMARY = true: the chunk's recurrence from a zero
+// state only, exporting its final state and the sum of its step sizes.
+template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool SUMMARY>
 __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int NS = S * W;        // padded state count
   constexpr int IT = T / W;        // cooperative items per thread per tile
@@ -116,23 +120,26 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int LNC = __builtin_ctz(NC);
   constexpr int WPS = BF16_IN ? 1 : 2;              // packed B/C words per step
   constexpr uint32_t IN_B = BF16_IN ? 2 : 4, OUT_B = BF16_OUT ? 2 : 4;
+  constexpr bool READOUT = !SUMMARY;
 
   // Step sizes live in a ring of 4 tile slots (tile k in slot k & 3): tiles
   // are prepared two at a time, every other tile. Partial readouts are
   // double-buffered by tile parity. One barrier per tile separates every
   // writer from every reader.
   __shared__ float2 sDD[4][T][64];                  // (dt, dt*u) per step and channel
-  __shared__ __attribute__((aligned(16))) float sP[2][T][64 * W];  // partial readouts
+  __shared__ __attribute__((aligned(16))) float sP[READOUT ? 2 : 1][T][READOUT ? 64 * W : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t tiles_d = (p.dim + 63) / 64;
-  const int64_t b = blockIdx.x / tiles_d;
-  const int ch_local = static_cast<int>((blockIdx.x % tiles_d) * 64);
-  const int64_t ch = ch_local + lane;
-  const bool ch_ok = ch < p.dim;
-  const int N = p.N;
-  const int64_t L = p.L, Lp = p.Lp, Dm = p.dim;
+  const int Dm = p.dim, N = p.N;
+  const int tiles_d = (Dm + 63) / 64;
+  const int b = blockIdx.x / tiles_d;
+  const int ch = static_cast<int>(blockIdx.x % tiles_d) * 64 + lane;
+  const bool ch_ok = ch < Dm;
+  const int c = blockIdx.y;                         // sequence chunk
+  const int t0 = c * p.chunk;
+  const int len = min(p.L - t0, p.chunk);           // valid steps of this chunk
+  const int nt = min(p.Lp - t0, p.chunk) / T;       // tiles (padded steps / T)
   // Slot of this wave's partial in the lane's row, and the order in which the
   // row's 16-byte chunks are read back. Both are XOR swizzles chosen so that
   // the 4-byte writes and the 16-byte reads hit distinct banks with either
@@ -140,44 +147,56 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   const int wpos = lane * W + ((w ^ (lane >> (5 - LW)) ^ (lane >> 5)) & (W - 1));
   const int rswz = ((lane >> (3 - LNC)) ^ (lane >> 3)) & (NC - 1);
 
-  // Recurrence state of this lane: states n = w*S + s of channel ch.
+  // Recurrence state of this lane: states n = w*S + s of channel ch. A
+  // single pass starts from h0 (or zeros); a chunked scan starts chunk c from
+  // its carried-in state (for chunk 0 a copy of h0, so that h_final may
+  // overwrite h0 while other chunks run); the summary pass from zeros.
+  const int64_t bdn = (static_cast<int64_t>(b) * Dm + ch) * N;
+  const float* hinit = SUMMARY ? nullptr
+                               : (p.carry ? p.carry + static_cast<int64_t>(c) * p.batch * Dm * N : p.h0);
   float A2[S], h[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int n = w * S + s;
     const bool ok = ch_ok && n < N;
-    A2[s] = ok ? p.A[ch * N + n] * kLog2e : 0.0f;
+    A2[s] = ok ? p.A[static_cast<int64_t>(ch) * N + n] * kLog2e : 0.0f;
     // Pass the loaded initial state through an ALU op here (fma(x, 1, 0) is
     // not folded: it maps -0 to +0), so the loop never inherits a pending load
     // on the state registers.
-    h[s] = __builtin_fmaf((ok && p.h0) ? p.h0[(b * Dm + ch) * N + n] : 0.0f, 1.0f, 0.0f);
+    h[s] = __builtin_fmaf((ok && hinit) ? hinit[bdn + n] : 0.0f, 1.0f, 0.0f);
   }
-  const float Dv = (ch_ok && p.D) ? p.D[ch] : 0.0f;
-  const float bv = (ch_ok && p.bias) ? p.bias[ch] : 0.0f;
-  const bool has_z = p.z != nullptr;
+  // Same ALU pass-through for the per-channel constants.
+  const float Dv = __builtin_fmaf((ch_ok && p.D) ? p.D[ch] : 0.0f, 1.0f, 0.0f);
+  const float bv = __builtin_fmaf((ch_ok && p.bias) ? p.bias[ch] : 0.0f, 1.0f, 0.0f);
+  const bool has_z = READOUT && p.z != nullptr;
+  float dt_sum = 0.0f;
 
-  // Buffer descriptors over this batch row's [L, d] planes; the host keeps
-  // each plane below the out-of-range offset. Missing z reads as zeros.
-  const uint32_t plane = static_cast<uint32_t>(L * Dm);
-  const int64_t pb = b * L * Dm;
-  const rsrc_t ru_b = raw_buffer(static_cast<const char*>(p.u) + pb * IN_B, plane * IN_B);
-  const rsrc_t rd_b = raw_buffer(static_cast<const char*>(p.delta) + pb * IN_B, plane * IN_B);
+  // Buffer descriptors over this chunk of this batch row's [L, d] planes
+  // (at most 2^30 bytes each). Missing z reads as zeros.
+  const int64_t pb = (static_cast<int64_t>(b) * p.L + t0) * Dm;
+  const uint32_t elems = static_cast<uint32_t>(len) * static_cast<uint32_t>(Dm);
+  const rsrc_t ru_b = raw_buffer(static_cast<const char*>(p.u) + pb * IN_B, elems * IN_B);
+  const rsrc_t rd_b = raw_buffer(static_cast<const char*>(p.delta) + pb * IN_B, elems * IN_B);
   const rsrc_t rz_b = raw_buffer(has_z ? static_cast<const char*>(p.z) + pb * IN_B : nullptr,
-                                 has_z ? plane * IN_B : 0u);
-  const rsrc_t ry_b = raw_buffer(static_cast<const char*>(p.y) + pb * OUT_B, plane * OUT_B);
-  // Element offset of this thread's cooperative item i in tile k:
-  // (k*T + w + W*i) * d + ch; out of range past L or d.
-  auto item_off = [&](int k, int i, uint32_t elem) -> uint32_t {
+                                 has_z ? elems * IN_B : 0u);
+  const rsrc_t ry_b = raw_buffer(READOUT ? static_cast<char*>(p.y) + pb * OUT_B : nullptr,
+                                 READOUT ? elems * OUT_B : 0u);
+  const uint32_t lane_in = ch_ok ? static_cast<uint32_t>(ch) * IN_B : kLaneOut;
+  const uint32_t lane_out = ch_ok ? static_cast<uint32_t>(ch) * OUT_B : kLaneOut;
+  // Wave-uniform part of the offset of cooperative item i of tile k: step
+  // k*T + w + W*i of the chunk, times the row pitch; out of range outside it.
+  auto step_off = [&](int k, int i, uint32_t elem) -> uint32_t {
     const int t = k * T + w + W * i;
-    const bool ok = ch_ok && t >= 0 && t < L;
-    return ok ? static_cast<uint32_t>(t * Dm + ch) * elem : kOutOfRange;
+    return static_cast<unsigned>(t) < static_cast<unsigned>(len)
+               ? static_cast<uint32_t>(t) * static_cast<uint32_t>(Dm) * elem
+               : kStepOut;
   };
 
   // This wave's packed B/C rows: read-only for the whole kernel (written by
   // the pre-pass launch), so the constant address space turns these
   // wave-uniform loads into scalar loads and the values into SGPR operands.
-  const_u32p bcw = (const_u32p)(p.BC) + (b * NS + w * S) * Lp * WPS;
-  const int nt = static_cast<int>(Lp / T);
+  const_u32p bcw = (const_u32p)(p.BC) + ((static_cast<int64_t>(b) * NS + w * S) * p.Lp + t0) * WPS;
+  const int64_t Lp = p.Lp;
 
   // Cooperative items of this thread: step w + W*i of each tile, channel ch.
   // Raw inputs (storage bits) are fetched two tiles at a time into two
@@ -190,57 +209,78 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     constexpr int R = decltype(set)::value;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const uint32_t off = item_off(k, i, IN_B);
+      const uint32_t off = lane_in + step_off(k, i, IN_B);
       ru[R][i] = buffer_load_bits<BF16_IN>(ru_b, off);
       rd[R][i] = buffer_load_bits<BF16_IN>(rd_b, off);
-      rz[R][i] = buffer_load_bits<BF16_IN>(rz_b, off);
+      if constexpr (READOUT) rz[R][i] = buffer_load_bits<BF16_IN>(rz_b, off);
     }
   };
   // Step sizes of tile k into its ring slot (and D*u, gate into registers).
-  // Branch-free: padding items get dt = 0 (exp2(0) = 1 and no input, so the
-  // state is unchanged) and the flags select rather than branch.
+  // Branch-free: padding steps get dt = 0 (exp2(0) = 1 and no input, so the
+  // state is unchanged).
   auto prepare = [&](int k, auto slot) {
     constexpr int SL = decltype(slot)::value;
     constexpr int R = SL & 1;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = w + W * i;
-      const int t = k * T + tt;
-      const bool ok = ch_ok && t < L;
+      const bool t_ok = k * T + tt < len;          // wave-uniform
       const float uv = bits_to_f32<BF16_IN>(ru[R][i]);
       const float x = bits_to_f32<BF16_IN>(rd[R][i]) + bv;
       float dt = SOFTPLUS ? softplus_f(x) : x;
-      dt = ok ? dt : 0.0f;
-      const float g = silu_f(bits_to_f32<BF16_IN>(rz[R][i]));
-      eDu[SL][i] = Dv * uv;
-      eG[SL][i] = has_z ? g : 1.0f;
+      dt = t_ok ? dt : 0.0f;
+      if constexpr (READOUT) {
+        const float g = silu_f(bits_to_f32<BF16_IN>(rz[R][i]));
+        eDu[SL][i] = Dv * uv;
+        eG[SL][i] = has_z ? g : 1.0f;
+      }
       sDD[SL][tt][lane] = make_float2(dt, dt * uv);
     }
   };
-  // Readout of one item of the tile in buffer P: the W partials summed as a
-  // fixed tree (every lane, every run, the same order).
-  auto gather_item = [&](auto par, int i) -> float {
+  // Readout of one item of the tile in buffer P: the W partials, fetched
+  // (gather_load) well before they are summed as a fixed tree (gather_sum;
+  // every lane, every run, the same order).
+  constexpr int GN = W >= 4 ? NC : 1;               // 16-byte reads per item
+  constexpr int GW = W >= 4 ? 4 : W;                // floats per read
+  auto gather_load = [&](auto par, int i, float (&g)[GN][GW]) {
     constexpr int P = decltype(par)::value;
     const int tt = w + W * i;
     if constexpr (W >= 4) {
+#pragma unroll
+      for (int q = 0; q < NC; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(&sP[P][tt][lane * W + 4 * (q ^ rswz)]);
+        g[q][0] = v.x;
+        g[q][1] = v.y;
+        g[q][2] = v.z;
+        g[q][3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < W; ++q) g[0][q] = sP[P][tt][lane * W + q];
+    }
+  };
+  auto gather_sum = [&](const float (&g)[GN][GW]) -> float {
+    if constexpr (W >= 4) {
       float c4[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(&sP[P][tt][lane * W + 4 * (c ^ rswz)]);
-        c4[c] = (v.x + v.y) + (v.z + v.w);
-      }
+      for (int q = 0; q < NC; ++q) c4[q] = (g[q][0] + g[q][1]) + (g[q][2] + g[q][3]);
 #pragma unroll
       for (int m = 1; m < NC; m <<= 1) {
 #pragma unroll
-        for (int c = 0; c < NC; c += 2 * m) c4[c] += c4[c + m];
+        for (int q = 0; q < NC; q += 2 * m) c4[q] += c4[q + m];
       }
       return c4[0];
     } else {
       float acc = 0.0f;
 #pragma unroll
-      for (int c = 0; c < W; ++c) acc += sP[P][tt][lane * W + c];
+      for (int q = 0; q < W; ++q) acc += g[0][q];
       return acc;
     }
+  };
+  auto gather_item = [&](auto par, int i) -> float {
+    float g[GN][GW];
+    gather_load(par, i, g);
+    return gather_sum(g);
   };
 
   // Packed B/C of the tile being scanned, wave-uniform (SGPRs), one set per
@@ -284,9 +324,10 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
         }
         const float abar = exp2_hw(dd[t].x * A2[s]);
         h[s] = fmaf(abar, h[s], dd[t].y * bval);
-        acc = fmaf(cval, h[s], acc);
+        if constexpr (READOUT) acc = fmaf(cval, h[s], acc);
       }
-      sP[P][t][wpos] = acc;
+      if constexpr (READOUT) sP[P][t][wpos] = acc;
+      if constexpr (SUMMARY) dt_sum += dd[t].x;
     }
   };
 
@@ -309,23 +350,28 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
           std::integral_constant<int, T / 2>{});
     __builtin_amdgcn_sched_barrier(0);
     read_dd(dd_next, std::integral_constant<int, (J + 1) & 3>{});
-    float part[IT];
+    float gp[IT][GN][GW];
+    if constexpr (READOUT) {
 #pragma unroll
-    for (int i = 0; i < IT; ++i) part[i] = gather_item(std::integral_constant<int, Q>{}, i);
+      for (int i = 0; i < IT; ++i) gather_load(std::integral_constant<int, Q>{}, i, gp[i]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
           std::integral_constant<int, T>{});
-    // Readout of tile k-1 (out of range at k = 0: the stores are dropped).
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      yv[P][i] = (part[i] + eDu[(J + 3) & 3][i]) * eG[(J + 3) & 3][i];
-      yo[P][i] = item_off(k - 1, i, OUT_B);
-    }
-    if constexpr (P == 1) {
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (READOUT) {
+      // Readout of tile k-1 (out of range at k = 0: the stores are dropped).
 #pragma unroll
       for (int i = 0; i < IT; ++i) {
-        buffer_store_f32<BF16_OUT>(yv[0][i], ry_b, yo[0][i]);
-        buffer_store_f32<BF16_OUT>(yv[1][i], ry_b, yo[1][i]);
+        yv[P][i] = (gather_sum(gp[i]) + eDu[(J + 3) & 3][i]) * eG[(J + 3) & 3][i];
+        yo[P][i] = lane_out + step_off(k - 1, i, OUT_B);
+      }
+      if constexpr (P == 1) {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+          buffer_store_f32<BF16_OUT>(yv[0][i], ry_b, yo[0][i]);
+          buffer_store_f32<BF16_OUT>(yv[1][i], ry_b, yo[1][i]);
+        }
       }
     }
     if constexpr (P == 0) {
@@ -344,11 +390,19 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     load_bc(0, std::integral_constant<int, 0>{});
     prepare(0, std::integral_constant<int, 0>{});
     prepare(1, std::integral_constant<int, 1>{});
-    // Retire every load so far (h0, A, D, bias, tiles 0-1): the wait analysis
-    // would otherwise carry them into the loop as possibly pending.
+    // Retire every load so far (state, A, D, bias, tiles 0-1): the wait
+    // analysis would otherwise carry them into the loop as possibly pending.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     load_raw(2, std::integral_constant<int, 0>{});
     load_raw(3, std::integral_constant<int, 1>{});
+    if constexpr (READOUT) {
+      // Out-of-range stores (dropped by the buffer unit) in the places of an
+      // odd tile's output stores: loop entry then sees the same queue of
+      // memory operations as the back edge, and the waits of the first tile
+      // need not cover stores.
+#pragma unroll
+      for (int i = 0; i < 2 * IT; ++i) buffer_store_f32<BF16_OUT>(0.0f, ry_b, kLaneOut + 64u * i);
+    }
     __syncthreads();
     read_dd(ddA, std::integral_constant<int, 0>{});
     // As above for the LDS counter: retire the first step-size read here.
@@ -366,101 +420,140 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   if (k < nt) iter(k, std::integral_constant<int, 0>{}, ddA, ddB);
   if (k + 1 < nt) iter(k + 1, std::integral_constant<int, 1>{}, ddB, ddA);
   if (k + 2 < nt) iter(k + 2, std::integral_constant<int, 2>{}, ddA, ddB);
-  if (nt > 0) {
-    // Held readout of tile nt-2 (when the last tile was even), then tile nt-1.
-    const int last = nt - 1;
-    if ((last & 1) == 0) {
-#pragma unroll
-      for (int i = 0; i < IT; ++i) buffer_store_f32<BF16_OUT>(yv[0][i], ry_b, yo[0][i]);
-    }
-    float part[IT];
-    if (last & 1) {
-#pragma unroll
-      for (int i = 0; i < IT; ++i) part[i] = gather_item(std::integral_constant<int, 1>{}, i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < IT; ++i) part[i] = gather_item(std::integral_constant<int, 0>{}, i);
-    }
-    const int sl = last & 3;
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const float du = sl == 0 ? eDu[0][i] : sl == 1 ? eDu[1][i] : sl == 2 ? eDu[2][i] : eDu[3][i];
-      const float g = sl == 0 ? eG[0][i] : sl == 1 ? eG[1][i] : sl == 2 ? eG[2][i] : eG[3][i];
-      buffer_store_f32<BF16_OUT>((part[i] + du) * g, ry_b, item_off(last, i, OUT_B));
-    }
-  }
 
-  if (p.h_final && ch_ok) {
+  if constexpr (READOUT) {
+    if (nt > 0) {
+      // Held readout of tile nt-2 (when the last tile was even), then tile nt-1.
+      const int last = nt - 1;
+      if ((last & 1) == 0) {
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int n = w * S + s;
-      if (n < N) p.h_final[(b * Dm + ch) * N + n] = h[s];
+        for (int i = 0; i < IT; ++i) buffer_store_f32<BF16_OUT>(yv[0][i], ry_b, yo[0][i]);
+      }
+      float part[IT];
+      if (last & 1) {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) part[i] = gather_item(std::integral_constant<int, 1>{}, i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) part[i] = gather_item(std::integral_constant<int, 0>{}, i);
+      }
+      const int sl = last & 3;
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const float du = sl == 0 ? eDu[0][i] : sl == 1 ? eDu[1][i] : sl == 2 ? eDu[2][i] : eDu[3][i];
+        const float g = sl == 0 ? eG[0][i] : sl == 1 ? eG[1][i] : sl == 2 ? eG[2][i] : eG[3][i];
+        buffer_store_f32<BF16_OUT>((part[i] + du) * g, ry_b, lane_out + step_off(last, i, OUT_B));
+      }
+    }
+    if (p.h_final && ch_ok && c == static_cast<int>(gridDim.y) - 1) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = w * S + s;
+        if (n < N) p.h_final[bdn + n] = h[s];
+      }
+    }
+  } else {
+    if (ch_ok) {
+      const int64_t cb = static_cast<int64_t>(c) * p.batch + b;
+      const int64_t cb1 = cb + p.batch;              // slot c + 1
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = w * S + s;
+        if (n < N) p.hsum[(cb1 * Dm + ch) * N + n] = h[s];
+      }
+      if (w == 0) p.ssum[cb * Dm + ch] = dt_sum;
     }
   }
 }
 
-int64_t padded_len(int64_t L) { return (L + kPad - 1) / kPad * kPad; }
-
-// Waves per block and states per lane for a padded state count.
-void shape_for(int64_t N, int* NS, int* W, int* S) {
-  *NS = ceil_pow2(N);
-  *W = *NS < 16 ? *NS : (*NS == 16 ? 8 : 16);
-  *S = *NS / *W;
+// In-order fold of the chunk summaries with the recurrence's combine rule:
+// the state entering chunk c+1 is exp(A * sum of chunk c's step sizes) times
+// the state entering chunk c, plus chunk c's final state from zero. One
+// thread per (b, d, n). Slot 0 receives the initial state (h0 or zeros);
+// slot c+1, which holds chunk c's summary state, is overwritten in place with
+// the state entering chunk c+1.
+__global__ __launch_bounds__(256) void carry_fold_kernel(const float* __restrict__ A,
+                                                         const float* __restrict__ h0,
+                                                         float* __restrict__ hsum,
+                                                         const float* __restrict__ ssum,
+                                                         int64_t bdn_total, int dim, int N,
+                                                         int folds) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= bdn_total) return;
+  const int n = static_cast<int>(i % N);
+  const int64_t bd = i / N;
+  const int ch = static_cast<int>(bd % dim);
+  const int64_t bd_total = bdn_total / N;
+  const float a2 = A[static_cast<int64_t>(ch) * N + n] * kLog2e;
+  float h = h0 ? h0[i] : 0.0f;
+  hsum[i] = h;
+  for (int c = 0; c < folds; ++c) {
+    const float decay = exp2_hw(a2 * ssum[c * bd_total + bd]);
+    float* slot = hsum + (c + 1) * bdn_total + i;
+    h = fmaf(decay, h, *slot);
+    *slot = h;
+  }
 }
 
 template <int S, int W, int T, bool BI, bool BO, bool SP>
-int launch_sw(const ScanArgs& a, const Scan& s, hipStream_t st) {
-  static_assert(kPad % T == 0, "tile must divide the padding");
-  const int64_t tiles_d = (a.dim + 63) / 64;
-  const int64_t blocks = a.batch * tiles_d;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
+  static_assert(kPadSteps % T == 0, "tile must divide the padding");
+  const int64_t blocks = a.batch * pl.dim_blocks;
+  if (blocks > 0x7fffffff || pl.chunks > 65535) return hipErrorInvalidConfiguration;
   Scan args = s;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP>),
-                         dim3(static_cast<unsigned>(blocks)), dim3(W * 64), kargs, 0, st);
+  if (pl.chunks > 1) {
+    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, true>),
+                              dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks - 1)),
+                              dim3(W * 64), kargs, 0, st);
+    if (err != 0) return err;
+    const int64_t bdn = a.batch * a.dim * a.dstate;
+    const float* A = a.A;
+    const float* h0 = a.h0;
+    float* hsum = args.hsum;
+    const float* ssum = args.ssum;
+    int dim = static_cast<int>(a.dim), N = static_cast<int>(a.dstate);
+    int folds = static_cast<int>(pl.chunks - 1);
+    void* fargs[] = {&A, &h0, &hsum, &ssum, const_cast<int64_t*>(&bdn), &dim, &N, &folds};
+    err = hipLaunchKernel(reinterpret_cast<const void*>(&carry_fold_kernel),
+                          dim3(static_cast<unsigned>((bdn + 255) / 256)), dim3(256), fargs, 0, st);
+    if (err != 0) return err;
+  }
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, false>),
+                         dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks)),
+                         dim3(W * 64), kargs, 0, st);
 }
 
 // Per padded state count: states per lane S, waves per block W (state
-// groups), tile length T. N = 16 uses two states per lane: half the LDS
-// traffic per state update of one state per lane, which the LDS bandwidth
-// (128 bytes per clock per CU) needs more than the extra waves.
+// groups), tile length T. N = 16 uses two states per lane on eight waves:
+// half the LDS traffic per state update of one state per lane, which the LDS
+// bandwidth (128 bytes per clock per CU) needs more than the extra waves.
 template <bool BI, bool BO, bool SP>
-int launch_ns(const ScanArgs& a, const Scan& s, hipStream_t st) {
-  int NS, W, S;
-  shape_for(a.dstate, &NS, &W, &S);
-  switch (NS) {
-    case 1: return launch_sw<1, 1, 16, BI, BO, SP>(a, s, st);
-    case 2: return launch_sw<1, 2, 16, BI, BO, SP>(a, s, st);
-    case 4: return launch_sw<1, 4, 16, BI, BO, SP>(a, s, st);
-    case 8: return launch_sw<1, 8, 16, BI, BO, SP>(a, s, st);
-    case 16: return launch_sw<2, 8, 8, BI, BO, SP>(a, s, st);
-    case 32: return launch_sw<2, 16, 16, BI, BO, SP>(a, s, st);
-    default: return launch_sw<4, 16, 16, BI, BO, SP>(a, s, st);
+int launch_ns(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
+  switch (pl.NS) {
+    case 1: return launch_sw<1, 1, 16, BI, BO, SP>(a, pl, s, st);
+    case 2: return launch_sw<1, 2, 16, BI, BO, SP>(a, pl, s, st);
+    case 4: return launch_sw<1, 4, 16, BI, BO, SP>(a, pl, s, st);
+    case 8: return launch_sw<1, 8, 16, BI, BO, SP>(a, pl, s, st);
+    case 16: return launch_sw<2, 8, 8, BI, BO, SP>(a, pl, s, st);
+    case 32: return launch_sw<2, 16, 16, BI, BO, SP>(a, pl, s, st);
+    default: return launch_sw<4, 16, 16, BI, BO, SP>(a, pl, s, st);
   }
 }
 
 template <bool BI, bool BO>
-int launch_io(const ScanArgs& a, const Scan& s, hipStream_t st) {
-  return a.delta_softplus ? launch_ns<BI, BO, true>(a, s, st) : launch_ns<BI, BO, false>(a, s, st);
+int launch_io(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
+  return a.delta_softplus ? launch_ns<BI, BO, true>(a, pl, s, st) : launch_ns<BI, BO, false>(a, pl, s, st);
 }
 
 }  // namespace
 
-size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
-  if (batch == 0 || dim == 0 || seqlen == 0) return 0;
-  int NS, W, S;
-  shape_for(dstate, &NS, &W, &S);
-  // Packed B/C: one word per (b, n, t) for bfloat16 inputs, two for float32;
-  // sized for the larger so the query does not depend on the dtype.
-  return static_cast<size_t>(2 * batch * NS * padded_len(seqlen)) * sizeof(uint32_t);
-}
-
 int launch_scan(const ScanArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.batch == 0 || a.dim == 0) return 0;
-  int NS, W, S;
-  shape_for(a.dstate, &NS, &W, &S);
-  const int64_t Lp = padded_len(a.seqlen);
+  const ScanPlan pl = plan_scan(a.batch, a.seqlen, a.dim, a.dstate);
+  if (!pl.ok) return hipErrorInvalidValue;
+  char* ws = static_cast<char*>(a.workspace);
   Scan s;
   s.u = a.u;
   s.delta = a.delta;
@@ -469,23 +562,28 @@ int launch_scan(const ScanArgs& a, void* stream) {
   s.D = a.D;
   s.bias = a.delta_bias;
   s.h0 = a.h0;
-  s.BC = static_cast<const uint32_t*>(a.workspace);
+  s.carry = pl.chunks > 1 ? reinterpret_cast<const float*>(ws + pl.off_hsum) : nullptr;
+  s.BC = reinterpret_cast<const uint32_t*>(ws + pl.off_bc);
   s.y = a.y;
   s.h_final = a.h_final;
-  s.L = a.seqlen;
-  s.Lp = Lp;
-  s.dim = a.dim;
+  s.hsum = pl.chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_hsum) : nullptr;
+  s.ssum = pl.chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_ssum) : nullptr;
+  s.L = static_cast<int>(a.seqlen);
+  s.Lp = static_cast<int>(pl.Lp);
+  s.dim = static_cast<int>(a.dim);
   s.N = static_cast<int>(a.dstate);
-  s.softplus = a.delta_softplus;
-  if (Lp > 0) {
-    const int64_t chunks = (Lp + 63) / 64;
+  s.chunk = static_cast<int>(pl.chunk);
+  s.batch = static_cast<int>(a.batch);
+  if (pl.Lp > 0) {
+    const int64_t chunks = (pl.Lp + 63) / 64;
     if (chunks > 0x7fffffff || a.batch > 65535) return hipErrorInvalidConfiguration;
     const void* bin = a.B;
     const void* cin = a.C;
-    uint32_t* out = static_cast<uint32_t*>(a.workspace);
+    uint32_t* out = reinterpret_cast<uint32_t*>(ws + pl.off_bc);
     int64_t L = a.seqlen;
-    int64_t Lpv = Lp;
+    int64_t Lpv = pl.Lp;
     int N = static_cast<int>(a.dstate);
+    int NS = pl.NS;
     void* kargs[] = {&bin, &cin, &out, &L, &Lpv, &N, &NS};
     const void* fn = a.in_bf16 ? reinterpret_cast<const void*>(&bc_pack_kernel<true>)
                                : reinterpret_cast<const void*>(&bc_pack_kernel<false>);
@@ -494,9 +592,9 @@ int launch_scan(const ScanArgs& a, void* stream) {
     if (err != 0) return err;
   }
   if (a.in_bf16) {
-    return a.out_bf16 ? launch_io<true, true>(a, s, st) : launch_io<true, false>(a, s, st);
+    return a.out_bf16 ? launch_io<true, true>(a, pl, s, st) : launch_io<true, false>(a, pl, s, st);
   }
-  return a.out_bf16 ? launch_io<false, true>(a, s, st) : launch_io<false, false>(a, s, st);
+  return a.out_bf16 ? launch_io<false, true>(a, pl, s, st) : launch_io<false, false>(a, pl, s, st);
 }
 
 }  // namespace ssm

@@ -119,6 +119,37 @@ def test_workspace_query(lib):
         assert scan(lib, B=1, L=262144, d=2560, N=16, ws=1 << 40, wsb=need - 1) == E_WORKSPACE
 
 
+def test_size_limits(lib):
+    assert scan(lib, B=1, L=1 << 30, d=4) == E_UNSUPPORTED
+    assert scan(lib, B=1, L=8, d=1 << 24) == E_UNSUPPORTED
+    assert lib.ssm_scan_chunks(1, 1 << 30, 4, 4) == 0
+    assert lib.ssm_scan_chunks(1, 8, 4, 65) == 0
+
+
+def test_chunk_plan(lib):
+    """When the sequence is split (ssm_scan_chunks in the header): only for few
+    channel blocks and long sequences, or for [L, d] planes above 2^30 bytes
+    at 4 bytes per element; and the workspace then holds the chunk summaries."""
+    ch = lib.ssm_scan_chunks
+    assert ch(4, 8192, 4096, 16) == 1            # 256 blocks of 64 channels: fills the device
+    assert ch(8, 2048, 1536, 16) == 1            # 192 blocks
+    assert ch(1, 2000, 64, 16) == 1              # too short to split
+    assert ch(1, 0, 64, 16) == 1
+    assert ch(1, 262144, 2560, 16) > 1           # 40 blocks: split in time
+    assert ch(1, 4096, 64, 16) > 1
+    assert ch(2, 5000, 100, 16) > 1
+    # plane limit alone: many blocks, but L * d * 4 bytes above 2^30
+    assert ch(200, (1 << 20) + 16, 256, 16) > 1
+    assert ch(200, 1 << 20, 256, 16) == 1
+    for B, L, d, N in [(1, 262144, 2560, 16), (1, 4096, 64, 16), (2, 5000, 100, 16), (1, 3000, 64, 3)]:
+        k = ch(B, L, d, N)
+        ws = lib.ssm_scan_workspace_bytes(B, L, d, N)
+        summaries = (k - 1) * B * d * (N + 1) * 4
+        assert ws >= summaries + 2 * B * N * L * 4 * (1 if N != 3 else 0), (B, L, d, N, k, ws)
+        # the chunks' padded lengths cover the sequence, each at least 1024 steps when split
+        assert k == 1 or L // k >= 1000
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     u = torch.zeros(1, 4, 2)

@@ -221,3 +221,98 @@ def test_guard_bands_and_full_coverage():
     assert torch.isnan(ybuf[:pad]).all() and torch.isnan(ybuf[-pad:]).all()
     assert torch.isnan(hbuf[:pad]).all() and torch.isnan(hbuf[-pad:]).all()
     assert not torch.isnan(y).any() and not torch.isnan(hf).any()
+
+
+# ---------------------------------------------------------------- sequence chunks
+# Shapes with few 64-channel blocks and long sequences run as parallel chunks
+# whose summaries are folded in order (ssm_scan_chunks > 1).
+
+CHUNKED = [
+    (1, 4096, 64, 16, "f32"), (2, 5000, 100, 16, "bf16"), (1, 3000, 64, 3, "f32"),
+    (1, 2100, 130, 33, "bf16"), (1, 2048, 1, 1, "f32"), (3, 6000, 40, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,L,d,N,dt", CHUNKED)
+def test_chunked_shapes(B, L, d, N, dt):
+    k = binding.ssm_scan_chunks(B, L, d, N)
+    assert k > 1, (B, L, d, N, k)
+    inp = synth.make_scan_inputs(B, L, d, N, dt, seed=12, stream=12000 + N)
+    rng = np.random.default_rng(L)
+    h0 = rng.standard_normal((B, d, N)).astype(np.float32) * 0.5
+    check_scan(f"chunked x{k} {(B, L, d, N)} {dt}", inp, "f32", h0=h0)
+    check_scan(f"chunked x{k} {(B, L, d, N)} {dt}", inp, "bf16")
+
+
+@pytest.mark.parametrize("opts", [
+    dict(use_D=False, use_z=False), dict(softplus=False, use_bias=False),
+])
+def test_chunked_optional_parts(opts):
+    inp = synth.make_scan_inputs(1, 4100, 64, 16, "f32", seed=13, stream=13000)
+    assert binding.ssm_scan_chunks(1, 4100, 64, 16) > 1
+    if opts.get("softplus") is False:
+        inp = dict(inp)
+        inp["delta"] = np.abs(inp["delta"]) * np.float32(0.05)
+    check_scan(f"chunked options {opts}", inp, "f32", gpu_kwargs=opts)
+
+
+def test_chunked_final_state_in_place_over_h0():
+    B, L, d, N = 1, 4500, 70, 16
+    assert binding.ssm_scan_chunks(B, L, d, N) > 1
+    inp = synth.make_scan_inputs(B, L, d, N, "bf16", seed=14, stream=14000)
+    dev = scan_inputs_to_device(inp)
+    h0_np = np.random.default_rng(1).standard_normal((B, d, N)).astype(np.float32)
+    h = upload(h0_np, "f32")
+    y = binding.ssm_selective_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], D=dev["D"],
+                                       z=dev["z"], delta_bias=dev["delta_bias"], delta_softplus=True,
+                                       h0=h, h_final=h, out_dtype=torch.float32)
+    ref, href, ymag, hmag = oracle_scan(inp, h0=h0_np)
+    report("chunked y with h_final == h0", oracle.scaled_error(download(y[0]), ref, ymag), tol_for("bf16", "f32"))
+    report("chunked h_final == h0 in place", oracle.scaled_error(download(h), href, hmag), tol_for("bf16", "f32"))
+
+
+def test_chunked_guard_bands_causality_determinism():
+    B, L, d, N = 2, 4200, 70, 16
+    k = binding.ssm_scan_chunks(B, L, d, N)
+    assert k > 1
+    inp = synth.make_scan_inputs(B, L, d, N, "bf16", seed=15, stream=15000)
+    dev = scan_inputs_to_device(inp)
+    pad = 64
+    ybuf = torch.full((2 * pad + B * L * d,), float("nan"), device="cuda")
+    y = ybuf[pad:pad + B * L * d].view(B, L, d)
+    hbuf = torch.full((2 * pad + B * d * N,), float("nan"), device="cuda")
+    hf = hbuf[pad:pad + B * d * N].view(B, d, N)
+
+    def run():
+        binding.ssm_selective_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], D=dev["D"],
+                                       z=dev["z"], delta_bias=dev["delta_bias"], delta_softplus=True, y=y,
+                                       h_final=hf, out_dtype=torch.float32)
+        return y.clone(), hf.clone()
+
+    y1, h1 = run()
+    assert torch.isnan(ybuf[:pad]).all() and torch.isnan(ybuf[-pad:]).all()
+    assert torch.isnan(hbuf[:pad]).all() and torch.isnan(hbuf[-pad:]).all()
+    assert not torch.isnan(y1).any() and not torch.isnan(h1).any()
+    y2, h2 = run()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    t = 3 * L // 4   # inside a later chunk
+    for key in ("u", "delta", "z", "B", "C"):
+        dev[key][:, t + 1:] = torch.randn_like(dev[key][:, t + 1:].float()).to(dev[key].dtype)
+    y3, _ = run()
+    assert torch.equal(y1[:, :t + 1], y3[:, :t + 1])
+    assert not torch.equal(y1[:, t + 1:], y3[:, t + 1:])
+
+
+def test_chunked_nan_stays_in_its_channel():
+    B, L, d, N = 1, 4096, 64, 16
+    assert binding.ssm_scan_chunks(B, L, d, N) > 1
+    inp = dict(synth.make_scan_inputs(B, L, d, N, "f32", seed=16, stream=16000))
+    u = inp["u"].copy()
+    u[0, 1500, 9] = np.nan
+    inp["u"] = u
+    dev = scan_inputs_to_device(inp)
+    y, h = run_scan(dev, inp, "f32")
+    yn = download(y)
+    bad = np.isnan(yn)
+    assert bad[0, 1500:, 9].all() and bad.sum() == L - 1500
+    assert np.isnan(download(h)[0, 9]).all() and np.isnan(download(h)).sum() == N
