@@ -84,6 +84,7 @@ SHAPES = [
     (1, 1, 1, 1, "f32"), (2, 67, 70, 16, "f32"), (1, 129, 130, 3, "bf16"), (3, 5, 64, 5, "f32"),
     (1, 300, 64, 33, "f32"), (2, 100, 33, 64, "bf16"), (1, 64, 256, 8, "f32"), (1, 17, 8, 2, "bf16"),
     (2, 200, 65, 16, "bf16"), (1, 1000, 3, 16, "f32"), (2, 130, 300, 12, "f32"), (4, 63, 128, 4, "bf16"),
+    (1, 150, 70, 32, "f32"), (2, 90, 64, 24, "bf16"),
 ]
 
 
