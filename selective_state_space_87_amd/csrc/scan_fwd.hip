@@ -107,6 +107,9 @@ struct Scan {
 constexpr uint32_t kLaneOut = 0x80000000u;
 constexpr uint32_t kStepOut = 0x40000000u;
 
+// Waves whose index has this bit set take the "late" tile order (see iter).
+constexpr int kLateWaveMask = 4;
+
 // SUMMARY = false: the scan of one chunk (or of the whole sequence), with
 // readout, gate and store. SUMMARY = true: the chunk's recurrence from a zero
 // state only, exporting its final state and the sum of its step sizes.
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   const uint32_t lane_out = ch_ok ? static_cast<uint32_t>(ch) * OUT_B : kLaneOut;
   // Wave-uniform part of the offset of cooperative item i of tile k: step
   // k*T + w + W*i of the chunk, times the row pitch; out of range outside it.
-  auto step_off = [&](int k, int i, uint32_t elem) -> uint32_t {
+  auto step_off = [&](int k, int i, uint32_t elem) __attribute__((always_inline)) -> uint32_t {
     const int t = k * T + w + W * i;
     return static_cast<unsigned>(t) < static_cast<unsigned>(len)
                ? static_cast<uint32_t>(t) * static_cast<uint32_t>(Dm) * elem
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   storage_t<BF16_IN> ru[2][IT], rd[2][IT], rz[2][IT];
   float eDu[4][IT], eG[4][IT];
 
-  auto load_raw = [&](int k, auto set) {
+  auto load_raw = [&](int k, auto set) __attribute__((always_inline)) {
     constexpr int R = decltype(set)::value;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // Step sizes of tile k into its ring slot (and D*u, gate into registers).
   // Branch-free: padding steps get dt = 0 (exp2(0) = 1 and no input, so the
   // state is unchanged).
-  auto prepare = [&](int k, auto slot) {
+  auto prepare = [&](int k, auto slot) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
     constexpr int R = SL & 1;
 #pragma unroll
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // every lane, every run, the same order).
   constexpr int GN = W >= 4 ? NC : 1;               // 16-byte reads per item
   constexpr int GW = W >= 4 ? 4 : W;                // floats per read
-  auto gather_load = [&](auto par, int i, float (&g)[GN][GW]) {
+  auto gather_load = [&](auto par, int i, float (&g)[GN][GW]) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
     const int tt = w + W * i;
     if constexpr (W >= 4) {
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       for (int q = 0; q < W; ++q) g[0][q] = sP[P][tt][lane * W + q];
     }
   };
-  auto gather_sum = [&](const float (&g)[GN][GW]) -> float {
+  auto gather_sum = [&](const float (&g)[GN][GW]) __attribute__((always_inline)) -> float {
     if constexpr (W >= 4) {
       float c4[NC];
 #pragma unroll
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       return acc;
     }
   };
-  auto gather_item = [&](auto par, int i) -> float {
+  auto gather_item = [&](auto par, int i) __attribute__((always_inline)) -> float {
     float g[GN][GW];
     gather_load(par, i, g);
     return gather_sum(g);
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // Packed B/C of the tile being scanned, wave-uniform (SGPRs), one set per
   // tile parity so the next tile's fetch overlaps this tile's recurrence.
   uint32_t bc[2][S][T * WPS];
-  auto load_bc = [&](int k, auto par) {
+  auto load_bc = [&](int k, auto par) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -302,12 +305,12 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   float yv[2][IT];
   uint32_t yo[2][IT];
 
-  auto read_dd = [&](float2 (&dd)[T], auto slot) {
+  auto read_dd = [&](float2 (&dd)[T], auto slot) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
 #pragma unroll
     for (int t = 0; t < T; ++t) dd[t] = sDD[SL][t][lane];
   };
-  auto steps = [&](const float2 (&dd)[T], auto par, auto lo, auto hi) {
+  auto steps = [&](const float2 (&dd)[T], auto par, auto lo, auto hi) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
 #pragma unroll
     for (int t = decltype(lo)::value; t < decltype(hi)::value; ++t) {
@@ -332,33 +335,34 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   };
 
   // Tile k with J = k & 3 (P = k & 1). Its step sizes are already in
-  // registers (read during tile k-1), so the recurrence starts right after
-  // the barrier. Order: scalar fetch of tile k+1's B/C; first half of the
-  // recurrence; LDS reads of tile k+1's step sizes and tile k-1's partials
-  // (issued here, waited on after the second half, when the scalar fetch is
-  // long done); second half; readout of tile k-1 (stored on odd tiles, two
-  // tiles at a time); on even tiles, preparation of tiles k+2 and k+3 and
-  // the fetch of the raw inputs of tiles k+4 and k+5. One barrier.
-  auto iter = [&](int k, auto jj, const float2 (&dd)[T], float2 (&dd_next)[T]) {
+  // registers (read during tile k-1) and its B/C in SGPR set P (fetched
+  // during tile k-1). The work of a tile, in the order of the "early" waves:
+  //   (1) scalar fetch of tile k+1's B/C; first half of the recurrence;
+  //   (2) LDS reads of tile k+1's step sizes and tile k-1's partials
+  //       (waited on after the second half, when the scalar fetch is long
+  //       done);
+  //   (3) second half of the recurrence;
+  //   (4) readout of tile k-1 (stored on odd tiles, two tiles at a time); on
+  //       even tiles, preparation of tiles k+2 and k+3 and the fetch of the
+  //       raw inputs of tiles k+4 and k+5.
+  // "Late" waves run (2), (4), (1), (3): the readout and the preparation
+  // first, then the whole recurrence. The two waves that share a SIMD take
+  // different orders, so while one runs the recurrence the other runs the
+  // cooperative work, instead of both waiting on the same phase. Every
+  // dependency is on data written before the previous barrier, so both
+  // orders are valid. One barrier per tile.
+  auto lds_reads = [&](auto jj, float2 (&dd_next)[T], float (&gp)[IT][GN][GW]) __attribute__((always_inline)) {
     constexpr int J = decltype(jj)::value;
-    constexpr int P = J & 1;
-    constexpr int Q = 1 - P;
-    load_bc(k + 1 < nt ? k + 1 : k, std::integral_constant<int, Q>{});  // clamped: stays in SGPRs
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, 0>{},
-          std::integral_constant<int, T / 2>{});
-    __builtin_amdgcn_sched_barrier(0);
+    constexpr int Q = 1 - (J & 1);
     read_dd(dd_next, std::integral_constant<int, (J + 1) & 3>{});
-    float gp[IT][GN][GW];
     if constexpr (READOUT) {
 #pragma unroll
       for (int i = 0; i < IT; ++i) gather_load(std::integral_constant<int, Q>{}, i, gp[i]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
-          std::integral_constant<int, T>{});
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto coop = [&](int k, auto jj, float (&gp)[IT][GN][GW]) __attribute__((always_inline)) {
+    constexpr int J = decltype(jj)::value;
+    constexpr int P = J & 1;
     if constexpr (READOUT) {
       // Readout of tile k-1 (out of range at k = 0: the stores are dropped).
 #pragma unroll
@@ -379,6 +383,38 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       prepare(k + 3, std::integral_constant<int, (J + 3) & 3>{});
       load_raw(k + 4, std::integral_constant<int, 0>{});
       load_raw(k + 5, std::integral_constant<int, 1>{});
+    }
+  };
+  auto iter = [&](int k, auto jj, auto late, const float2 (&dd)[T], float2 (&dd_next)[T]) __attribute__((always_inline)) {
+    constexpr int J = decltype(jj)::value;
+    constexpr int P = J & 1;
+    constexpr int Q = 1 - P;
+    float gp[IT][GN][GW];
+    if constexpr (decltype(late)::value) {
+      lds_reads(jj, dd_next, gp);
+      __builtin_amdgcn_sched_barrier(0);
+      coop(k, jj, gp);
+      __builtin_amdgcn_sched_barrier(0);
+      load_bc(k + 1 < nt ? k + 1 : k, std::integral_constant<int, Q>{});  // clamped: stays in SGPRs
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, 0>{},
+            std::integral_constant<int, T / 2>{});
+      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
+            std::integral_constant<int, T>{});
+    } else {
+      load_bc(k + 1 < nt ? k + 1 : k, std::integral_constant<int, Q>{});  // clamped: stays in SGPRs
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, 0>{},
+            std::integral_constant<int, T / 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      lds_reads(jj, dd_next, gp);
+      __builtin_amdgcn_sched_barrier(0);
+      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
+            std::integral_constant<int, T>{});
+      __builtin_amdgcn_sched_barrier(0);
+      coop(k, jj, gp);
     }
     __syncthreads();
   };
@@ -410,16 +446,29 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
 #pragma unroll
     for (int t = 0; t < T; ++t) ddA[t].x = __builtin_fmaf(ddA[t].x, 1.0f, 0.0f);
   }
-  int k = 0;
-  for (; k + 3 < nt; k += 4) {
-    iter(k, std::integral_constant<int, 0>{}, ddA, ddB);
-    iter(k + 1, std::integral_constant<int, 1>{}, ddB, ddA);
-    iter(k + 2, std::integral_constant<int, 2>{}, ddA, ddB);
-    iter(k + 3, std::integral_constant<int, 3>{}, ddB, ddA);
+  auto run = [&](auto late) __attribute__((always_inline)) {
+    int k = 0;
+    for (; k + 3 < nt; k += 4) {
+      iter(k, std::integral_constant<int, 0>{}, late, ddA, ddB);
+      iter(k + 1, std::integral_constant<int, 1>{}, late, ddB, ddA);
+      iter(k + 2, std::integral_constant<int, 2>{}, late, ddA, ddB);
+      iter(k + 3, std::integral_constant<int, 3>{}, late, ddB, ddA);
+    }
+    if (k < nt) iter(k, std::integral_constant<int, 0>{}, late, ddA, ddB);
+    if (k + 1 < nt) iter(k + 1, std::integral_constant<int, 1>{}, late, ddB, ddA);
+    if (k + 2 < nt) iter(k + 2, std::integral_constant<int, 2>{}, late, ddA, ddB);
+  };
+  // Two orders only where two waves of the block share each SIMD (eight
+  // waves); elsewhere the second copy of the loop would cost registers.
+  if constexpr (W == 8) {
+    if ((w & kLateWaveMask) != 0) {
+      run(std::true_type{});
+    } else {
+      run(std::false_type{});
+    }
+  } else {
+    run(std::false_type{});
   }
-  if (k < nt) iter(k, std::integral_constant<int, 0>{}, ddA, ddB);
-  if (k + 1 < nt) iter(k + 1, std::integral_constant<int, 1>{}, ddB, ddA);
-  if (k + 2 < nt) iter(k + 2, std::integral_constant<int, 2>{}, ddA, ddB);
 
   if constexpr (READOUT) {
     if (nt > 0) {
