@@ -8,9 +8,10 @@
 //
 // The state [B, d, N] float32 is read once and written once: the kernel is a
 // streaming read-modify-write bound by HBM. A row (b, d) is owned by R lanes
-// of one wave, each holding V consecutive states (V = 4 when N % 4 == 0, a
-// 16-byte nontemporal load and store); the row's readout is summed across
-// those lanes with xor shuffles inside the wave.
+// of one wave, each holding V consecutive states (V a multiple of 4 when
+// N % V == 0: V/4 16-byte nontemporal loads and stores per lane, all issued
+// before any is used, so each lane keeps V*4 bytes in flight); the row's
+// readout is summed across those lanes with xor shuffles inside the wave.
 #include <hip/hip_runtime.h>
 
 #include "device_math.h"
@@ -21,6 +22,7 @@ namespace ssm {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWideV = 16;  // states per lane when N allows
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int V, int R, bool BF16_IN, bool BF16_OUT>
@@ -44,26 +46,52 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(const UpdateArgs
   const float du = dt * x;
 
   float acc = 0.0f;
-  for (int64_t n0 = static_cast<int64_t>(j) * V; n0 < N; n0 += static_cast<int64_t>(R) * V) {
-    if (!ok) continue;
-    if constexpr (V == 4) {
-      f32x4* sp = reinterpret_cast<f32x4*>(a.state + row * N + n0);
-      f32x4 s = __builtin_nontemporal_load(sp);
-      const f32x4 av = *reinterpret_cast<const f32x4*>(a.A + ch * N + n0);
-      float bv[4], cv[4];
+  if constexpr (V % 4 == 0) {
+    // Lane j owns the 4-state chunks j, j + R, ..., j + (Q-1) R of its row:
+    // each load instruction of the R lanes covers R consecutive chunks.
+    constexpr int Q = V / 4;
+    if (ok) {
+      f32x4* sp = reinterpret_cast<f32x4*>(a.state + row * N) + j;
+      const f32x4* ap = reinterpret_cast<const f32x4*>(a.A + ch * N) + j;
+      f32x4 s[Q], av[Q];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        bv[v] = load_elem<BF16_IN>(a.B, b * N + n0 + v);
-        cv[v] = load_elem<BF16_IN>(a.C, b * N + n0 + v);
+      for (int q = 0; q < Q; ++q) s[q] = __builtin_nontemporal_load(sp + q * R);
+#pragma unroll
+      for (int q = 0; q < Q; ++q) av[q] = ap[q * R];
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int64_t n0 = 4 * (static_cast<int64_t>(q) * R + j);
+        float bv[4], cv[4];
+        if constexpr (BF16_IN) {
+          const uint16_t* bp = static_cast<const uint16_t*>(a.B) + b * N + n0;
+          const uint16_t* cp = static_cast<const uint16_t*>(a.C) + b * N + n0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            bv[v] = bf16_bits_to_f32(bp[v]);
+            cv[v] = bf16_bits_to_f32(cp[v]);
+          }
+        } else {
+          const f32x4 b4 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.B) + b * N + n0);
+          const f32x4 c4 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.C) + b * N + n0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            bv[v] = b4[v];
+            cv[v] = c4[v];
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float abar = exp2_hw(dt * (av[q][v] * kLog2e));
+          s[q][v] = fmaf(abar, s[q][v], du * bv[v]);
+          acc = fmaf(cv[v], s[q][v], acc);
+        }
       }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float abar = exp2_hw(dt * (av[v] * kLog2e));
-        s[v] = fmaf(abar, s[v], du * bv[v]);
-        acc = fmaf(cv[v], s[v], acc);
-      }
-      __builtin_nontemporal_store(s, sp);
-    } else {
+      for (int q = 0; q < Q; ++q) __builtin_nontemporal_store(s[q], sp + q * R);
+    }
+  } else {
+    for (int64_t n0 = j; n0 < N; n0 += R) {
+      if (!ok) continue;
       float* sp = a.state + row * N + n0;
       const float abar = exp2_hw(dt * (a.A[ch * N + n0] * kLog2e));
       const float s = fmaf(abar, *sp, du * load_elem<BF16_IN>(a.B, b * N + n0));
@@ -93,7 +121,8 @@ int launch_vr(const UpdateArgs& a, hipStream_t st) {
                          dim3(static_cast<unsigned>(blocks)), dim3(kThreads), kargs, 0, st);
 }
 
-// Lanes per row: enough to cover N with V states each, a power of two <= 64.
+// Lanes per row: enough to cover N with V states each, a power of two <= 64
+// (the wide paths need N == R * V exactly; the scalar path loops).
 template <int V, bool BI, bool BO>
 int launch_v(const UpdateArgs& a, hipStream_t st) {
   const int64_t need = (a.dstate + V - 1) / V;
@@ -106,12 +135,17 @@ int launch_v(const UpdateArgs& a, hipStream_t st) {
   return launch_vr<V, 64, BI, BO>(a, st);
 }
 
-// 16-byte state/A accesses need N % 4 == 0 and 16-byte aligned bases.
+// 16-byte state/A/B/C accesses need N % V == 0 and 16-byte aligned bases
+// (B and C: 16-byte aligned by the ABI; their rows then stay aligned when
+// N * element size is a multiple of 16).
 template <bool BI, bool BO>
 int launch_io(const UpdateArgs& a, hipStream_t st) {
-  const bool vec4 = a.dstate % 4 == 0 && reinterpret_cast<uintptr_t>(a.state) % 16 == 0 &&
-                    reinterpret_cast<uintptr_t>(a.A) % 16 == 0;
-  return vec4 ? launch_v<4, BI, BO>(a, st) : launch_v<1, BI, BO>(a, st);
+  const bool base16 = reinterpret_cast<uintptr_t>(a.state) % 16 == 0 &&
+                      reinterpret_cast<uintptr_t>(a.A) % 16 == 0;
+  const bool pow2 = (a.dstate & (a.dstate - 1)) == 0;
+  if (base16 && pow2 && a.dstate >= kWideV && a.dstate / kWideV <= 64) return launch_v<kWideV, BI, BO>(a, st);
+  if (base16 && pow2 && a.dstate >= 4 && a.dstate / 4 <= 64) return launch_v<4, BI, BO>(a, st);
+  return launch_v<1, BI, BO>(a, st);
 }
 
 }  // namespace
