@@ -200,6 +200,7 @@ def bench_decode(args, torch, binding, synth):
     us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
     state_b, alg_b = decode_alg_bytes(w.batch, w.dim, w.dstate)
     gbs = alg_b / (us * 1e-6) / 1e9
+    traffic = counter_traffic("state_update_decode_counters.md", kernel_source_hash())
     return {
         "workload": f"{w.name} (batch={w.batch}, d_inner={w.dim}, N={w.dstate}, f32, "
                     f"{args.decode_steps} chained steps, same token)",
@@ -207,7 +208,7 @@ def bench_decode(args, torch, binding, synth):
         "state_GBps": state_b / (us * 1e-6) / 1e9,
         "G_updates_per_s": w.batch * w.dim * w.dstate / (us * 1e-6) / 1e9,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_BPS / 1e9, "unit": "GB/s",
-                     "frac": gbs / (HBM_BPS / 1e9), "traffic": None,
+                     "frac": gbs / (HBM_BPS / 1e9), "traffic": traffic,
                      "alg_bytes_per_launch": alg_b},
     }
 
