@@ -18,6 +18,7 @@ Sources, cited by tag throughout:
 - [Notes]       lyirs.cc, "Mamba" (study notes on Gu & Dao 2023).
 """
 
+from .conv_oracle import causal_conv1d, causal_conv1d_update  # noqa: F401
 from .ssm_oracle import (  # noqa: F401
     softplus,
     silu,

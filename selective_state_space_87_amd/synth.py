@@ -14,6 +14,10 @@ Recipe (the same for every workload; the sizes differ):
   float64, cast to float32. With softplus on and delta_raw ~ N(0,1), each
   channel's median step is log-uniform in [lo, hi].
 - Decode state: 0.1 * N(0, 1), float32.
+- Convolution before the scan (width K): x ~ N(0, 1) in the storage dtype;
+  weight [d, K] and bias [d] ~ U(-1/sqrt(K), 1/sqrt(K)) float32 (the range a
+  Conv1d module with one input channel per group starts from); carried
+  state [B, d, K-1] ~ N(0, 1) float32.
 - bf16 tensors are float32 draws rounded to nearest-even. On the host they
   are kept as uint16 bit patterns, so both sides see the exact same values.
 
@@ -32,6 +36,7 @@ import numpy as np
 
 BLOCK = 4096
 TID_DT, TID_U, TID_DELTA, TID_B, TID_C, TID_Z, TID_STATE = range(7)
+TID_CONV_X, TID_CONV_W, TID_CONV_BIAS, TID_CONV_STATE = range(7, 11)
 
 
 @dataclass(frozen=True)
@@ -173,6 +178,19 @@ def make_decode_inputs(batch, dim, dstate, in_dtype="f32", dt_range=(1e-3, 1e-1)
                 A=s4d_real_A(dim, dstate), D=np.ones(dim, dtype=np.float32),
                 delta_bias=delta_bias_for(dim, dt_range, seed, stream),
                 in_dtype=in_dtype, delta_softplus=True)
+
+
+def make_conv_inputs(batch, seqlen, dim, width, in_dtype="f32", seed=0, stream=400, with_state=True):
+    """Inputs of the causal conv1d: x [B, L, d] in ``in_dtype``; weight [d, K],
+    bias [d] and (optionally) state [B, d, K-1] float32."""
+    x = _normal_blocks(seed, stream, TID_CONV_X, batch, seqlen, dim, dtype=in_dtype)
+    bound = 1.0 / np.sqrt(width)
+    w = _rng(seed, stream, TID_CONV_W).uniform(-bound, bound, size=(dim, width)).astype(np.float32)
+    bias = _rng(seed, stream, TID_CONV_BIAS).uniform(-bound, bound, size=dim).astype(np.float32)
+    state = None
+    if with_state:
+        state = _normal_blocks(seed, stream, TID_CONV_STATE, batch, dim, width - 1)
+    return dict(x=x, weight=w, bias=bias, state=state, in_dtype=in_dtype)
 
 
 def workload_inputs(i: int, seed: int = 0):
