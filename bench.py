@@ -225,6 +225,64 @@ def copy_calibration(torch, mib):
     del src, dst
 
 
+def conv_alg_bytes(B, L, d, K, in_bytes, out_bytes):
+    """x read once, y written once, weight + bias, carried state read and written."""
+    return B * L * d * (in_bytes + out_bytes) + d * K * 4 + d * 4 + 2 * B * d * (K - 1) * 4
+
+
+def _timed(torch, fn, reps, warm):
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps  # microseconds
+
+
+def hbm_roofline(alg_b, us, traffic=None):
+    gbs = alg_b / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_BPS / 1e9, "unit": "GB/s",
+            "frac": gbs / (HBM_BPS / 1e9), "traffic": traffic, "alg_bytes_per_launch": alg_b}
+
+
+def bench_conv(args, torch, binding, synth):
+    """The causal depthwise conv1d + SiLU before the scan (1.4B-shaped layer, width 4,
+    bf16 in and out, state carried in and out) and its decode update (batch 128,
+    d_inner 4096, width 4, float32)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    B, L, d, K = 4, 8192, 4096, 4
+    ci = synth.make_conv_inputs(B, L, d, K, "bf16", seed=0, stream=700)
+    x = torch.from_numpy(ci["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(ci["weight"]).to(dev)
+    bias = torch.from_numpy(ci["bias"]).to(dev)
+    s_in = torch.from_numpy(ci["state"]).to(dev)
+    y = torch.empty_like(x)
+    s_out = torch.empty_like(s_in)
+    us = _timed(torch, lambda: binding.ssm_causal_conv1d_fwd(x, w, bias, s_in, y=y, state_out=s_out),
+                args.conv_steps, 10)
+    alg = conv_alg_bytes(B, L, d, K, 2, 2)
+    fwd = {"workload": f"causal conv1d + SiLU (batch={B}, seqlen={L}, d_inner={d}, width={K}, bf16 in/out, "
+                       f"state in/out)", "us_per_call": us,
+           "roofline": hbm_roofline(alg, us, counter_traffic("conv1d_mamba14b_counters.md", kernel_source_hash()))}
+    del x, y
+    Bd = 128
+    ui = synth.make_conv_inputs(Bd, 1, d, K, "f32", seed=0, stream=701)
+    xs = torch.from_numpy(ui["x"][:, 0]).to(dev)
+    st = torch.from_numpy(ui["state"]).to(dev)
+    yu = torch.empty_like(xs)
+    us_u = _timed(torch, lambda: binding.ssm_causal_conv1d_update(st, xs, w, bias, y=yu), 1000, 20)
+    alg_u = Bd * d * 8 + d * K * 4 + d * 4 + 2 * Bd * d * (K - 1) * 4
+    upd = {"workload": f"causal conv1d update (batch={Bd}, d_inner={d}, width={K}, float32, 1000 chained steps)",
+           "us_per_step": us_u, "roofline": hbm_roofline(alg_u, us_u)}
+    return fwd, upd
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +293,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--conv-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=8192)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -299,6 +359,8 @@ def main():
     }
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, binding, synth)
+    if not args.no_conv:
+        result["conv1d"], result["conv1d_update"] = bench_conv(args, torch, binding, synth)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_steps)
     else:

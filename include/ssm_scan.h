@@ -158,6 +158,57 @@ int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
                                const float* D, const void* z, const float* delta_bias,
                                void* y, void* stream);
 
+/*
+ * Causal depthwise conv1d (+ SiLU) over a sequence: the short local
+ * convolution that precedes the selective scan in the block ("从 Transformer
+ * 到 Mamba", ybb.press, section 5: depthwise Conv1d of width d_conv padded by
+ * width-1 and cut to the first L outputs, then SiLU; lyirs.cc notes, "Mamba
+ * block 的结构" and the fixed-size conv_state kept between tokens).
+ *
+ *   out[b,l,d] = bias[d] + sum_{k<K} weight[d,k] * x[b, l-(K-1)+k, d]
+ *   y[b,l,d]   = silu(out) if silu_activation, else out
+ *
+ * Inputs before step 0 are state_in[b,d,j] = x[b, j-(K-1), d] (oldest first),
+ * or zero when state_in is NULL. state_out receives the last K-1 inputs the
+ * same way (some from state_in when L < K-1), ready for the next call or for
+ * ssm_causal_conv1d_update.
+ *
+ *   batch, seqlen, dim, width  : B >= 0, 0 <= L <= 4194240, d >= 0,
+ *                                1 <= K <= 8; B <= 65535 (else
+ *                                SSM_E_UNSUPPORTED).
+ *   in_dtype, out_dtype        : 0 float32, 1 bfloat16 (x / y).
+ *   x         [B, L, d]  in_dtype   input (may be NULL when L = 0)
+ *   weight    [d, K]     float32    filter; weight[d, K-1] meets the newest input
+ *   bias      [d]        float32    (optional, 0)
+ *   state_in  [B, d, K-1] float32   (optional, zeros)
+ *   y         [B, L, d]  out_dtype  output; must not overlap any input
+ *   state_out [B, d, K-1] float32   (optional); must not overlap y or any
+ *                                   input, state_in included
+ *   stream                          hipStream_t
+ * x and y must be 16-byte aligned; float32 arrays 4-byte aligned.
+ */
+int ssm_causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                          int in_dtype, int out_dtype, int silu_activation,
+                          const void* x, const float* weight, const float* bias,
+                          const float* state_in, void* y, float* state_out, void* stream);
+
+/*
+ * Decode: one token through the convolution, updating the carried state in
+ * place (the conv_state of the lyirs.cc notes; the per-token step of ybb.press
+ * section 6.3). Equal to ssm_causal_conv1d_fwd with L = 1, state_in = state
+ * and state_out = state.
+ *
+ *   batch, dim, width          : B >= 0, d >= 0, 1 <= K <= 8.
+ *   state     [B, d, K-1] float32   read, then overwritten (may be NULL when K = 1)
+ *   x         [B, d]     in_dtype
+ *   weight    [d, K], bias [d] (optional)   float32
+ *   y         [B, d]     out_dtype  must not overlap state or inputs
+ */
+int ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width,
+                             int in_dtype, int out_dtype, int silu_activation,
+                             float* state, const void* x, const float* weight, const float* bias,
+                             void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,6 +8,8 @@ unloadable library raises at once.
 
 from .binding import (  # noqa: F401
     ssm_abi_version,
+    ssm_causal_conv1d_fwd,
+    ssm_causal_conv1d_update,
     ssm_scan_chunks,
     ssm_scan_workspace_bytes,
     ssm_selective_scan_fwd,

@@ -62,6 +62,12 @@ def _load():
         lib.ssm_selective_state_update.argtypes = [i64, i64, i64, i32, i32, i32,
                                                    vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                    vp, vp]
+        lib.ssm_causal_conv1d_fwd.restype = i32
+        lib.ssm_causal_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32, i32, i32,
+                                              vp, vp, vp, vp, vp, vp, vp]
+        lib.ssm_causal_conv1d_update.restype = i32
+        lib.ssm_causal_conv1d_update.argtypes = [i64, i64, i64, i32, i32, i32,
+                                                 vp, vp, vp, vp, vp, vp]
         _lib = lib
         return lib
 
@@ -214,4 +220,79 @@ def ssm_selective_state_update(state, x, delta, A, B, C, D=None, z=None, delta_b
             _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), _ptr(y), _stream_handle(stream, dev))
     _check("ssm_selective_state_update", st)
+    return y
+
+
+def ssm_causal_conv1d_fwd(x, weight, bias=None, state_in=None, silu_activation=True, out_dtype=None,
+                          return_final_state=False, y=None, state_out=None, stream=None):
+    """Causal depthwise conv1d (+ SiLU); see ssm_causal_conv1d_fwd in include/ssm_scan.h.
+
+    x: [B, L, d] float32 or bfloat16; weight: [d, K], bias: [d], state_in: [B, d, K-1]
+    (float32). Returns y ([B, L, d]) or (y, state_out).
+    """
+    lib = _load()
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a 3-d tensor [B, L, d]")
+    if x.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported input dtype {x.dtype}")
+    dev = x.device
+    Bt, L, d = x.shape
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise ValueError("weight must be a 2-d tensor [d, K]")
+    K = weight.shape[1]
+    _dev_tensor("x", x, (Bt, L, d), (x.dtype,), dev)
+    _dev_tensor("weight", weight, (d, K), (torch.float32,), dev)
+    _dev_tensor("bias", bias, (d,), (torch.float32,), dev)
+    _dev_tensor("state_in", state_in, (Bt, d, K - 1), (torch.float32,), dev)
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    if y is None:
+        y = torch.empty((Bt, L, d), dtype=out_dtype, device=dev)
+    _dev_tensor("y", y, (Bt, L, d), (out_dtype,), dev)
+    if return_final_state and state_out is None:
+        state_out = torch.empty((Bt, d, K - 1), dtype=torch.float32, device=dev)
+    _dev_tensor("state_out", state_out, (Bt, d, K - 1), (torch.float32,), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssm_causal_conv1d_fwd(Bt, L, d, K, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype],
+                                       int(bool(silu_activation)), _ptr(x), _ptr(weight), _ptr(bias),
+                                       _ptr(state_in), _ptr(y), _ptr(state_out), _stream_handle(stream, dev))
+    _check("ssm_causal_conv1d_fwd", st)
+    if return_final_state or state_out is not None:
+        return y, state_out
+    return y
+
+
+def ssm_causal_conv1d_update(state, x, weight, bias=None, silu_activation=True, out_dtype=None,
+                             y=None, stream=None):
+    """One token through the convolution, state updated in place; see
+    ssm_causal_conv1d_update in include/ssm_scan.h.
+
+    state: [B, d, K-1] float32 (in place); x: [B, d]; weight: [d, K], bias: [d].
+    Returns y [B, d].
+    """
+    lib = _load()
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.dtype not in _DTYPE_CODE:
+        raise ValueError("x must be a 2-d float32 or bfloat16 tensor [B, d]")
+    dev = x.device
+    Bt, d = x.shape
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise ValueError("weight must be a 2-d tensor [d, K]")
+    K = weight.shape[1]
+    _dev_tensor("x", x, (Bt, d), (x.dtype,), dev)
+    _dev_tensor("weight", weight, (d, K), (torch.float32,), dev)
+    _dev_tensor("bias", bias, (d,), (torch.float32,), dev)
+    if K > 1 or state is not None:
+        _dev_tensor("state", state, (Bt, d, K - 1), (torch.float32,), dev)
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    if y is None:
+        y = torch.empty((Bt, d), dtype=out_dtype, device=dev)
+    _dev_tensor("y", y, (Bt, d), (out_dtype,), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssm_causal_conv1d_update(Bt, d, K, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype],
+                                          int(bool(silu_activation)), _ptr(state), _ptr(x), _ptr(weight),
+                                          _ptr(bias), _ptr(y), _stream_handle(stream, dev))
+    _check("ssm_causal_conv1d_update", st)
     return y

@@ -12,6 +12,8 @@ namespace {
 constexpr int64_t kMaxScanState = 64;
 constexpr int64_t kMaxDecodeState = 256;
 constexpr int64_t kMaxElems = int64_t(1) << 52;
+constexpr int64_t kMaxConvWidth = 8;
+constexpr int64_t kMaxConvSeq = int64_t(65535) * 64;  // 65535 segments of 64 steps
 
 struct Range {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -210,6 +212,96 @@ int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
   a.out_bf16 = out_dtype;
   a.delta_softplus = delta_softplus ? 1 : 0;
   return map_hip(ssm::launch_state_update(a, stream));
+}
+
+int ssm_causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                          int in_dtype, int out_dtype, int silu_activation,
+                          const void* x, const float* weight, const float* bias,
+                          const float* state_in, void* y, float* state_out, void* stream) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || width < 1) return SSM_E_SHAPE;
+  if (width > kMaxConvWidth || batch > 65535 || seqlen > kMaxConvSeq) return SSM_E_UNSUPPORTED;
+  if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return SSM_E_DTYPE;
+  int64_t bl, bld, bd, bds, dk;
+  if (!safe_mul(batch, seqlen, &bl) || !safe_mul(bl, dim, &bld) || !safe_mul(batch, dim, &bd) ||
+      !safe_mul(bd, width - 1, &bds) || !safe_mul(dim, width, &dk)) {
+    return SSM_E_SHAPE;
+  }
+  if (batch == 0 || dim == 0) return SSM_OK;
+  if (weight == nullptr) return SSM_E_NULLPTR;
+  if (seqlen > 0 && (x == nullptr || y == nullptr)) return SSM_E_NULLPTR;
+  if ((x && !aligned(x, 16)) || (y && !aligned(y, 16))) return SSM_E_ALIGN;
+  const void* f32_ptrs[] = {weight, bias, state_in, state_out};
+  for (const void* p : f32_ptrs) {
+    if (p && !aligned(p, 4)) return SSM_E_ALIGN;
+  }
+  const int64_t isz = in_dtype == 1 ? 2 : 4, osz = out_dtype == 1 ? 2 : 4;
+  const Range ry = span(y, seqlen > 0 ? bld : 0, osz);
+  const Range rso = span(state_out, bds, 4);
+  const Range inputs[] = {span(x, bld, isz), span(weight, dk, 4), span(bias, dim, 4), span(state_in, bds, 4)};
+  for (const Range& r : inputs) {
+    if (overlaps(ry, r) || overlaps(rso, r)) return SSM_E_ALIAS;
+  }
+  if (overlaps(ry, rso)) return SSM_E_ALIAS;
+
+  ssm::ConvArgs a;
+  a.x = x;
+  a.weight = weight;
+  a.bias = bias;
+  a.state_in = state_in;
+  a.y = y;
+  a.state_out = state_out;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.dim = dim;
+  a.width = width;
+  a.in_bf16 = in_dtype;
+  a.out_bf16 = out_dtype;
+  a.silu = silu_activation ? 1 : 0;
+  return map_hip(ssm::launch_conv1d_fwd(a, stream));
+}
+
+int ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width,
+                             int in_dtype, int out_dtype, int silu_activation,
+                             float* state, const void* x, const float* weight, const float* bias,
+                             void* y, void* stream) {
+  if (batch < 0 || dim < 0 || width < 1) return SSM_E_SHAPE;
+  if (width > kMaxConvWidth) return SSM_E_UNSUPPORTED;
+  if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return SSM_E_DTYPE;
+  int64_t bd, bds, dk;
+  if (!safe_mul(batch, dim, &bd) || !safe_mul(bd, width - 1, &bds) || !safe_mul(dim, width, &dk)) {
+    return SSM_E_SHAPE;
+  }
+  if (bd == 0) return SSM_OK;
+  if (x == nullptr || weight == nullptr || y == nullptr || (width > 1 && state == nullptr)) {
+    return SSM_E_NULLPTR;
+  }
+  if (!aligned(x, 16) || !aligned(y, 16)) return SSM_E_ALIGN;
+  const void* f32_ptrs[] = {state, weight, bias};
+  for (const void* p : f32_ptrs) {
+    if (p && !aligned(p, 4)) return SSM_E_ALIGN;
+  }
+  const int64_t isz = in_dtype == 1 ? 2 : 4, osz = out_dtype == 1 ? 2 : 4;
+  const Range ry = span(y, bd, osz);
+  const Range rs = span(state, bds, 4);
+  const Range inputs[] = {span(x, bd, isz), span(weight, dk, 4), span(bias, dim, 4)};
+  for (const Range& r : inputs) {
+    if (overlaps(ry, r) || overlaps(rs, r)) return SSM_E_ALIAS;
+  }
+  if (overlaps(ry, rs)) return SSM_E_ALIAS;
+
+  ssm::ConvUpdateArgs a;
+  a.state = state;
+  a.x = x;
+  a.weight = weight;
+  a.bias = bias;
+  a.y = y;
+  a.batch = batch;
+  a.dim = dim;
+  a.width = width;
+  a.in_bf16 = in_dtype;
+  a.out_bf16 = out_dtype;
+  a.silu = silu_activation ? 1 : 0;
+  return map_hip(ssm::launch_conv1d_update(a, stream));
 }
 
 }  // extern "C"

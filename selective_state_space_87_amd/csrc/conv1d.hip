@@ -1,0 +1,227 @@
+// Causal depthwise conv1d + SiLU before the selective scan, and its decode
+// update, for gfx950.
+//
+// Per batch b, channel d, step l, filter width K ("从 Transformer 到 Mamba",
+// ybb.press, section 5: the block's depthwise Conv1d padded by K-1 and cut to
+// the first L outputs, then SiLU; the lyirs.cc "Mamba" notes, block structure
+// and the fixed-size conv_state kept between tokens):
+//   out = bias[d] + sum_k weight[d, k] * x[b, l-(K-1)+k, d];  y = silu(out)
+// Inputs before step 0 come from the carried state [B, d, K-1] (oldest first)
+// or are zero; the state after the sequence holds its last K-1 inputs.
+//
+// Both kernels are HBM-bound streams (x read once, y written once). The
+// sequence kernel gives each thread VC = 4 adjacent channels (one 8- or
+// 16-byte load per step, consecutive across the wave's lanes) and a segment of
+// kSeg steps, walked with a circular register window: the input of step t
+// sits in slot t mod KM, so after unrolling by KM nothing moves between
+// registers. Filters are applied at a compile-time width KM (4 or 8) with the
+// weights right-aligned and zero-padded in front.
+#include <hip/hip_runtime.h>
+
+#include "device_math.h"
+#include "kernels.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kSeg = 64;      // steps per thread
+constexpr int kBlock = 256;   // threads per block (channel groups)
+
+template <int VC, bool BF16>
+__device__ __forceinline__ void load_vec(const void* base, int64_t i, float (&v)[VC]) {
+  if constexpr (VC == 4 && BF16) {
+    const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
+    v[0] = __uint_as_float(r.x << 16);
+    v[1] = __uint_as_float(r.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.y << 16);
+    v[3] = __uint_as_float(r.y & 0xffff0000u);
+  } else if constexpr (VC == 4) {
+    const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+    v[0] = r.x;
+    v[1] = r.y;
+    v[2] = r.z;
+    v[3] = r.w;
+  } else {
+#pragma unroll
+    for (int c = 0; c < VC; ++c) v[c] = load_elem<BF16>(base, i + c);
+  }
+}
+
+template <int VC, bool BF16>
+__device__ __forceinline__ void store_vec(void* base, int64_t i, const float (&v)[VC]) {
+  if constexpr (VC == 4 && BF16) {
+    uint2 r;
+    r.x = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+    r.y = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + i) = r;
+  } else if constexpr (VC == 4) {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + i) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < VC; ++c) store_elem<BF16>(base, i + c, v[c]);
+  }
+}
+
+template <int KM, int VC, bool BI, bool BO, bool SILU>
+__global__ __launch_bounds__(kBlock) void conv1d_fwd_kernel(const ConvArgs a) {
+  static_assert(kSeg % KM == 0, "segment must be a multiple of the window");
+  const int64_t L = a.seqlen, Dm = a.dim;
+  const int K = static_cast<int>(a.width);
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * VC;
+  if (c0 >= Dm) return;
+  const int64_t b = blockIdx.z;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kSeg;
+  const int64_t row0 = b * L;  // first row of this batch in [B, L, d]
+
+  // Right-aligned, zero-padded weights and the bias of this thread's channels.
+  float wp[KM][VC], bv[VC];
+#pragma unroll
+  for (int c = 0; c < VC; ++c) {
+    bv[c] = a.bias ? a.bias[c0 + c] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < KM; ++i) {
+      const int k = i - (KM - K);
+      wp[i][c] = k >= 0 ? a.weight[(c0 + c) * K + k] : 0.0f;
+    }
+  }
+
+  // Input at step t (t may be negative: carried state, or zero).
+  auto input = [&](int64_t t, float (&v)[VC]) __attribute__((always_inline)) {
+    if (t >= 0) {
+      load_vec<VC, BI>(a.x, (row0 + t) * Dm + c0, v);
+    } else {
+      const int64_t j = (K - 1) + t;  // state slot, oldest first
+#pragma unroll
+      for (int c = 0; c < VC; ++c) {
+        v[c] = (a.state_in && j >= 0) ? a.state_in[((b * Dm) + c0 + c) * (K - 1) + j] : 0.0f;
+      }
+    }
+  };
+
+  // Window: slot s holds the input of the step congruent to s modulo KM.
+  float win[KM][VC];
+#pragma unroll
+  for (int j = 0; j < KM - 1; ++j) {
+    // steps t0-KM+1 .. t0-1 go to slots 1 .. KM-1
+    input(t0 - (KM - 1) + j, win[1 + j]);
+  }
+  const int64_t t_end = min(t0 + kSeg, L);
+  for (int64_t tb = t0; tb < t_end; tb += KM) {
+#pragma unroll
+    for (int u = 0; u < KM; ++u) {
+      const int64_t t = tb + u;
+      if (t < t_end) {
+        input(t, win[u]);
+        float out[VC];
+#pragma unroll
+        for (int c = 0; c < VC; ++c) {
+          float acc = bv[c];
+#pragma unroll
+          for (int i = 0; i < KM; ++i) acc = fmaf(wp[i][c], win[(u + 1 + i) % KM][c], acc);
+          out[c] = SILU ? silu_f(acc) : acc;
+        }
+        store_vec<VC, BO>(a.y, (row0 + t) * Dm + c0, out);
+      }
+    }
+  }
+
+  // The thread holding the last step writes the carried-out state: inputs
+  // L-(K-1) .. L-1 (some from the carried-in state when L < K-1).
+  const int64_t last_seg = L > 0 ? (L - 1) / kSeg : 0;
+  if (a.state_out && K > 1 && static_cast<int64_t>(blockIdx.y) == last_seg) {
+    for (int j = 0; j < K - 1; ++j) {
+      float v[VC];
+      input(L - (K - 1) + j, v);
+#pragma unroll
+      for (int c = 0; c < VC; ++c) a.state_out[((b * Dm) + c0 + c) * (K - 1) + j] = v[c];
+    }
+  }
+}
+
+template <int KM, bool BI, bool BO, bool SILU>
+__global__ __launch_bounds__(kBlock) void conv1d_update_kernel(const ConvUpdateArgs a) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t rows = a.batch * a.dim;
+  if (i >= rows) return;
+  const int64_t ch = i % a.dim;
+  const int K = static_cast<int>(a.width);
+  float* st = a.state + i * (K - 1);
+  // Window of KM inputs, newest last: state (oldest first) then x.
+  float win[KM], wp[KM];
+#pragma unroll
+  for (int s = 0; s < KM; ++s) {
+    const int k = s - (KM - K);  // filter tap and, below KM-1, state slot
+    wp[s] = k >= 0 ? a.weight[ch * K + k] : 0.0f;
+    if (s < KM - 1) win[s] = k >= 0 ? st[k] : 0.0f;
+  }
+  win[KM - 1] = load_elem<BI>(a.x, i);
+  float acc = a.bias ? a.bias[ch] : 0.0f;
+#pragma unroll
+  for (int s = 0; s < KM; ++s) acc = fmaf(wp[s], win[s], acc);
+  // New state: the last K-1 inputs, oldest first.
+#pragma unroll
+  for (int s = 1; s < KM; ++s) {
+    const int j = s - (KM - K) - 1;
+    if (j >= 0) st[j] = win[s];
+  }
+  store_elem<BO>(a.y, i, SILU ? silu_f(acc) : acc);
+}
+
+template <int KM, int VC, bool BI, bool BO>
+int launch_fwd_k(const ConvArgs& a, hipStream_t st) {
+  const int64_t groups = (a.dim + VC - 1) / VC;
+  const int64_t gx = (groups + kBlock - 1) / kBlock;
+  const int64_t gy = a.seqlen > 0 ? (a.seqlen + kSeg - 1) / kSeg : 1;
+  if (gx > 0x7fffffff || gy > 65535 || a.batch > 65535) return hipErrorInvalidConfiguration;
+  ConvArgs args = a;
+  void* kargs[] = {&args};
+  const void* fn = a.silu ? reinterpret_cast<const void*>(&conv1d_fwd_kernel<KM, VC, BI, BO, true>)
+                          : reinterpret_cast<const void*>(&conv1d_fwd_kernel<KM, VC, BI, BO, false>);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy),
+                                  static_cast<unsigned>(a.batch)),
+                         dim3(kBlock), kargs, 0, st);
+}
+
+template <bool BI, bool BO>
+int launch_fwd_io(const ConvArgs& a, hipStream_t st) {
+  // Four channels per thread when rows stay aligned for 8/16-byte accesses.
+  const bool vec = a.dim % 4 == 0;
+  if (a.width <= 4) return vec ? launch_fwd_k<4, 4, BI, BO>(a, st) : launch_fwd_k<4, 1, BI, BO>(a, st);
+  return vec ? launch_fwd_k<8, 4, BI, BO>(a, st) : launch_fwd_k<8, 1, BI, BO>(a, st);
+}
+
+template <int KM, bool BI, bool BO>
+int launch_upd_k(const ConvUpdateArgs& a, hipStream_t st) {
+  const int64_t rows = a.batch * a.dim;
+  const int64_t blocks = (rows + kBlock - 1) / kBlock;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  ConvUpdateArgs args = a;
+  void* kargs[] = {&args};
+  const void* fn = a.silu ? reinterpret_cast<const void*>(&conv1d_update_kernel<KM, BI, BO, true>)
+                          : reinterpret_cast<const void*>(&conv1d_update_kernel<KM, BI, BO, false>);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), kargs, 0, st);
+}
+
+template <bool BI, bool BO>
+int launch_upd_io(const ConvUpdateArgs& a, hipStream_t st) {
+  return a.width <= 4 ? launch_upd_k<4, BI, BO>(a, st) : launch_upd_k<8, BI, BO>(a, st);
+}
+
+}  // namespace
+
+int launch_conv1d_fwd(const ConvArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.batch == 0 || a.dim == 0) return 0;
+  if (a.in_bf16) return a.out_bf16 ? launch_fwd_io<true, true>(a, st) : launch_fwd_io<true, false>(a, st);
+  return a.out_bf16 ? launch_fwd_io<false, true>(a, st) : launch_fwd_io<false, false>(a, st);
+}
+
+int launch_conv1d_update(const ConvUpdateArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.batch == 0 || a.dim == 0) return 0;
+  if (a.in_bf16) return a.out_bf16 ? launch_upd_io<true, true>(a, st) : launch_upd_io<true, false>(a, st);
+  return a.out_bf16 ? launch_upd_io<false, true>(a, st) : launch_upd_io<false, false>(a, st);
+}
+
+}  // namespace ssm

@@ -39,6 +39,27 @@ struct UpdateArgs {
   int in_bf16, out_bf16, delta_softplus;
 };
 
+struct ConvArgs {
+  const void* x;
+  const float* weight;
+  const float* bias;
+  const float* state_in;
+  void* y;
+  float* state_out;
+  int64_t batch, seqlen, dim, width;
+  int in_bf16, out_bf16, silu;
+};
+
+struct ConvUpdateArgs {
+  float* state;
+  const void* x;
+  const float* weight;
+  const float* bias;
+  void* y;
+  int64_t batch, dim, width;
+  int in_bf16, out_bf16, silu;
+};
+
 // How a scan of a given shape is run. The sequence is split into `chunks`
 // pieces of `chunk` steps (the last may be shorter) when there are too few
 // channel blocks to fill the device, or when one batch row's [L, d] plane is
@@ -71,5 +92,7 @@ size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
 // validated. Return 0 or the HIP error code of the failing launch.
 int launch_scan(const ScanArgs& a, void* stream);
 int launch_state_update(const UpdateArgs& a, void* stream);
+int launch_conv1d_fwd(const ConvArgs& a, void* stream);
+int launch_conv1d_update(const ConvUpdateArgs& a, void* stream);
 
 }  // namespace ssm

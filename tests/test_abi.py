@@ -156,3 +156,37 @@ def test_python_binding_rejects_cpu_tensors():
     A = torch.zeros(2, 4)
     with pytest.raises(ValueError, match="device tensor"):
         binding.ssm_selective_scan_fwd(u, u, A, torch.zeros(1, 4, 4), torch.zeros(1, 4, 4))
+
+
+def conv(lib, B=2, L=8, d=4, K=4, ind=0, outd=0, silu=1, x=P, w=2 * P, bias=3 * P, sin=4 * P, y=5 * P, sout=6 * P):
+    return lib.ssm_causal_conv1d_fwd(B, L, d, K, ind, outd, silu, vp(x), vp(w), vp(bias), vp(sin), vp(y),
+                                     vp(sout), None)
+
+
+def conv_upd(lib, B=2, d=4, K=4, ind=0, outd=0, silu=1, state=P, x=2 * P, w=3 * P, bias=4 * P, y=5 * P):
+    return lib.ssm_causal_conv1d_update(B, d, K, ind, outd, silu, vp(state), vp(x), vp(w), vp(bias), vp(y), None)
+
+
+def test_conv_validation(lib):
+    assert conv(lib, B=-1) == E_SHAPE
+    assert conv(lib, K=0) == E_SHAPE
+    assert conv(lib, K=9) == E_UNSUPPORTED
+    assert conv(lib, B=65536) == E_UNSUPPORTED
+    assert conv(lib, L=65535 * 64 + 1) == E_UNSUPPORTED
+    assert conv(lib, ind=3) == E_DTYPE
+    assert conv(lib, w=None) == E_NULLPTR
+    assert conv(lib, x=None) == E_NULLPTR
+    assert conv(lib, y=None) == E_NULLPTR
+    assert conv(lib, x=P + 8) == E_ALIGN
+    assert conv(lib, w=2 * P + 2) == E_ALIGN
+    assert conv(lib, y=P) == E_ALIAS                  # y == x
+    assert conv(lib, sout=4 * P) == E_ALIAS           # state_out == state_in
+    assert conv(lib, sout=5 * P + 16) == E_ALIAS      # state_out inside y
+    assert conv(lib, B=0, x=None, y=None, w=None) == OK
+    assert conv_upd(lib, K=9) == E_UNSUPPORTED
+    assert conv_upd(lib, state=None) == E_NULLPTR
+    assert conv_upd(lib, y=None) == E_NULLPTR
+    assert conv_upd(lib, x=2 * P + 4) == E_ALIGN
+    assert conv_upd(lib, y=P + 16) == E_ALIAS         # y inside state
+    assert conv_upd(lib, state=3 * P) == E_ALIAS      # state over weight
+    assert conv_upd(lib, B=0, state=None, x=None, y=None) == OK

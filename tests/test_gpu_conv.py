@@ -1,0 +1,147 @@
+"""GPU parity of the causal depthwise conv1d (+ SiLU) and its decode update
+against the float64 oracle, through the C ABI.
+
+Scaled error: |y - y_ref| / m, where m is the magnitude companion of the
+pre-activation (the same convolution on |x|, |w|, |bias|, |state|; SiLU is
+1.1-Lipschitz, so m bounds the error budget of y as well).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from selective_state_space_87_amd import binding, synth
+from tests.gpu_util import download, tol_for, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+
+
+def report(name, err, tol):
+    print(f"[parity] {name}: scaled error {err:.3e} (tol {tol:.1e})", flush=True)
+    assert err <= tol, f"{name}: scaled error {err:.3e} > {tol:.1e}"
+
+
+def dev_inputs(inp):
+    dt = inp["in_dtype"]
+    return dict(x=upload(inp["x"], dt), weight=upload(inp["weight"], "f32"), bias=upload(inp["bias"], "f32"),
+                state=None if inp["state"] is None else upload(inp["state"], "f32"))
+
+
+def oracle_conv(inp, use_state=True, use_bias=True, silu=True, channels=None):
+    f = synth.as_float64(inp)
+    sl = slice(None) if channels is None else np.asarray(channels)
+    x, w = f["x"][:, :, sl], f["weight"][sl]
+    b = f["bias"][sl] if use_bias else None
+    st = f["state"][:, sl] if (use_state and f.get("state") is not None) else None
+    y, s = oracle.causal_conv1d(x, w, b, silu, st)
+    m, _ = oracle.causal_conv1d(np.abs(x), np.abs(w), None if b is None else np.abs(b), False,
+                                None if st is None else np.abs(st))
+    return y, s, m
+
+
+def check(name, inp, out_dtype="f32", use_state=True, use_bias=True, silu=True, channels=None):
+    dv = dev_inputs(inp)
+    y, so = binding.ssm_causal_conv1d_fwd(dv["x"], dv["weight"], dv["bias"] if use_bias else None,
+                                          dv["state"] if use_state else None, silu_activation=silu,
+                                          out_dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32,
+                                          return_final_state=True)
+    torch.cuda.synchronize()
+    yg, sg = download(y), download(so)
+    if channels is not None:
+        yg, sg = yg[:, :, channels], sg[:, channels]
+    ref, sref, mag = oracle_conv(inp, use_state, use_bias, silu, channels)
+    tol = tol_for(inp["in_dtype"], out_dtype)
+    report(f"{name} y[{out_dtype}]", oracle.scaled_error(yg, ref, mag + 1e-30), tol)
+    # the carried-out state is a copy of inputs: exact
+    assert np.array_equal(sg, sref), f"{name}: state_out differs"
+    return y, so
+
+
+SHAPES = [
+    (1, 1, 1, 1, "f32"), (2, 100, 64, 4, "bf16"), (3, 70, 33, 3, "f32"), (1, 300, 128, 2, "f32"),
+    (2, 130, 256, 4, "f32"), (1, 65, 12, 5, "bf16"), (2, 200, 20, 8, "f32"), (1, 4096, 64, 4, "bf16"),
+    (2, 2, 40, 4, "f32"), (1, 129, 1028, 4, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,L,d,K,dt", SHAPES)
+def test_conv_shapes(B, L, d, K, dt):
+    inp = synth.make_conv_inputs(B, L, d, K, dt, seed=1, stream=500 + K)
+    check(f"conv {(B, L, d, K)} {dt}", inp, "f32")
+    check(f"conv {(B, L, d, K)} {dt} no state", inp, "bf16", use_state=False)
+
+
+@pytest.mark.parametrize("opts", [dict(silu=False), dict(use_bias=False), dict(silu=False, use_bias=False,
+                                                                                use_state=False)])
+def test_conv_options(opts):
+    inp = synth.make_conv_inputs(2, 150, 96, 4, "f32", seed=2, stream=600)
+    check(f"conv options {opts}", inp, "f32", **opts)
+
+
+def test_conv_mamba14b_layer_sampled():
+    inp = synth.make_conv_inputs(4, 8192, 4096, 4, "bf16", seed=0, stream=700)
+    ch = np.r_[0:5, 1023:1026, 4091:4096]
+    check("conv (4,8192,4096,4) bf16 sampled", inp, "f32", channels=ch)
+    check("conv (4,8192,4096,4) bf16-out sampled", inp, "bf16", channels=ch)
+
+
+def test_conv_continuation_and_updates_bitwise():
+    B, L, d, K = 2, 150, 72, 4
+    inp = synth.make_conv_inputs(B, L, d, K, "f32", seed=3, stream=800)
+    dv = dev_inputs(inp)
+    y, s_end = binding.ssm_causal_conv1d_fwd(dv["x"], dv["weight"], dv["bias"], dv["state"],
+                                             return_final_state=True)
+    L1 = 67
+    ya, sa = binding.ssm_causal_conv1d_fwd(dv["x"][:, :L1].contiguous(), dv["weight"], dv["bias"], dv["state"],
+                                           return_final_state=True)
+    yb, sb = binding.ssm_causal_conv1d_fwd(dv["x"][:, L1:].contiguous(), dv["weight"], dv["bias"], sa,
+                                           return_final_state=True)
+    assert torch.equal(torch.cat([ya, yb], 1), y) and torch.equal(sb, s_end)
+    st = dv["state"].clone()
+    for t in range(0, 20):
+        yt = binding.ssm_causal_conv1d_update(st, dv["x"][:, t].contiguous(), dv["weight"], dv["bias"])
+        assert torch.equal(yt, y[:, t]), f"update step {t} differs from the sequence"
+    _, s20 = binding.ssm_causal_conv1d_fwd(dv["x"][:, :20].contiguous(), dv["weight"], dv["bias"], dv["state"],
+                                           return_final_state=True)
+    assert torch.equal(st, s20)
+
+
+@pytest.mark.parametrize("K,dt", [(4, "f32"), (2, "bf16"), (6, "f32"), (1, "f32")])
+def test_conv_update_against_oracle(K, dt):
+    B, d = 5, 130
+    inp = synth.make_conv_inputs(B, 1, d, K, dt, seed=4, stream=900 + K)
+    f = synth.as_float64(inp)
+    dv = dev_inputs(inp)
+    st = dv["state"]
+    y = binding.ssm_causal_conv1d_update(st, dv["x"][:, 0].contiguous(), dv["weight"], dv["bias"])
+    ref, sref = oracle.causal_conv1d_update(f["state"], f["x"][:, 0], f["weight"], f["bias"])
+    _, _, mag = oracle_conv(inp)
+    report(f"conv update K={K} {dt}", oracle.scaled_error(download(y), ref, mag[:, 0] + 1e-30), tol_for(dt, "f32"))
+    assert np.array_equal(download(st), sref)
+
+
+def test_conv_empty_sequence_and_guard_bands():
+    inp = synth.make_conv_inputs(2, 0, 40, 4, "f32", seed=5, stream=1000)
+    dv = dev_inputs(inp)
+    y, so = binding.ssm_causal_conv1d_fwd(dv["x"], dv["weight"], dv["bias"], dv["state"], return_final_state=True)
+    assert y.shape == (2, 0, 40) and torch.equal(so, dv["state"])
+    B, L, d, K = 2, 70, 90, 4
+    inp = synth.make_conv_inputs(B, L, d, K, "bf16", seed=6, stream=1001)
+    dv = dev_inputs(inp)
+    pad = 64
+    ybuf = torch.full((2 * pad + B * L * d,), float("nan"), device="cuda")
+    y = ybuf[pad:pad + B * L * d].view(B, L, d)
+    sbuf = torch.full((2 * pad + B * d * (K - 1),), float("nan"), device="cuda")
+    so = sbuf[pad:pad + B * d * (K - 1)].view(B, d, K - 1)
+    binding.ssm_causal_conv1d_fwd(dv["x"], dv["weight"], dv["bias"], dv["state"], y=y, state_out=so,
+                                  out_dtype=torch.float32)
+    assert torch.isnan(ybuf[:pad]).all() and torch.isnan(ybuf[-pad:]).all()
+    assert torch.isnan(sbuf[:pad]).all() and torch.isnan(sbuf[-pad:]).all()
+    assert not torch.isnan(y).any() and not torch.isnan(so).any()
