@@ -25,19 +25,24 @@ namespace ssm {
 
 namespace {
 
-constexpr int kSeg = 64;      // steps per thread
+// x and y stream through once: their vector accesses are non-temporal.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSeg = 128;     // steps per thread
+constexpr int kGroup = 16;    // steps whose loads are issued together
 constexpr int kBlock = 256;   // threads per block (channel groups)
 
 template <int VC, bool BF16>
 __device__ __forceinline__ void load_vec(const void* base, int64_t i, float (&v)[VC]) {
   if constexpr (VC == 4 && BF16) {
-    const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
+    const u32x2 r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i));
     v[0] = __uint_as_float(r.x << 16);
     v[1] = __uint_as_float(r.x & 0xffff0000u);
     v[2] = __uint_as_float(r.y << 16);
     v[3] = __uint_as_float(r.y & 0xffff0000u);
   } else if constexpr (VC == 4) {
-    const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+    const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i));
     v[0] = r.x;
     v[1] = r.y;
     v[2] = r.z;
@@ -51,12 +56,13 @@ __device__ __forceinline__ void load_vec(const void* base, int64_t i, float (&v)
 template <int VC, bool BF16>
 __device__ __forceinline__ void store_vec(void* base, int64_t i, const float (&v)[VC]) {
   if constexpr (VC == 4 && BF16) {
-    uint2 r;
+    u32x2 r;
     r.x = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
     r.y = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + i) = r;
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + i));
   } else if constexpr (VC == 4) {
-    *reinterpret_cast<float4*>(static_cast<float*>(base) + i) = make_float4(v[0], v[1], v[2], v[3]);
+    const f32x4 r = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(static_cast<float*>(base) + i));
   } else {
 #pragma unroll
     for (int c = 0; c < VC; ++c) store_elem<BF16>(base, i + c, v[c]);
@@ -65,7 +71,7 @@ __device__ __forceinline__ void store_vec(void* base, int64_t i, const float (&v
 
 template <int KM, int VC, bool BI, bool BO, bool SILU>
 __global__ __launch_bounds__(kBlock) void conv1d_fwd_kernel(const ConvArgs a) {
-  static_assert(kSeg % KM == 0, "segment must be a multiple of the window");
+  static_assert(kSeg % KM == 0 && kGroup % KM == 0, "segment and group must be multiples of the window");
   const int64_t L = a.seqlen, Dm = a.dim;
   const int K = static_cast<int>(a.width);
   const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * VC;
@@ -106,23 +112,39 @@ __global__ __launch_bounds__(kBlock) void conv1d_fwd_kernel(const ConvArgs a) {
     // steps t0-KM+1 .. t0-1 go to slots 1 .. KM-1
     input(t0 - (KM - 1) + j, win[1 + j]);
   }
+  // One step at slot u: the window already holds the step's input.
+  auto emit = [&](int64_t t, int u) __attribute__((always_inline)) {
+    float out[VC];
+#pragma unroll
+    for (int c = 0; c < VC; ++c) {
+      float acc = bv[c];
+#pragma unroll
+      for (int i = 0; i < KM; ++i) acc = fmaf(wp[i][c], win[(u + 1 + i) % KM][c], acc);
+      out[c] = SILU ? silu_f(acc) : acc;
+    }
+    store_vec<VC, BO>(a.y, (row0 + t) * Dm + c0, out);
+  };
   const int64_t t_end = min(t0 + kSeg, L);
-  for (int64_t tb = t0; tb < t_end; tb += KM) {
+  int64_t tb = t0;
+  // Full groups of kGroup steps: every load of the group is issued before the
+  // first is used (no per-step bounds test stands in between).
+  for (; tb + kGroup <= t_end; tb += kGroup) {
+    float in[kGroup][VC];
 #pragma unroll
-    for (int u = 0; u < KM; ++u) {
-      const int64_t t = tb + u;
-      if (t < t_end) {
-        input(t, win[u]);
-        float out[VC];
+    for (int g = 0; g < kGroup; ++g) load_vec<VC, BI>(a.x, (row0 + tb + g) * Dm + c0, in[g]);
 #pragma unroll
-        for (int c = 0; c < VC; ++c) {
-          float acc = bv[c];
+    for (int g = 0; g < kGroup; ++g) {
 #pragma unroll
-          for (int i = 0; i < KM; ++i) acc = fmaf(wp[i][c], win[(u + 1 + i) % KM][c], acc);
-          out[c] = SILU ? silu_f(acc) : acc;
-        }
-        store_vec<VC, BO>(a.y, (row0 + t) * Dm + c0, out);
-      }
+      for (int c = 0; c < VC; ++c) win[g % KM][c] = in[g][c];
+      emit(tb + g, g % KM);
+    }
+  }
+  // Tail: fewer than kGroup steps, each tested.
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g) {
+    if (tb + g < t_end) {
+      input(tb + g, win[g % KM]);
+      emit(tb + g, g % KM);
     }
   }
 
