@@ -159,6 +159,55 @@ int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
                                void* y, void* stream);
 
 /*
+ * Bytes of device workspace ssm_selective_scan_bwd needs for this shape: B and
+ * C repacked per state, the states at every 8-step tile start
+ * ([B][ceil(L/8)][N'][d] float32, N' = N rounded up to a power of two), and
+ * per-block / per-batch partial sums of dB, dC, dA, dD and the bias gradient.
+ * Returns 0 for invalid or unsupported sizes.
+ */
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * Selective scan backward: gradients of a loss through ssm_selective_scan_fwd
+ * with the same inputs, given dy = dL/dy and optionally dh_final = dL/dh_final.
+ * Reverse-mode steps of the forward recurrence (its gradient flows back
+ * through every later state: "Mamba的隐藏代价" (kongchang.com), section on the
+ * optimisation problems of sequential gradients):
+ *
+ *   lam_l   = dp_l C_l + exp(dt_{l+1} A) lam_{l+1},  dp = dy * silu(z) (or dy)
+ *   du      = dp D + sum_n lam dt B          ddelta = softplus'(x) sum_n lam (A exp(dt A) h_{l-1} + B u)
+ *   dA      = sum_{b,l} lam dt exp(dt A) h_{l-1}      dB_l = sum_d lam dt u,  dC_l = sum_d dp h_l
+ *   dD      = sum_{b,l} dp u                 dz = dy p silu'(z), p = sum_n C h + D u
+ *   ddelta_bias = sum_{b,l} ddelta           dh0 = exp(dt_0 A) lam_0
+ *
+ *   batch, seqlen, dim, dstate : as the forward, with 1 <= N <= 16 (else
+ *                                SSM_E_UNSUPPORTED).
+ *   in_dtype, delta_softplus, u, delta, A, B, C, D, z, delta_bias, h0 : the
+ *                                forward's inputs (same layouts and rules).
+ *   dy        [B, L, d]  float32    gradient of the loss w.r.t. y
+ *   dh_final  [B, d, N]  float32    gradient w.r.t. h_final (optional, 0)
+ *   du, ddelta [B, L, d] float32    outputs (ddelta w.r.t. the raw delta)
+ *   dA        [d, N]     float32    output
+ *   dB, dC    [B, L, N]  float32    outputs
+ *   dD [d], dz [B, L, d], ddelta_bias [d] : float32 outputs, optional; written
+ *                                only when D, z, delta_bias are given
+ *   dh0       [B, d, N]  float32    output (optional)
+ *   workspace, workspace_bytes      at least ssm_scan_bwd_workspace_bytes()
+ * No output may overlap an input, another output or the workspace. Results
+ * are bitwise deterministic from run to run (sums over channels and batches
+ * in a fixed order; no floating-point atomics).
+ */
+int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           int in_dtype, int delta_softplus,
+                           const void* u, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, const float* h0,
+                           const float* dy, const float* dh_final,
+                           float* du, float* ddelta, float* dA, float* dB, float* dC,
+                           float* dD, float* dz, float* ddelta_bias, float* dh0,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Causal depthwise conv1d (+ SiLU) over a sequence: the short local
  * convolution that precedes the selective scan in the block ("从 Transformer
  * 到 Mamba", ybb.press, section 5: depthwise Conv1d of width d_conv padded by

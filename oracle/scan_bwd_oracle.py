@@ -100,7 +100,9 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
         g = silu(z)
         dsilu = s * (1.0 + z * (1.0 - s))
         dp, dpm = dy * g, np.abs(dy * g)
-        dz, dzm = dy * p * dsilu, np.abs(dy) * pm * np.abs(dsilu)
+        # silu' = s + s z (1 - s): its companion bounds the two terms
+        # separately (they cancel near z = -1.28).
+        dz, dzm = dy * p * dsilu, np.abs(dy) * pm * (s * (1.0 + np.abs(z) * (1.0 - s)))
     else:
         dp, dpm = dy.copy(), np.abs(dy)
         dz = dzm = None

@@ -10,8 +10,10 @@ from .binding import (  # noqa: F401
     ssm_abi_version,
     ssm_causal_conv1d_fwd,
     ssm_causal_conv1d_update,
+    ssm_scan_bwd_workspace_bytes,
     ssm_scan_chunks,
     ssm_scan_workspace_bytes,
+    ssm_selective_scan_bwd,
     ssm_selective_scan_fwd,
     ssm_selective_state_update,
     SSMError,

@@ -62,6 +62,10 @@ def _load():
         lib.ssm_selective_state_update.argtypes = [i64, i64, i64, i32, i32, i32,
                                                    vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                    vp, vp]
+        lib.ssm_scan_bwd_workspace_bytes.restype = sz
+        lib.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        lib.ssm_selective_scan_bwd.restype = i32
+        lib.ssm_selective_scan_bwd.argtypes = [i64, i64, i64, i64, i32, i32] + [vp] * 21 + [sz, vp]
         lib.ssm_causal_conv1d_fwd.restype = i32
         lib.ssm_causal_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32, i32, i32,
                                               vp, vp, vp, vp, vp, vp, vp]
@@ -296,3 +300,60 @@ def ssm_causal_conv1d_update(state, x, weight, bias=None, silu_activation=True, 
                                           _ptr(bias), _ptr(y), _stream_handle(stream, dev))
     _check("ssm_causal_conv1d_update", st)
     return y
+
+
+def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate) -> int:
+    return int(_load().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate))
+
+
+def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False,
+                           h0=None, dh_final=None, workspace=None, stream=None):
+    """Gradients of the selective scan; see ssm_selective_scan_bwd in include/ssm_scan.h.
+
+    Inputs as ssm_selective_scan_fwd, plus dy [B, L, d] and dh_final [B, d, N]
+    (float32). Returns a dict of float32 tensors: du, ddelta, dA, dB, dC, dh0,
+    and dD / dz / ddelta_bias when D / z / delta_bias are given.
+    """
+    lib = _load()
+    if not isinstance(u, torch.Tensor) or u.dim() != 3 or u.dtype not in _DTYPE_CODE:
+        raise ValueError("u must be a 3-d float32 or bfloat16 tensor [B, L, d]")
+    dev = u.device
+    Bt, L, d = u.shape
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be a 2-d tensor [d, N]")
+    N = A.shape[1]
+    ind = (u.dtype,)
+    f32 = (torch.float32,)
+    _dev_tensor("u", u, (Bt, L, d), ind, dev)
+    _dev_tensor("delta", delta, (Bt, L, d), ind, dev)
+    _dev_tensor("A", A, (d, N), f32, dev)
+    _dev_tensor("B", B, (Bt, L, N), ind, dev)
+    _dev_tensor("C", C, (Bt, L, N), ind, dev)
+    _dev_tensor("D", D, (d,), f32, dev)
+    _dev_tensor("z", z, (Bt, L, d), ind, dev)
+    _dev_tensor("delta_bias", delta_bias, (d,), f32, dev)
+    _dev_tensor("h0", h0, (Bt, d, N), f32, dev)
+    _dev_tensor("dy", dy, (Bt, L, d), f32, dev)
+    _dev_tensor("dh_final", dh_final, (Bt, d, N), f32, dev)
+    new = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)  # noqa: E731
+    g = dict(du=new(Bt, L, d), ddelta=new(Bt, L, d), dA=new(d, N), dB=new(Bt, L, N), dC=new(Bt, L, N),
+             dh0=new(Bt, d, N))
+    if D is not None:
+        g["dD"] = new(d)
+    if z is not None:
+        g["dz"] = new(Bt, L, d)
+    if delta_bias is not None:
+        g["ddelta_bias"] = new(d)
+    ws_bytes = int(lib.ssm_scan_bwd_workspace_bytes(Bt, L, d, N))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.ssm_selective_scan_bwd(
+            Bt, L, d, N, _DTYPE_CODE[u.dtype], int(bool(delta_softplus)),
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0),
+            _ptr(dy), _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+            _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g["dh0"]),
+            _ptr(workspace), ws_size, _stream_handle(stream, dev))
+    _check("ssm_selective_scan_bwd", st)
+    return g

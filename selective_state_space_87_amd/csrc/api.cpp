@@ -214,6 +214,98 @@ int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
   return map_hip(ssm::launch_state_update(a, stream));
 }
 
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return 0;
+  int64_t t;
+  if (!safe_mul(batch, seqlen, &t) || !safe_mul(t, dim, &t) || !safe_mul(t, dstate, &t)) return 0;
+  const ssm::ScanBwdPlan p = ssm::plan_scan_bwd(batch, seqlen, dim, dstate);
+  return p.ok ? p.bytes : 0;
+}
+
+int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           int in_dtype, int delta_softplus,
+                           const void* u, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, const float* h0,
+                           const float* dy, const float* dh_final,
+                           float* du, float* ddelta, float* dA, float* dB, float* dC,
+                           float* dD, float* dz, float* ddelta_bias, float* dh0,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
+  if (in_dtype != 0 && in_dtype != 1) return SSM_E_DTYPE;
+  int64_t bl, bld, bln, bdn, dn, bldn;
+  if (!safe_mul(batch, seqlen, &bl) || !safe_mul(bl, dim, &bld) || !safe_mul(bl, dstate, &bln) ||
+      !safe_mul(batch, dim, &bdn) || !safe_mul(bdn, dstate, &bdn) || !safe_mul(dim, dstate, &dn) ||
+      !safe_mul(bld, dstate, &bldn)) {
+    return SSM_E_SHAPE;
+  }
+  const ssm::ScanBwdPlan plan = ssm::plan_scan_bwd(batch, seqlen, dim, dstate);
+  if (!plan.ok) return SSM_E_UNSUPPORTED;
+  if (dim == 0) return SSM_OK;
+  if (A == nullptr || dA == nullptr) return SSM_E_NULLPTR;
+  if (bl > 0 && (u == nullptr || delta == nullptr || B == nullptr || C == nullptr || dy == nullptr ||
+                 du == nullptr || ddelta == nullptr || dB == nullptr || dC == nullptr)) {
+    return SSM_E_NULLPTR;
+  }
+  const void* vec_ptrs[] = {u, delta, B, C, z};
+  for (const void* p : vec_ptrs) {
+    if (p && !aligned(p, 16)) return SSM_E_ALIGN;
+  }
+  const void* f32_ptrs[] = {A, D, delta_bias, h0, dy, dh_final, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0};
+  for (const void* p : f32_ptrs) {
+    if (p && !aligned(p, 4)) return SSM_E_ALIGN;
+  }
+  const size_t need = plan.bytes;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SSM_E_WORKSPACE;
+  const int64_t isz = in_dtype == 1 ? 2 : 4;
+  const Range inputs[] = {span(u, bld, isz), span(delta, bld, isz), span(z, bld, isz), span(B, bln, isz),
+                          span(C, bln, isz), span(A, dn, 4), span(D, dim, 4), span(delta_bias, dim, 4),
+                          span(h0, bdn, 4), span(dy, bld, 4), span(dh_final, bdn, 4)};
+  const Range outputs[] = {span(du, bld, 4), span(ddelta, bld, 4), span(dA, dn, 4), span(dB, bln, 4),
+                           span(dC, bln, 4), span(D ? dD : nullptr, dim, 4), span(z ? dz : nullptr, bld, 4),
+                           span(delta_bias ? ddelta_bias : nullptr, dim, 4), span(dh0, bdn, 4),
+                           span(workspace, static_cast<int64_t>(need), 1)};
+  constexpr int kOut = sizeof(outputs) / sizeof(outputs[0]);
+  for (int i = 0; i < kOut; ++i) {
+    for (const Range& r : inputs) {
+      if (overlaps(outputs[i], r)) return SSM_E_ALIAS;
+    }
+    for (int j = i + 1; j < kOut; ++j) {
+      if (overlaps(outputs[i], outputs[j])) return SSM_E_ALIAS;
+    }
+  }
+
+  ssm::ScanBwdArgs a;
+  a.u = u;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.z = z;
+  a.delta_bias = delta_bias;
+  a.h0 = h0;
+  a.dy = dy;
+  a.dh_final = dh_final;
+  a.du = du;
+  a.ddelta = ddelta;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dD = D ? dD : nullptr;
+  a.dz = z ? dz : nullptr;
+  a.ddelta_bias = delta_bias ? ddelta_bias : nullptr;
+  a.dh0 = dh0;
+  a.workspace = workspace;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.dim = dim;
+  a.dstate = dstate;
+  a.in_bf16 = in_dtype;
+  a.delta_softplus = delta_softplus ? 1 : 0;
+  return map_hip(ssm::launch_scan_bwd(a, stream));
+}
+
 int ssm_causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
                           int in_dtype, int out_dtype, int silu_activation,
                           const void* x, const float* weight, const float* bias,

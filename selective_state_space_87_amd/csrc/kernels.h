@@ -39,6 +39,32 @@ struct UpdateArgs {
   int in_bf16, out_bf16, delta_softplus;
 };
 
+struct ScanBwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* delta_bias;
+  const float* h0;
+  const float* dy;
+  const float* dh_final;
+  float* du;
+  float* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;
+  float* dz;
+  float* ddelta_bias;
+  float* dh0;
+  void* workspace;
+  int64_t batch, seqlen, dim, dstate;
+  int in_bf16, delta_softplus;
+};
+
 struct ConvArgs {
   const void* x;
   const float* weight;
@@ -85,6 +111,20 @@ constexpr int64_t kChunkWhenBlocksAtMost = 128;
 
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
+// Backward: same state mapping (N <= 16), tiles of kBwdTile steps; workspace
+// = packed B/C, per-tile state checkpoints [B][tiles][NS][d], per-block
+// partials of dB and dC [blocks_d][B][Lp][NS], per-batch partials of dA
+// [B][d][N], dD and the bias gradient [B][d].
+constexpr int64_t kBwdTile = 8;
+constexpr int64_t kBwdMaxState = 16;
+struct ScanBwdPlan {
+  bool ok;
+  int NS, W, S;
+  int64_t Lp, dim_blocks;
+  size_t off_bc, off_ckpt, off_dbp, off_dcp, off_dap, off_ddp, off_dbiasp, bytes;
+};
+ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
 // Workspace bytes the scan needs for this shape.
 size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
@@ -92,6 +132,7 @@ size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
 // validated. Return 0 or the HIP error code of the failing launch.
 int launch_scan(const ScanArgs& a, void* stream);
 int launch_state_update(const UpdateArgs& a, void* stream);
+int launch_scan_bwd(const ScanBwdArgs& a, void* stream);
 int launch_conv1d_fwd(const ConvArgs& a, void* stream);
 int launch_conv1d_update(const ConvUpdateArgs& a, void* stream);
 

@@ -66,6 +66,36 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   return p;
 }
 
+ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  ScanBwdPlan p{};
+  p.ok = batch >= 0 && seqlen >= 0 && dim >= 0 && dstate >= 1 && dstate <= kBwdMaxState &&
+         seqlen < (int64_t(1) << 30) && dim < (int64_t(1) << 24) && batch < (int64_t(1) << 24);
+  if (!p.ok) return p;
+  p.NS = ceil_pow2(dstate);
+  p.W = p.NS < 16 ? p.NS : 8;
+  p.S = p.NS / p.W;
+  p.Lp = round_up(seqlen, kPadSteps);
+  p.dim_blocks = ceil_div(dim, 64);
+  const int64_t tiles = p.Lp / kBwdTile;
+  size_t off = 0;
+  p.off_bc = off;
+  off += align256(size_t(2 * batch * p.NS * p.Lp) * 4);
+  p.off_ckpt = off;
+  off += align256(size_t(batch * tiles * p.NS * dim) * 4);
+  p.off_dbp = off;
+  off += align256(size_t(p.dim_blocks * batch * p.Lp * p.NS) * 4);
+  p.off_dcp = off;
+  off += align256(size_t(p.dim_blocks * batch * p.Lp * p.NS) * 4);
+  p.off_dap = off;
+  off += align256(size_t(batch * dim * dstate) * 4);
+  p.off_ddp = off;
+  off += align256(size_t(batch * dim) * 4);
+  p.off_dbiasp = off;
+  off += align256(size_t(batch * dim) * 4);
+  p.bytes = off;
+  return p;
+}
+
 size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   const ScanPlan p = plan_scan(batch, seqlen, dim, dstate);
   return p.ok ? p.bytes : 0;

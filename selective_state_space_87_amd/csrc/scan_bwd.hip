@@ -1,0 +1,501 @@
+// Selective scan backward for gfx950: gradients of a loss through the
+// forward scan, given dL/dy (and optionally dL/dh_final).
+//
+// Per batch b, channel d, state n, step l (forward as in scan_fwd.hip; the
+// reverse-mode steps follow from it, and the adjoint state is the
+// recurrence's own gradient flowing back through every later step, as
+// "Mamba的隐藏代价" (kongchang.com) describes for sequential gradients):
+//   lam_l  = dp_l C_l + a_{l+1} lam_{l+1},  dp = dy silu(z),  a = exp(dt A)
+//   ddt_l  = sum_n lam_l (A a_l h_{l-1} + B_l u_l)      du_l = dp_l D + sum_n lam_l dt_l B_l
+//   dA     = sum lam_l dt_l a_l h_{l-1}                 dh0  = a_0 lam_0
+//   dB_l   = sum_d lam_l dt_l u_l                       dC_l = sum_d dp_l h_l
+//   dz_l   = dy_l p_l silu'(z_l) with p the pre-gate output; ddelta = ddt softplus'(x)
+//
+// One block per (batch, 64 channels), the forward's mapping: lane = channel,
+// wave w = states w*S .. w*S+S-1. Two sweeps:
+//   1. forward over tiles of T steps, storing every wave's states at each
+//      tile start (checkpoints, in the workspace);
+//   2. backward over the tiles in reverse: recompute the tile's states and
+//      transitions from its checkpoint, read the pre-gate output out of them
+//      (partials over waves in LDS, as in the forward), then run the adjoint
+//      recurrence. Per-step sums over states (ddt, du) go through LDS;
+//      per-(step, state) sums over channels (dB, dC) are reduced across the
+//      wave's 64 lanes with a transposed butterfly and written as per-block
+//      partials, summed over blocks in a fixed order by a second kernel
+//      (together with dA, dD and the bias gradient over batches), so results
+//      are deterministic.
+// Per-(b, l, d) work (step size, gate, their derivatives) is done once per
+// item by the block's threads and shared through LDS.
+#include <hip/hip_runtime.h>
+
+#include "bc_pack.h"
+#include "device_math.h"
+#include "kernels.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kBwdT = 8;  // steps per tile
+
+struct ScanBwd {
+  const void* u;
+  const void* delta;
+  const void* z;
+  const float* A;
+  const float* D;
+  const float* bias;
+  const float* h0;
+  const uint32_t* BC;    // packed B/C (bc_pack_kernel)
+  const float* dy;
+  const float* dh_final;
+  float* du;
+  float* ddelta;
+  float* dz;
+  float* dh0;
+  float* ckpt;           // [B][tiles][NS][d]
+  float* dBp;            // [blocks_d][B][Lp][NS]
+  float* dCp;
+  float* dAp;            // [B][d][N]
+  float* dDp;            // [B][d]
+  float* dbiasp;         // [B][d]
+  int L, Lp, dim, N, batch;
+};
+
+__device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
+
+// Sum over the wave's 64 lanes of each of G values (G a power of two, at most
+// 64), transposed: on return lane l holds the total of value (l >> (6 - log2 G))
+// ... in the order fixed by the butterfly (see below). Each stage keeps half
+// of the lane's values (the half selected by the lane's bit) and adds the
+// partner's copy of that half.
+template <int G>
+__device__ __forceinline__ float lane_transpose_sum(float (&v)[G], int lane) {
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "power of two up to 64");
+  int m = 32;
+  static_for<0, __builtin_ctz(G)>([&](auto st) {
+    constexpr int H = G >> (decltype(st)::value + 1);  // values kept after this stage
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float keep = upper ? v[i + H] : v[i];
+      const float send = upper ? v[i] : v[i + H];
+      v[i] = keep + __shfl_xor(send, m);
+    }
+    m >>= 1;
+  });
+  float r = v[0];
+  for (; m >= 1; m >>= 1) r += __shfl_xor(r, m);
+  return r;
+}
+
+template <int S, int W, bool BF16_IN, bool SOFTPLUS>
+__global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
+  constexpr int T = kBwdT;
+  constexpr int NS = S * W;
+  constexpr int IT = T >= W ? T / W : 1;   // cooperative items per thread per tile
+  constexpr int WPS = BF16_IN ? 1 : 2;
+  constexpr int G = 2 * T * S;              // values per lane reduced over channels
+  static_assert(G <= 64, "backward supports at most 32 (step, state) pairs per wave");
+
+  __shared__ float4 sQ[T][64];                       // (dt, dt*u, dp, u) per step, channel
+  __shared__ uint32_t sBC[NS][T * WPS];              // packed B/C of the tile
+  __shared__ float sP[T][64 * W];                    // readout partials (pre-gate output)
+  __shared__ float sG[T][64 * W];                    // ddt partials
+  __shared__ float sU[T][64 * W];                    // du partials
+  __shared__ float sRed[2][W][64];                   // final per-channel sums
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Dm = p.dim, N = p.N, L = p.L, Lp = p.Lp;
+  const int tiles_d = (Dm + 63) / 64;
+  const int b = blockIdx.x / tiles_d;
+  const int blk = blockIdx.x % tiles_d;
+  const int ch = blk * 64 + lane;
+  const bool ch_ok = ch < Dm;
+  const int nt = Lp / T;
+  const int64_t bdn = (static_cast<int64_t>(b) * Dm + ch) * N;
+
+  float A1[S], A2[S], h[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int n = w * S + s;
+    const bool ok = ch_ok && n < N;
+    A1[s] = ok ? p.A[static_cast<int64_t>(ch) * N + n] : 0.0f;
+    A2[s] = A1[s] * kLog2e;
+    h[s] = (ok && p.h0) ? p.h0[bdn + n] : 0.0f;
+  }
+  const float Dv = (ch_ok && p.D) ? p.D[ch] : 0.0f;
+  const float bv = (ch_ok && p.bias) ? p.bias[ch] : 0.0f;
+  const bool has_z = p.z != nullptr;
+  const uint32_t* bcb = p.BC + static_cast<int64_t>(b) * NS * Lp * WPS;
+  const int64_t plane = static_cast<int64_t>(b) * L;
+
+  // Cooperative: this thread's items of tile k are steps w + W*i (i < IT) of
+  // channel `lane`; with more waves than steps, waves >= T have none.
+  auto item_step = [&](int i) __attribute__((always_inline)) { return w + W * i; };
+  auto load_in = [&](const void* ptr, int t) __attribute__((always_inline)) -> float {
+    return (ch_ok && t >= 0 && t < L) ? load_elem<BF16_IN>(ptr, (plane + t) * Dm + ch) : 0.0f;
+  };
+  auto load_bc_tile = [&](int k) __attribute__((always_inline)) {
+    for (int i = threadIdx.x; i < NS * T * WPS; i += W * 64) {
+      const int n = i / (T * WPS), j = i % (T * WPS);
+      sBC[n][j] = bcb[(static_cast<int64_t>(n) * Lp + k * T) * WPS + j];
+    }
+  };
+  auto bc_of = [&](int n, int t, float& bval, float& cval) __attribute__((always_inline)) {
+    if constexpr (BF16_IN) {
+      const uint32_t wd = sBC[n][t];
+      bval = __uint_as_float(wd & 0xffff0000u);
+      cval = __uint_as_float(wd << 16);
+    } else {
+      bval = __uint_as_float(sBC[n][2 * t]);
+      cval = __uint_as_float(sBC[n][2 * t + 1]);
+    }
+  };
+  auto step_size = [&](int t, float& x_out) __attribute__((always_inline)) -> float {
+    const float x = load_in(p.delta, t) + bv;
+    x_out = x;
+    const float dt = SOFTPLUS ? softplus_f(x) : x;
+    return t < L ? dt : 0.0f;
+  };
+
+  // ---------------------------------------------------------------- sweep 1
+  for (int k = 0; k < nt; ++k) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int tt = item_step(i);
+      if (tt < T) {
+        const int t = k * T + tt;
+        float x;
+        const float dt = step_size(t, x);
+        const float uv = load_in(p.u, t);
+        sQ[tt][lane] = make_float4(dt, dt * uv, 0.0f, uv);
+      }
+    }
+    load_bc_tile(k);
+    __syncthreads();
+    // checkpoint: the states entering tile k
+    float* ck = p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (ch_ok) ck[static_cast<int64_t>(s) * Dm] = h[s];
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float4 q = sQ[t][lane];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        float bval, cval;
+        bc_of(w * S + s, t, bval, cval);
+        h[s] = fmaf(exp2_hw(q.x * A2[s]), h[s], q.y * bval);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- sweep 2
+  float mu[S], dA_acc[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int n = w * S + s;
+    mu[s] = (ch_ok && n < N && p.dh_final) ? p.dh_final[bdn + n] : 0.0f;
+    dA_acc[s] = 0.0f;
+  }
+  float dD_acc = 0.0f, dbias_acc = 0.0f;
+  // Items of the tile being finished (kept from its preparation to its epilogue).
+  float e_dy[IT], e_dsilu[IT], e_dsp[IT], e_u[IT], e_dp[IT];
+
+  auto prepare_bwd = [&](int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int tt = item_step(i);
+      if (tt < T) {
+        const int t = k * T + tt;
+        float x;
+        const float dt = step_size(t, x);
+        const float uv = load_in(p.u, t);
+        const float dyv = (ch_ok && t >= 0 && t < L) ? p.dy[(plane + t) * Dm + ch] : 0.0f;
+        float g = 1.0f, dsilu = 0.0f;
+        if (has_z) {
+          const float zv = load_in(p.z, t);
+          const float sg = sigmoid_f(zv);
+          g = zv * sg;
+          dsilu = sg * fmaf(zv, 1.0f - sg, 1.0f);
+        }
+        const float dp = dyv * g;
+        e_dy[i] = dyv;
+        e_dsilu[i] = dsilu;
+        e_dsp[i] = SOFTPLUS ? sigmoid_f(x) : 1.0f;
+        e_u[i] = uv;
+        e_dp[i] = dp;
+        sQ[tt][lane] = make_float4(dt, dt * uv, dp, uv);
+      }
+    }
+    load_bc_tile(k);
+  };
+
+  if (nt > 0) prepare_bwd(nt - 1);
+  __syncthreads();
+  for (int k = nt - 1; k >= 0; --k) {
+    // -- waves: recompute the tile, then the adjoint recurrence
+    float dtv[T], dtu[T], dpv[T], uvv[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float4 q = sQ[t][lane];
+      dtv[t] = q.x;
+      dtu[t] = q.y;
+      dpv[t] = q.z;
+      uvv[t] = q.w;
+    }
+    const float* ck = p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
+    float hh[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) hh[s] = ch_ok ? ck[static_cast<int64_t>(s) * Dm] : 0.0f;
+    float av[T][S], ahv[T][S], hs[T][S];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        float bval, cval;
+        bc_of(w * S + s, t, bval, cval);
+        av[t][s] = exp2_hw(dtv[t] * A2[s]);
+        ahv[t][s] = av[t][s] * hh[s];
+        hh[s] = fmaf(dtu[t], bval, ahv[t][s]);
+        hs[t][s] = hh[s];
+        acc = fmaf(cval, hh[s], acc);
+      }
+      sP[t][lane * W + w] = acc;
+    }
+    float gv[G];
+#pragma unroll
+    for (int t = T - 1; t >= 0; --t) {
+      float ddt_acc = 0.0f, du_acc = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        float bval, cval;
+        bc_of(w * S + s, t, bval, cval);
+        const float lam = fmaf(dpv[t], cval, mu[s]);
+        gv[t * S + s] = lam * dtu[t];                 // -> dB (sum over channels)
+        gv[T * S + t * S + s] = dpv[t] * hs[t][s];    // -> dC (sum over channels)
+        ddt_acc = fmaf(lam, fmaf(A1[s], ahv[t][s], bval * uvv[t]), ddt_acc);
+        du_acc = fmaf(lam, dtv[t] * bval, du_acc);
+        dA_acc[s] = fmaf(lam * dtv[t], ahv[t][s], dA_acc[s]);
+        mu[s] = av[t][s] * lam;
+      }
+      sG[t][lane * W + w] = ddt_acc;
+      sU[t][lane * W + w] = du_acc;
+    }
+    // dB / dC partials of this block: value j = lane >> (6 - log2 G) after the
+    // transposed butterfly; one lane of each group writes it.
+    {
+      const float r = lane_transpose_sum<G>(gv, lane);
+      constexpr int LG = __builtin_ctz(G);
+      const int j = lane >> (6 - LG);
+      if ((lane & ((1 << (6 - LG)) - 1)) == 0) {
+        const int which = j / (T * S), rem = j % (T * S);
+        const int t = k * T + rem / S, n = w * S + rem % S;
+        float* dst = which == 0 ? p.dBp : p.dCp;
+        dst[((static_cast<int64_t>(blk) * p.batch + b) * Lp + t) * NS + n] = r;
+      }
+    }
+    __syncthreads();
+    // -- epilogue of tile k (per item), then preparation of tile k-1
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int tt = item_step(i);
+      if (tt < T) {
+        const int t = k * T + tt;
+        float pre = 0.0f, ddt = 0.0f, dus = 0.0f;
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+          pre += sP[tt][lane * W + q];
+          ddt += sG[tt][lane * W + q];
+          dus += sU[tt][lane * W + q];
+        }
+        if (ch_ok && t < L) {
+          const int64_t o = (plane + t) * Dm + ch;
+          pre = fmaf(Dv, e_u[i], pre);
+          if (has_z && p.dz) p.dz[o] = e_dy[i] * pre * e_dsilu[i];
+          const float dd = ddt * e_dsp[i];
+          p.ddelta[o] = dd;
+          p.du[o] = fmaf(e_dp[i], Dv, dus);
+          dD_acc = fmaf(e_dp[i], e_u[i], dD_acc);
+          dbias_acc += dd;
+        }
+      }
+    }
+    if (k > 0) prepare_bwd(k - 1);
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- per-block outputs
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int n = w * S + s;
+    if (ch_ok && n < N) {
+      if (p.dh0) p.dh0[bdn + n] = mu[s];
+      p.dAp[bdn + n] = dA_acc[s];
+    }
+  }
+  sRed[0][w][lane] = dD_acc;
+  sRed[1][w][lane] = dbias_acc;
+  __syncthreads();
+  if (w == 0 && ch_ok) {
+    float sd = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      sd += sRed[0][q][lane];
+      sb += sRed[1][q][lane];
+    }
+    p.dDp[static_cast<int64_t>(b) * Dm + ch] = sd;
+    p.dbiasp[static_cast<int64_t>(b) * Dm + ch] = sb;
+  }
+}
+
+// dB, dC [B, L, N] = sum over channel blocks (in block order) of the partials.
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ dBp,
+                                                            const float* __restrict__ dCp,
+                                                            float* __restrict__ dB, float* __restrict__ dC,
+                                                            int blocks_d, int batch, int L, int Lp, int N,
+                                                            int NS) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(batch) * L * N;
+  if (i >= total) return;
+  const int n = static_cast<int>(i % N);
+  const int64_t bt = i / N;
+  const int t = static_cast<int>(bt % L);
+  const int b = static_cast<int>(bt / L);
+  float sb = 0.0f, sc = 0.0f;
+  for (int k = 0; k < blocks_d; ++k) {
+    const int64_t o = ((static_cast<int64_t>(k) * batch + b) * Lp + t) * NS + n;
+    sb += dBp[o];
+    sc += dCp[o];
+  }
+  dB[i] = sb;
+  dC[i] = sc;
+}
+
+// dA [d, N], dD [d], dbias [d] = sums over batches (in batch order).
+__global__ __launch_bounds__(256) void bwd_reduce_d_kernel(const float* __restrict__ dAp,
+                                                           const float* __restrict__ dDp,
+                                                           const float* __restrict__ dbiasp,
+                                                           float* __restrict__ dA, float* __restrict__ dD,
+                                                           float* __restrict__ dbias, int batch, int dim, int N) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t dn = static_cast<int64_t>(dim) * N;
+  if (i >= dn) return;
+  float s = 0.0f;
+  for (int b = 0; b < batch; ++b) s += dAp[b * dn + i];
+  dA[i] = s;
+  if (i % N == 0) {
+    const int64_t ch = i / N;
+    float sd = 0.0f, sb = 0.0f;
+    for (int b = 0; b < batch; ++b) {
+      sd += dDp[b * static_cast<int64_t>(dim) + ch];
+      sb += dbiasp[b * static_cast<int64_t>(dim) + ch];
+    }
+    if (dD) dD[ch] = sd;
+    if (dbias) dbias[ch] = sb;
+  }
+}
+
+int launch_reduce_d(const ScanBwdArgs& a, const float* dAp, const float* dDp, const float* dbiasp,
+                    hipStream_t st) {
+  float* dA = a.dA;
+  float* dD = a.dD;
+  float* dbias = a.ddelta_bias;
+  int batch = static_cast<int>(a.batch), dim = static_cast<int>(a.dim), N = static_cast<int>(a.dstate);
+  const int64_t dn = a.dim * a.dstate;
+  void* kargs[] = {&dAp, &dDp, &dbiasp, &dA, &dD, &dbias, &batch, &dim, &N};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_reduce_d_kernel),
+                         dim3(static_cast<unsigned>((dn + 255) / 256)), dim3(256), kargs, 0, st);
+}
+
+template <int S, int W, bool BI, bool SP>
+int launch_bwd_sw(const ScanBwdArgs& a, const ScanBwd& s, int64_t blocks, hipStream_t st) {
+  ScanBwd args = s;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_bwd_kernel<S, W, BI, SP>),
+                         dim3(static_cast<unsigned>(blocks)), dim3(W * 64), kargs, 0, st);
+}
+
+template <bool BI, bool SP>
+int launch_bwd_ns(const ScanBwdArgs& a, const ScanBwdPlan& pl, const ScanBwd& s, int64_t blocks, hipStream_t st) {
+  switch (pl.NS) {
+    case 1: return launch_bwd_sw<1, 1, BI, SP>(a, s, blocks, st);
+    case 2: return launch_bwd_sw<1, 2, BI, SP>(a, s, blocks, st);
+    case 4: return launch_bwd_sw<1, 4, BI, SP>(a, s, blocks, st);
+    case 8: return launch_bwd_sw<1, 8, BI, SP>(a, s, blocks, st);
+    default: return launch_bwd_sw<2, 8, BI, SP>(a, s, blocks, st);
+  }
+}
+
+}  // namespace
+
+int launch_scan_bwd(const ScanBwdArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.dim == 0) return 0;
+  const ScanBwdPlan pl = plan_scan_bwd(a.batch, a.seqlen, a.dim, a.dstate);
+  if (!pl.ok) return hipErrorInvalidValue;
+  char* ws = static_cast<char*>(a.workspace);
+  int err = 0;
+  if (a.batch == 0) return launch_reduce_d(a, nullptr, nullptr, nullptr, st);  // dA, dD, dbias = 0
+  err = launch_bc_pack(a.B, a.C, reinterpret_cast<uint32_t*>(ws + pl.off_bc), a.batch, a.seqlen, pl.Lp,
+                           static_cast<int>(a.dstate), pl.NS, a.in_bf16 != 0, st);
+  if (err != 0) return err;
+  ScanBwd s;
+  s.u = a.u;
+  s.delta = a.delta;
+  s.z = a.z;
+  s.A = a.A;
+  s.D = a.D;
+  s.bias = a.delta_bias;
+  s.h0 = a.h0;
+  s.BC = reinterpret_cast<const uint32_t*>(ws + pl.off_bc);
+  s.dy = a.dy;
+  s.dh_final = a.dh_final;
+  s.du = a.du;
+  s.ddelta = a.ddelta;
+  s.dz = a.dz;
+  s.dh0 = a.dh0;
+  s.ckpt = reinterpret_cast<float*>(ws + pl.off_ckpt);
+  s.dBp = reinterpret_cast<float*>(ws + pl.off_dbp);
+  s.dCp = reinterpret_cast<float*>(ws + pl.off_dcp);
+  s.dAp = reinterpret_cast<float*>(ws + pl.off_dap);
+  s.dDp = reinterpret_cast<float*>(ws + pl.off_ddp);
+  s.dbiasp = reinterpret_cast<float*>(ws + pl.off_dbiasp);
+  s.L = static_cast<int>(a.seqlen);
+  s.Lp = static_cast<int>(pl.Lp);
+  s.dim = static_cast<int>(a.dim);
+  s.N = static_cast<int>(a.dstate);
+  s.batch = static_cast<int>(a.batch);
+  const int64_t blocks = a.batch * pl.dim_blocks;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.in_bf16) {
+    err = a.delta_softplus ? launch_bwd_ns<true, true>(a, pl, s, blocks, st)
+                           : launch_bwd_ns<true, false>(a, pl, s, blocks, st);
+  } else {
+    err = a.delta_softplus ? launch_bwd_ns<false, true>(a, pl, s, blocks, st)
+                           : launch_bwd_ns<false, false>(a, pl, s, blocks, st);
+  }
+  if (err != 0) return err;
+  {
+    const float* dBp = s.dBp;
+    const float* dCp = s.dCp;
+    float* dB = a.dB;
+    float* dC = a.dC;
+    int blocks_d = static_cast<int>(pl.dim_blocks), batch = s.batch, L = s.L, Lp = s.Lp, N = s.N, NS = pl.NS;
+    const int64_t total = a.batch * a.seqlen * a.dstate;
+    if (total > 0) {
+      void* kargs[] = {&dBp, &dCp, &dB, &dC, &blocks_d, &batch, &L, &Lp, &N, &NS};
+      err = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_reduce_bc_kernel),
+                            dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), kargs, 0, st);
+      if (err != 0) return err;
+    }
+  }
+  return launch_reduce_d(a, s.dAp, s.dDp, s.dbiasp, st);
+}
+
+}  // namespace ssm

@@ -27,6 +27,7 @@
 // the VALU (one v_exp_f32 per state update plus 4 FMA-pipe ops).
 #include <hip/hip_runtime.h>
 
+#include "bc_pack.h"
 #include "device_math.h"
 #include "kernels.h"
 
@@ -41,45 +42,6 @@ typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 
-
-// ---------------------------------------------------------------- B/C pre-pass
-// B, C [Bt, L, N] -> one 32-bit word per (b, n, t), time-contiguous, zero
-// beyond N and L:
-//  * bfloat16 inputs: word = (B bits << 16) | C bits (exact);
-//  * float32 inputs: two words (B, C) per step, i.e. a float2 per step.
-// A wave owning state n then fetches a whole tile of its B and C with one or
-// two scalar loads.
-template <bool BF16_IN>
-__global__ __launch_bounds__(256) void bc_pack_kernel(const void* __restrict__ Bin,
-                                                      const void* __restrict__ Cin,
-                                                      uint32_t* __restrict__ out, int64_t L,
-                                                      int64_t Lp, int N, int NS) {
-  __shared__ uint32_t sb[64][65];
-  __shared__ uint32_t sc[64][65];
-  const int64_t b = blockIdx.y;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 64;
-  for (int i = threadIdx.x; i < 64 * NS; i += 256) {
-    const int tt = i / NS, n = i % NS;
-    const int64_t t = t0 + tt;
-    const bool ok = t < L && n < N;
-    sb[tt][n] = ok ? load_bits<BF16_IN>(Bin, (b * L + t) * N + n) : 0u;
-    sc[tt][n] = ok ? load_bits<BF16_IN>(Cin, (b * L + t) * N + n) : 0u;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * NS; i += 256) {
-    const int n = i / 64, tt = i % 64;
-    const int64_t t = t0 + tt;
-    if (t < Lp) {
-      const int64_t o = (b * NS + n) * Lp + t;
-      if constexpr (BF16_IN) {
-        out[o] = (sb[tt][n] << 16) | sc[tt][n];
-      } else {
-        out[2 * o] = sb[tt][n];
-        out[2 * o + 1] = sc[tt][n];
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------- scan
 
@@ -623,23 +585,9 @@ int launch_scan(const ScanArgs& a, void* stream) {
   s.N = static_cast<int>(a.dstate);
   s.chunk = static_cast<int>(pl.chunk);
   s.batch = static_cast<int>(a.batch);
-  if (pl.Lp > 0) {
-    const int64_t chunks = (pl.Lp + 63) / 64;
-    if (chunks > 0x7fffffff || a.batch > 65535) return hipErrorInvalidConfiguration;
-    const void* bin = a.B;
-    const void* cin = a.C;
-    uint32_t* out = reinterpret_cast<uint32_t*>(ws + pl.off_bc);
-    int64_t L = a.seqlen;
-    int64_t Lpv = pl.Lp;
-    int N = static_cast<int>(a.dstate);
-    int NS = pl.NS;
-    void* kargs[] = {&bin, &cin, &out, &L, &Lpv, &N, &NS};
-    const void* fn = a.in_bf16 ? reinterpret_cast<const void*>(&bc_pack_kernel<true>)
-                               : reinterpret_cast<const void*>(&bc_pack_kernel<false>);
-    const int err = hipLaunchKernel(fn, dim3(static_cast<unsigned>(chunks), static_cast<unsigned>(a.batch)),
-                                    dim3(256), kargs, 0, st);
-    if (err != 0) return err;
-  }
+  const int err = launch_bc_pack(a.B, a.C, reinterpret_cast<uint32_t*>(ws + pl.off_bc), a.batch, a.seqlen,
+                                 pl.Lp, static_cast<int>(a.dstate), pl.NS, a.in_bf16 != 0, st);
+  if (err != 0) return err;
   if (a.in_bf16) {
     return a.out_bf16 ? launch_io<true, true>(a, pl, s, st) : launch_io<true, false>(a, pl, s, st);
   }

@@ -190,3 +190,32 @@ def test_conv_validation(lib):
     assert conv_upd(lib, y=P + 16) == E_ALIAS         # y inside state
     assert conv_upd(lib, state=3 * P) == E_ALIAS      # state over weight
     assert conv_upd(lib, B=0, state=None, x=None, y=None) == OK
+
+
+def bwd(lib, B=2, L=8, d=4, N=4, ind=0, sp=1, ws=40 * P, wsb=1 << 24, **kw):
+    ptrs = dict(u=P, delta=2 * P, A=3 * P, Bm=4 * P, Cm=5 * P, D=6 * P, z=7 * P, bias=8 * P, h0=9 * P,
+                dy=10 * P, dhf=11 * P, du=12 * P, ddelta=13 * P, dA=14 * P, dB=15 * P, dC=16 * P, dD=17 * P,
+                dz=18 * P, dbias=19 * P, dh0=20 * P)
+    ptrs.update(kw)
+    order = ("u", "delta", "A", "Bm", "Cm", "D", "z", "bias", "h0", "dy", "dhf", "du", "ddelta", "dA", "dB",
+             "dC", "dD", "dz", "dbias", "dh0")
+    return lib.ssm_selective_scan_bwd(B, L, d, N, ind, sp, *[vp(ptrs[k]) for k in order], vp(ws), wsb, None)
+
+
+def test_scan_bwd_validation(lib):
+    assert bwd(lib, B=-1) == E_SHAPE
+    assert bwd(lib, N=17) == E_UNSUPPORTED
+    assert bwd(lib, ind=4) == E_DTYPE
+    assert bwd(lib, dy=None) == E_NULLPTR
+    assert bwd(lib, dA=None) == E_NULLPTR
+    assert bwd(lib, dB=None) == E_NULLPTR
+    assert bwd(lib, u=P + 4) == E_ALIGN
+    assert bwd(lib, du=12 * P + 2) == E_ALIGN
+    assert bwd(lib, ws=None) == E_WORKSPACE
+    assert bwd(lib, wsb=16) == E_WORKSPACE
+    assert bwd(lib, du=P) == E_ALIAS                 # output over an input
+    assert bwd(lib, dC=15 * P + 16) == E_ALIAS       # two outputs overlap
+    assert bwd(lib, ws=20 * P) == E_ALIAS            # workspace over dh0
+    assert bwd(lib, d=0) == OK
+    need = lib.ssm_scan_bwd_workspace_bytes(2, 8, 4, 4)
+    assert need > 0 and lib.ssm_scan_bwd_workspace_bytes(1, 8, 4, 17) == 0
