@@ -57,8 +57,12 @@ def compare(name, g, ref, mag, tol, channels=None, skip=()):
         got = download(g[k])
         if channels is not None:
             ch = np.asarray(channels)
-            got = {"du": got[:, :, ch], "ddelta": got[:, :, ch], "dz": got[:, :, ch], "dA": got[ch],
-                   "dD": got[ch], "ddelta_bias": got[ch], "dh0": got[:, ch]}[k]
+            if k in ("du", "ddelta", "dz"):
+                got = got[:, :, ch]
+            elif k == "dh0":
+                got = got[:, ch]
+            else:                       # dA, dD, ddelta_bias
+                got = got[ch]
         report(f"{name} {k}", oracle.scaled_error(got, ref[k], mag[k]), tol)
 
 
