@@ -283,6 +283,47 @@ def bench_conv(args, torch, binding, synth):
     return fwd, upd
 
 
+# Algorithmic VALU work of the backward, per state update: the transition
+# exp(dt*A) [2 + 1 slots], the state and readout recomputed [2], the adjoint
+# lam = dp*C + mu and mu = a*lam [2], dA [2], d(dt) [3], du [2], dB and dC
+# contributions [2]; per (b,l,d): softplus and its derivative, silu and its
+# derivative, dz, dD, bias and output scaling [~20].
+BWD_SLOTS_PER_UPDATE = 16
+BWD_SLOTS_PER_BLD = 20
+
+
+def bench_bwd(args, torch, binding, synth, inp):
+    """Backward of the selective scan on the 1.4B-shaped layer (float32 dy)."""
+    import numpy as np
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dt = inp["in_dtype"]
+
+    def up(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t = {k: up(inp[k], dt) for k in ("u", "delta", "B", "C", "z")}
+    for k in ("A", "D", "delta_bias"):
+        t[k] = up(inp[k], "f32")
+    dy = torch.from_numpy((np.random.default_rng(26).standard_normal(inp["u"].shape) * 0.1)
+                          .astype(np.float32)).to(dev)
+    ws = torch.empty(binding.ssm_scan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate),
+                     dtype=torch.uint8, device=dev)
+    fn = lambda: binding.ssm_selective_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, D=t["D"],  # noqa
+                                                z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True,
+                                                workspace=ws)
+    us = _timed(torch, fn, args.bwd_steps, 2)
+    ups = w.updates
+    slots = ups * BWD_SLOTS_PER_UPDATE + w.batch * w.seqlen * w.dim * BWD_SLOTS_PER_BLD
+    ach = slots / (us * 1e-6) / 1e12
+    return {"workload": f"{w.name} backward (dy float32, all gradients float32)", "us_per_call": us,
+            "G_updates_per_s": ups / (us * 1e-6) / 1e9,
+            "roofline": {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_SLOTS / 1e12, "unit": "Tslot/s",
+                         "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +335,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--conv-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=8192)
@@ -359,6 +402,8 @@ def main():
     }
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, binding, synth)
+    if not args.no_bwd:
+        result["scan_bwd"] = bench_bwd(args, torch, binding, synth, inp)
     if not args.no_conv:
         result["conv1d"], result["conv1d_update"] = bench_conv(args, torch, binding, synth)
     if not args.no_cpu_baseline:

@@ -132,15 +132,40 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   const int64_t plane = static_cast<int64_t>(b) * L;
 
   // Cooperative: this thread's items of tile k are steps w + W*i (i < IT) of
-  // channel `lane`; with more waves than steps, waves >= T have none.
+  // channel `lane`; with more waves than steps, waves >= T have none. The
+  // inputs of the next tile are fetched into registers (raw storage bits)
+  // while the current tile is computed, then staged into LDS.
+  constexpr int BCW = (NS * T * WPS + W * 64 - 1) / (W * 64);  // packed B/C words per thread
   auto item_step = [&](int i) __attribute__((always_inline)) { return w + W * i; };
-  auto load_in = [&](const void* ptr, int t) __attribute__((always_inline)) -> float {
-    return (ch_ok && t >= 0 && t < L) ? load_elem<BF16_IN>(ptr, (plane + t) * Dm + ch) : 0.0f;
+  auto item_ok = [&](int t) __attribute__((always_inline)) { return ch_ok && t >= 0 && t < L; };
+  auto raw_in = [&](const void* ptr, int t) __attribute__((always_inline)) -> uint32_t {
+    return item_ok(t) ? load_bits<BF16_IN>(ptr, (plane + t) * Dm + ch) : 0u;
   };
-  auto load_bc_tile = [&](int k) __attribute__((always_inline)) {
-    for (int i = threadIdx.x; i < NS * T * WPS; i += W * 64) {
-      const int n = i / (T * WPS), j = i % (T * WPS);
-      sBC[n][j] = bcb[(static_cast<int64_t>(n) * Lp + k * T) * WPS + j];
+  uint32_t r_u[IT], r_d[IT], r_z[IT], r_bc[BCW];
+  float r_dy[IT];
+  auto fetch_items = [&](int k, bool with_grad) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int t = k * T + item_step(i);
+      r_u[i] = raw_in(p.u, t);
+      r_d[i] = raw_in(p.delta, t);
+      if (with_grad) {
+        r_z[i] = has_z ? raw_in(p.z, t) : 0u;
+        r_dy[i] = item_ok(t) ? p.dy[(plane + t) * Dm + ch] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BCW; ++j) {
+      const int idx = threadIdx.x + j * W * 64;
+      const int n = idx / (T * WPS), q = idx % (T * WPS);
+      r_bc[j] = idx < NS * T * WPS ? bcb[(static_cast<int64_t>(n) * Lp + k * T) * WPS + q] : 0u;
+    }
+  };
+  auto stage_bc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < BCW; ++j) {
+      const int idx = threadIdx.x + j * W * 64;
+      if (idx < NS * T * WPS) sBC[idx / (T * WPS)][idx % (T * WPS)] = r_bc[j];
     }
   };
   auto bc_of = [&](int n, int t, float& bval, float& cval) __attribute__((always_inline)) {
@@ -153,28 +178,35 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       cval = __uint_as_float(sBC[n][2 * t + 1]);
     }
   };
-  auto step_size = [&](int t, float& x_out) __attribute__((always_inline)) -> float {
-    const float x = load_in(p.delta, t) + bv;
+  // Step size of item i of tile k from the fetched raw delta (0 beyond L).
+  auto step_size = [&](int k, int i, float& x_out) __attribute__((always_inline)) -> float {
+    const float x = bits_to_f32<BF16_IN>(r_d[i]) + bv;
     x_out = x;
     const float dt = SOFTPLUS ? softplus_f(x) : x;
-    return t < L ? dt : 0.0f;
+    return k * T + item_step(i) < L ? dt : 0.0f;
   };
 
   // ---------------------------------------------------------------- sweep 1
-  for (int k = 0; k < nt; ++k) {
+  auto stage1 = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = item_step(i);
       if (tt < T) {
-        const int t = k * T + tt;
         float x;
-        const float dt = step_size(t, x);
-        const float uv = load_in(p.u, t);
+        const float dt = step_size(k, i, x);
+        const float uv = bits_to_f32<BF16_IN>(r_u[i]);
         sQ[tt][lane] = make_float4(dt, dt * uv, 0.0f, uv);
       }
     }
-    load_bc_tile(k);
-    __syncthreads();
+    stage_bc();
+  };
+  if (nt > 0) {
+    fetch_items(0, false);
+    stage1(0);
+  }
+  __syncthreads();
+  for (int k = 0; k < nt; ++k) {
+    if (k + 1 < nt) fetch_items(k + 1, false);
     // checkpoint: the states entering tile k
     float* ck = p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
 #pragma unroll
@@ -192,6 +224,8 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       }
     }
     __syncthreads();
+    if (k + 1 < nt) stage1(k + 1);
+    __syncthreads();
   }
 
   // ---------------------------------------------------------------- sweep 2
@@ -203,22 +237,28 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
     dA_acc[s] = 0.0f;
   }
   float dD_acc = 0.0f, dbias_acc = 0.0f;
-  // Items of the tile being finished (kept from its preparation to its epilogue).
+  // Items of the tile being finished (kept from its staging to its epilogue).
   float e_dy[IT], e_dsilu[IT], e_dsp[IT], e_u[IT], e_dp[IT];
-
-  auto prepare_bwd = [&](int k) __attribute__((always_inline)) {
+  // Checkpoint of the next tile to process, fetched one tile ahead.
+  float r_ck[S];
+  auto fetch2 = [&](int k) __attribute__((always_inline)) {
+    fetch_items(k, true);
+    const float* ck = p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
+#pragma unroll
+    for (int s = 0; s < S; ++s) r_ck[s] = ch_ok ? ck[static_cast<int64_t>(s) * Dm] : 0.0f;
+  };
+  auto stage2 = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = item_step(i);
       if (tt < T) {
-        const int t = k * T + tt;
         float x;
-        const float dt = step_size(t, x);
-        const float uv = load_in(p.u, t);
-        const float dyv = (ch_ok && t >= 0 && t < L) ? p.dy[(plane + t) * Dm + ch] : 0.0f;
+        const float dt = step_size(k, i, x);
+        const float uv = bits_to_f32<BF16_IN>(r_u[i]);
+        const float dyv = r_dy[i];
         float g = 1.0f, dsilu = 0.0f;
         if (has_z) {
-          const float zv = load_in(p.z, t);
+          const float zv = bits_to_f32<BF16_IN>(r_z[i]);
           const float sg = sigmoid_f(zv);
           g = zv * sg;
           dsilu = sg * fmaf(zv, 1.0f - sg, 1.0f);
@@ -232,12 +272,19 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         sQ[tt][lane] = make_float4(dt, dt * uv, dp, uv);
       }
     }
-    load_bc_tile(k);
+    stage_bc();
   };
 
-  if (nt > 0) prepare_bwd(nt - 1);
+  if (nt > 0) {
+    fetch2(nt - 1);
+    stage2(nt - 1);
+  }
   __syncthreads();
   for (int k = nt - 1; k >= 0; --k) {
+    float hh[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) hh[s] = r_ck[s];
+    if (k > 0) fetch2(k - 1);
     // -- waves: recompute the tile, then the adjoint recurrence
     float dtv[T], dtu[T], dpv[T], uvv[T];
 #pragma unroll
@@ -248,10 +295,6 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       dpv[t] = q.z;
       uvv[t] = q.w;
     }
-    const float* ck = p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
-    float hh[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) hh[s] = ch_ok ? ck[static_cast<int64_t>(s) * Dm] : 0.0f;
     float av[T][S], ahv[T][S], hs[T][S];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -301,7 +344,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       }
     }
     __syncthreads();
-    // -- epilogue of tile k (per item), then preparation of tile k-1
+    // -- epilogue of tile k (per item), then staging of tile k-1
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = item_step(i);
@@ -326,7 +369,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         }
       }
     }
-    if (k > 0) prepare_bwd(k - 1);
+    if (k > 0) stage2(k - 1);
     __syncthreads();
   }
 
