@@ -111,11 +111,10 @@ constexpr int64_t kChunkWhenBlocksAtMost = 128;
 
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
-// Backward: same state mapping (N <= 16), tiles of kBwdTile steps; workspace
+// Backward: same state mapping (N <= 16), the forward's tiles; workspace
 // = packed B/C, per-tile state checkpoints [B][tiles][NS][d], per-block
 // partials of dB and dC [blocks_d][B][Lp][NS], per-batch partials of dA
 // [B][d][N], dD and the bias gradient [B][d].
-constexpr int64_t kBwdTile = 8;
 constexpr int64_t kBwdMaxState = 16;
 struct ScanBwdPlan {
   bool ok;
@@ -133,6 +132,11 @@ size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
 int launch_scan(const ScanArgs& a, void* stream);
 int launch_state_update(const UpdateArgs& a, void* stream);
 int launch_scan_bwd(const ScanBwdArgs& a, void* stream);
+// Forward recurrence only (N <= 16, one pass over each batch row), storing the
+// states at every tile start into ckpt [B][tiles][NS][d]; B/C already packed
+// at bc. Tiles are scan_tile_steps(NS) steps long.
+int launch_scan_checkpoints(const ScanArgs& a, const uint32_t* bc, float* ckpt, void* stream);
+int scan_tile_steps(int NS);
 int launch_conv1d_fwd(const ConvArgs& a, void* stream);
 int launch_conv1d_update(const ConvUpdateArgs& a, void* stream);
 

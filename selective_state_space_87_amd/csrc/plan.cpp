@@ -69,14 +69,15 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
 ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   ScanBwdPlan p{};
   p.ok = batch >= 0 && seqlen >= 0 && dim >= 0 && dstate >= 1 && dstate <= kBwdMaxState &&
-         seqlen < (int64_t(1) << 30) && dim < (int64_t(1) << 24) && batch < (int64_t(1) << 24);
+         seqlen < (int64_t(1) << 30) && dim < (int64_t(1) << 24) && batch < (int64_t(1) << 24) &&
+         seqlen * dim * 4 <= kPlaneBytesMax;  // one pass per batch row: 32-bit buffer offsets
   if (!p.ok) return p;
   p.NS = ceil_pow2(dstate);
   p.W = p.NS < 16 ? p.NS : 8;
   p.S = p.NS / p.W;
   p.Lp = round_up(seqlen, kPadSteps);
   p.dim_blocks = ceil_div(dim, 64);
-  const int64_t tiles = p.Lp / kBwdTile;
+  const int64_t tiles = p.Lp / (p.NS == 16 ? 8 : 16);  // the forward's tile length for this NS
   size_t off = 0;
   p.off_bc = off;
   off += align256(size_t(2 * batch * p.NS * p.Lp) * 4);

@@ -12,10 +12,10 @@
 //   dz_l   = dy_l p_l silu'(z_l) with p the pre-gate output; ddelta = ddt softplus'(x)
 //
 // One block per (batch, 64 channels), the forward's mapping: lane = channel,
-// wave w = states w*S .. w*S+S-1. Two sweeps:
-//   1. forward over tiles of T steps, storing every wave's states at each
-//      tile start (checkpoints, in the workspace);
-//   2. backward over the tiles in reverse: recompute the tile's states and
+// wave w = states w*S .. w*S+S-1. Two passes:
+//   1. the forward kernel in its checkpoint mode stores every wave's states
+//      at each tile start (scan_fwd.hip; same mapping and tiles);
+//   2. this kernel, over the tiles in reverse: recompute the tile's states and
 //      transitions from its checkpoint, read the pre-gate output out of them
 //      (partials over waves in LDS, as in the forward), then run the adjoint
 //      recurrence. Per-step sums over states (ddt, du) go through LDS;
@@ -35,8 +35,6 @@
 namespace ssm {
 
 namespace {
-
-constexpr int kBwdT = 8;  // steps per tile
 
 struct ScanBwd {
   const void* u;
@@ -89,9 +87,8 @@ __device__ __forceinline__ float lane_transpose_sum(float (&v)[G], int lane) {
   return r;
 }
 
-template <int S, int W, bool BF16_IN, bool SOFTPLUS>
+template <int S, int W, int T, bool BF16_IN, bool SOFTPLUS>
 __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
-  constexpr int T = kBwdT;
   constexpr int NS = S * W;
   constexpr int IT = T >= W ? T / W : 1;   // cooperative items per thread per tile
   constexpr int WPS = BF16_IN ? 1 : 2;
@@ -116,14 +113,13 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   const int nt = Lp / T;
   const int64_t bdn = (static_cast<int64_t>(b) * Dm + ch) * N;
 
-  float A1[S], A2[S], h[S];
+  float A1[S], A2[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int n = w * S + s;
     const bool ok = ch_ok && n < N;
     A1[s] = ok ? p.A[static_cast<int64_t>(ch) * N + n] : 0.0f;
     A2[s] = A1[s] * kLog2e;
-    h[s] = (ok && p.h0) ? p.h0[bdn + n] : 0.0f;
   }
   const float Dv = (ch_ok && p.D) ? p.D[ch] : 0.0f;
   const float bv = (ch_ok && p.bias) ? p.bias[ch] : 0.0f;
@@ -143,16 +139,14 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   };
   uint32_t r_u[IT], r_d[IT], r_z[IT], r_bc[BCW];
   float r_dy[IT];
-  auto fetch_items = [&](int k, bool with_grad) __attribute__((always_inline)) {
+  auto fetch_items = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int t = k * T + item_step(i);
       r_u[i] = raw_in(p.u, t);
       r_d[i] = raw_in(p.delta, t);
-      if (with_grad) {
-        r_z[i] = has_z ? raw_in(p.z, t) : 0u;
-        r_dy[i] = item_ok(t) ? p.dy[(plane + t) * Dm + ch] : 0.0f;
-      }
+      r_z[i] = has_z ? raw_in(p.z, t) : 0u;
+      r_dy[i] = item_ok(t) ? p.dy[(plane + t) * Dm + ch] : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < BCW; ++j) {
@@ -186,49 +180,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
     return k * T + item_step(i) < L ? dt : 0.0f;
   };
 
-  // ---------------------------------------------------------------- sweep 1
-  auto stage1 = [&](int k) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int tt = item_step(i);
-      if (tt < T) {
-        float x;
-        const float dt = step_size(k, i, x);
-        const float uv = bits_to_f32<BF16_IN>(r_u[i]);
-        sQ[tt][lane] = make_float4(dt, dt * uv, 0.0f, uv);
-      }
-    }
-    stage_bc();
-  };
-  if (nt > 0) {
-    fetch_items(0, false);
-    stage1(0);
-  }
-  __syncthreads();
-  for (int k = 0; k < nt; ++k) {
-    if (k + 1 < nt) fetch_items(k + 1, false);
-    // checkpoint: the states entering tile k
-    float* ck = p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (ch_ok) ck[static_cast<int64_t>(s) * Dm] = h[s];
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float4 q = sQ[t][lane];
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        float bval, cval;
-        bc_of(w * S + s, t, bval, cval);
-        h[s] = fmaf(exp2_hw(q.x * A2[s]), h[s], q.y * bval);
-      }
-    }
-    __syncthreads();
-    if (k + 1 < nt) stage1(k + 1);
-    __syncthreads();
-  }
-
-  // ---------------------------------------------------------------- sweep 2
+  // ------------------------------------------- backward over the tiles
   float mu[S], dA_acc[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -242,7 +194,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   // Checkpoint of the next tile to process, fetched one tile ahead.
   float r_ck[S];
   auto fetch2 = [&](int k) __attribute__((always_inline)) {
-    fetch_items(k, true);
+    fetch_items(k);
     const float* ck = p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
 #pragma unroll
     for (int s = 0; s < S; ++s) r_ck[s] = ch_ok ? ck[static_cast<int64_t>(s) * Dm] : 0.0f;
@@ -458,9 +410,10 @@ int launch_reduce_d(const ScanBwdArgs& a, const float* dAp, const float* dDp, co
 
 template <int S, int W, bool BI, bool SP>
 int launch_bwd_sw(const ScanBwdArgs& a, const ScanBwd& s, int64_t blocks, hipStream_t st) {
+  constexpr int T = S * W == 16 ? 8 : 16;  // the forward's tiles (checkpoint spacing)
   ScanBwd args = s;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_bwd_kernel<S, W, BI, SP>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_bwd_kernel<S, W, T, BI, SP>),
                          dim3(static_cast<unsigned>(blocks)), dim3(W * 64), kargs, 0, st);
 }
 
@@ -488,6 +441,25 @@ int launch_scan_bwd(const ScanBwdArgs& a, void* stream) {
   err = launch_bc_pack(a.B, a.C, reinterpret_cast<uint32_t*>(ws + pl.off_bc), a.batch, a.seqlen, pl.Lp,
                            static_cast<int>(a.dstate), pl.NS, a.in_bf16 != 0, st);
   if (err != 0) return err;
+  {
+    ScanArgs f{};
+    f.u = a.u;
+    f.delta = a.delta;
+    f.A = a.A;
+    f.delta_bias = a.delta_bias;
+    f.h0 = a.h0;
+    f.batch = a.batch;
+    f.seqlen = a.seqlen;
+    f.dim = a.dim;
+    f.dstate = a.dstate;
+    f.in_bf16 = a.in_bf16;
+    f.delta_softplus = a.delta_softplus;
+    if (pl.Lp > 0) {
+      err = launch_scan_checkpoints(f, reinterpret_cast<const uint32_t*>(ws + pl.off_bc),
+                                    reinterpret_cast<float*>(ws + pl.off_ckpt), st);
+      if (err != 0) return err;
+    }
+  }
   ScanBwd s;
   s.u = a.u;
   s.delta = a.delta;

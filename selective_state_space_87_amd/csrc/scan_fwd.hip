@@ -57,7 +57,8 @@ struct Scan {
   const uint32_t* BC;  // packed B/C (see bc_pack_kernel)
   void* y;
   float* h_final;
-  float* hsum;         // summary pass: chunk c's final state from zero into slot c + 1
+  float* hsum;         // summary pass: chunk c's final state from zero into slot c + 1;
+                       // checkpoint pass: states at every tile start, [B][tiles][NS][d]
   float* ssum;         // summary pass: chunk c's sum of step sizes, [chunks-1][B][d]
   int L, Lp, dim, N, chunk, batch;
 };
@@ -72,10 +73,14 @@ constexpr uint32_t kStepOut = 0x40000000u;
 // Waves whose index has this bit set take the "late" tile order (see iter).
 constexpr int kLateWaveMask = 4;
 
-// SUMMARY = false: the scan of one chunk (or of the whole sequence), with
-// readout, gate and store. SUMMARY = true: the chunk's recurrence from a zero
-// state only, exporting its final state and the sum of its step sizes.
-template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool SUMMARY>
+// MODE kFull: the scan of one chunk (or of the whole sequence), with readout,
+// gate and store. kSummary: the chunk's recurrence from a zero state only,
+// exporting its final state and the sum of its step sizes. kCheckpoint: the
+// recurrence from h0 only, storing every wave's states at each tile start
+// (for the backward pass, which recomputes each tile from them).
+constexpr int kFull = 0, kSummary = 1, kCheckpoint = 2;
+
+template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, int MODE>
 __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int NS = S * W;        // padded state count
   constexpr int IT = T / W;        // cooperative items per thread per tile
@@ -85,7 +90,8 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int LNC = __builtin_ctz(NC);
   constexpr int WPS = BF16_IN ? 1 : 2;              // packed B/C words per step
   constexpr uint32_t IN_B = BF16_IN ? 2 : 4, OUT_B = BF16_OUT ? 2 : 4;
-  constexpr bool READOUT = !SUMMARY;
+  constexpr bool READOUT = MODE == kFull;
+  constexpr bool SUMMARY = MODE == kSummary;
 
   // Step sizes live in a ring of 4 tile slots (tile k in slot k & 3): tiles
   // are prepared two at a time, every other tile. Partial readouts are
@@ -117,7 +123,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // its carried-in state (for chunk 0 a copy of h0, so that h_final may
   // overwrite h0 while other chunks run); the summary pass from zeros.
   const int64_t bdn = (static_cast<int64_t>(b) * Dm + ch) * N;
-  const float* hinit = SUMMARY ? nullptr
+  const float* hinit = MODE == kSummary ? nullptr
                                : (p.carry ? p.carry + static_cast<int64_t>(c) * p.batch * Dm * N : p.h0);
   float A2[S], h[S];
 #pragma unroll
@@ -352,6 +358,13 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     constexpr int P = J & 1;
     constexpr int Q = 1 - P;
     float gp[IT][GN][GW];
+    if constexpr (MODE == kCheckpoint) {
+      if (ch_ok) {
+        float* ck = p.hsum + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
+#pragma unroll
+        for (int s = 0; s < S; ++s) ck[static_cast<int64_t>(s) * Dm] = h[s];
+      }
+    }
     if constexpr (decltype(late)::value) {
       lds_reads(jj, dd_next, gp);
       __builtin_amdgcn_sched_barrier(0);
@@ -463,7 +476,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
         if (n < N) p.h_final[bdn + n] = h[s];
       }
     }
-  } else {
+  } else if constexpr (MODE == kSummary) {
     if (ch_ok) {
       const int64_t cb = static_cast<int64_t>(c) * p.batch + b;
       const int64_t cb1 = cb + p.batch;              // slot c + 1
@@ -514,7 +527,7 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
   Scan args = s;
   void* kargs[] = {&args};
   if (pl.chunks > 1) {
-    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, true>),
+    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, kSummary>),
                               dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks - 1)),
                               dim3(W * 64), kargs, 0, st);
     if (err != 0) return err;
@@ -530,7 +543,7 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
                           dim3(static_cast<unsigned>((bdn + 255) / 256)), dim3(256), fargs, 0, st);
     if (err != 0) return err;
   }
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, false>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, kFull>),
                          dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks)),
                          dim3(W * 64), kargs, 0, st);
 }
@@ -558,6 +571,53 @@ int launch_io(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
 }
 
 }  // namespace
+
+template <bool BI, bool SP>
+int launch_ckpt_ns(const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_t st) {
+  Scan args = s;
+  void* kargs[] = {&args};
+  const void* fn = nullptr;
+  switch (pl.NS) {
+    case 1: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 1, 16, BI, false, SP, kCheckpoint>); break;
+    case 2: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 2, 16, BI, false, SP, kCheckpoint>); break;
+    case 4: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 4, 16, BI, false, SP, kCheckpoint>); break;
+    case 8: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 8, 16, BI, false, SP, kCheckpoint>); break;
+    case 16: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<2, 8, 8, BI, false, SP, kCheckpoint>); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(pl.W * 64), kargs, 0, st);
+}
+
+int scan_tile_steps(int NS) { return NS == 16 ? 8 : 16; }
+
+int launch_scan_checkpoints(const ScanArgs& a, const uint32_t* bc, float* ckpt, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ScanPlan pl = plan_scan(a.batch, a.seqlen, a.dim, a.dstate);
+  if (!pl.ok || pl.NS > 16 || a.batch == 0 || a.dim == 0) return hipErrorInvalidValue;
+  // one pass over the whole sequence: each batch row's plane must fit the
+  // 32-bit buffer offsets
+  if (a.seqlen * a.dim * 4 > kPlaneBytesMax) return hipErrorInvalidValue;
+  Scan s{};
+  s.u = a.u;
+  s.delta = a.delta;
+  s.A = a.A;
+  s.bias = a.delta_bias;
+  s.h0 = a.h0;
+  s.BC = bc;
+  s.hsum = ckpt;
+  s.L = static_cast<int>(a.seqlen);
+  s.Lp = static_cast<int>(pl.Lp);
+  s.dim = static_cast<int>(a.dim);
+  s.N = static_cast<int>(a.dstate);
+  s.chunk = static_cast<int>(pl.Lp);
+  s.batch = static_cast<int>(a.batch);
+  const int64_t blocks = a.batch * pl.dim_blocks;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.in_bf16) {
+    return a.delta_softplus ? launch_ckpt_ns<true, true>(pl, s, blocks, st) : launch_ckpt_ns<true, false>(pl, s, blocks, st);
+  }
+  return a.delta_softplus ? launch_ckpt_ns<false, true>(pl, s, blocks, st) : launch_ckpt_ns<false, false>(pl, s, blocks, st);
+}
 
 int launch_scan(const ScanArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
