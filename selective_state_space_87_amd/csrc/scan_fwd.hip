@@ -314,7 +314,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   //       even tiles, preparation of tiles k+2 and k+3 and the fetch of the
   //       raw inputs of tiles k+4 and k+5.
   // "Late" waves run (2), (4), (1), (3): the readout and the preparation
-  // first, then the whole recurrence. The two waves that share a SIMD take
+  // first, then the whole recurrence. A wave raises its issue priority while
+  // it runs the recurrence, so the SIMD's arbiter prefers it over the other
+  // wave's cooperative work (which mostly waits on memory and LDS). The two waves that share a SIMD take
   // different orders, so while one runs the recurrence the other runs the
   // cooperative work, instead of both waiting on the same phase. Every
   // dependency is on data written before the previous barrier, so both
@@ -373,14 +375,17 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       load_bc(k + 1 < nt ? k + 1 : k, std::integral_constant<int, Q>{});  // clamped: stays in SGPRs
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(2);
       steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, 0>{},
             std::integral_constant<int, T / 2>{});
       steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
             std::integral_constant<int, T>{});
+      __builtin_amdgcn_s_setprio(0);
     } else {
       load_bc(k + 1 < nt ? k + 1 : k, std::integral_constant<int, Q>{});  // clamped: stays in SGPRs
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(2);
       steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, 0>{},
             std::integral_constant<int, T / 2>{});
       __builtin_amdgcn_sched_barrier(0);
@@ -388,6 +393,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       __builtin_amdgcn_sched_barrier(0);
       steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
             std::integral_constant<int, T>{});
+      __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       coop(k, jj, gp);
     }
