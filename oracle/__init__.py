@@ -24,6 +24,7 @@ from .ssm_oracle import (  # noqa: F401
     softplus,
     silu,
     discretize_delta,
+    input_coefficient,
     selective_scan,
     selective_state_update,
     scaled_error,

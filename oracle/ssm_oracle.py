@@ -17,8 +17,9 @@ Readings of the pages taken here (the pages disagree or are silent):
 - The exponent is exp(delta * A) with A <= 0 passed in directly. One listing
   on [TtoM] negates the exponent while also negating A, which makes every
   step grow; the discretisation snippet in [TtoM] section 3.1 has no minus.
-- B-bar x is delta * B * x (the simplified form both listings in [TtoM] use),
-  not the exact zero-order-hold integral that [Breakthrough] section 2.3 names.
+- B-bar x is delta * B * x (the simplified form both listings in [TtoM] use)
+  by default; the exact zero-order-hold integral that [Breakthrough] section
+  2.3 names, (exp(delta A) - 1) / A * B * x, is an option (``zoh=True``).
 - The optional bias is added before softplus ([TtoM] section 5: the step-size
   projection has a bias and its output goes through softplus).
 - The gate multiplies after the D skip: out = (C h + D u) * silu(z)
@@ -39,6 +40,7 @@ __all__ = [
     "discretize_delta",
     "selective_scan",
     "selective_state_update",
+    "input_coefficient",
     "scaled_error",
 ]
 
@@ -90,8 +92,26 @@ def discretize_delta(delta_raw, delta_bias=None, delta_softplus=False):
     return dt
 
 
+def input_coefficient(dt, A, zoh=False):
+    """Coefficient k of the input term, B-bar x = k * B * x, per (.., d, n).
+
+    Simplified form (default): k = dt, the form of both listings in [TtoM]
+    (sections 3.1 and 5). Exact zero-order hold ([Breakthrough] section 二.3
+    names ZOH; for a diagonal A the integral of exp(A s) over one step is
+    closed-form): k = (exp(dt A) - 1) / A, and k = dt where A = 0 (the limit).
+    dt: [..., d, 1] or broadcastable; A: [d, N].
+    """
+    dt = np.asarray(dt, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    if not zoh:
+        return np.broadcast_to(dt, np.broadcast_shapes(dt.shape, A.shape))
+    x = dt * A
+    safe_A = np.where(A == 0.0, 1.0, A)
+    return np.where(A == 0.0, dt, np.expm1(x) / safe_A)
+
+
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                   delta_softplus=False, h0=None, want_magnitude=False):
+                   delta_softplus=False, h0=None, want_magnitude=False, zoh=False):
     """Sequential selective scan in float64.
 
     Shapes follow the selective_scan docstring of [TtoM] section 3.1:
@@ -128,7 +148,8 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     for l in range(L):
         dt_l = dt[:, l, :]                                   # [Bt, d]
         a = np.exp(dt_l[:, :, None] * A[None, :, :])         # Abar  [Bt, d, N]
-        bx = dt_l[:, :, None] * B[:, l, None, :] * u[:, l, :, None]  # Bbar x
+        k = input_coefficient(dt_l[:, :, None], A[None, :, :], zoh)
+        bx = k * B[:, l, None, :] * u[:, l, :, None]                 # Bbar x
         h = a * h + bx
         y[:, l, :] = (h * C[:, l, None, :]).sum(axis=-1)
         if want_magnitude:
@@ -151,7 +172,7 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
 
 def selective_state_update(state, x, delta, A, B, C, D=None, z=None,
                            delta_bias=None, delta_softplus=False,
-                           want_magnitude=False):
+                           want_magnitude=False, zoh=False):
     """One decode step: new state and output for a single token, in float64.
 
     [TtoM] section 6.3 (each generation step does a fixed amount of work on
@@ -172,7 +193,7 @@ def selective_state_update(state, x, delta, A, B, C, D=None, z=None,
     C = _f64(C)
     dt = discretize_delta(delta, delta_bias, delta_softplus)   # [Bt, d]
     a = np.exp(dt[:, :, None] * A[None, :, :])
-    bx = dt[:, :, None] * B[:, None, :] * x[:, :, None]
+    bx = input_coefficient(dt[:, :, None], A[None, :, :], zoh) * B[:, None, :] * x[:, :, None]
     s_new = a * s + bx
     y = (s_new * C[:, None, :]).sum(axis=-1)
     if want_magnitude:
