@@ -29,7 +29,8 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", os.path.join(ROOT, "include")]
 CXX = os.environ.get("CXX_HOST", "g++")
 
-DEVICE_SOURCES = ["scan_fwd.hip", "scan_bwd.hip", "state_update.hip", "conv1d.hip"]
+DEVICE_SOURCES = ["scan_fwd.hip", "scan_fwd_bb.hip", "scan_fwd_bf.hip", "scan_fwd_fb.hip", "scan_fwd_ff.hip",
+                  "scan_bwd.hip", "state_update.hip", "conv1d.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 

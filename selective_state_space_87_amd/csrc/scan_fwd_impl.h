@@ -1,0 +1,609 @@
+// Selective scan forward for gfx950: kernel templates and their launchers,
+// shared by the per-dtype translation units (scan_fwd_{bb,bf,fb,ff}.hip).
+//
+// Recurrence ("从 Transformer 到 Mamba", ybb.press, sections 3.1 and 5):
+//   dt = softplus(delta + bias); h[n] = exp(dt*A[n]) h[n] + dt*B[n]*u;
+//   y = (sum_n C[n] h[n] + D u) * silu(z)      (gate as in section 5's block)
+//
+// Work decomposition. A block owns 64 channels (b, d0..d0+63) of one batch
+// row (and one sequence chunk) and all N states of each: lane l of every wave
+// is channel d0+l, and wave w owns states n = w*S .. w*S+S-1, kept in VGPRs
+// for the whole chunk; every state chain is walked once, in order. N = 16
+// runs two states per lane on eight waves; smaller N one state per wave.
+//
+// Time is processed in tiles of T steps (8 at N = 16). Per tile:
+//   * recurrence: each wave advances its states through the tile. B[t, n] and
+//     C[t, n] are the same for every lane of the wave: a pre-pass packs them
+//     per state, time-major, and the wave reads a tile of them with scalar
+//     loads into SGPRs. The wave's share of the readout, sum_s C h, goes to an
+//     LDS ring (XOR-swizzled: conflict-free writes and 16-byte reads).
+//   * cooperative: the block finishes an earlier tile (sum of the partial
+//     readouts in a fixed order, + D u, * silu(z), store) and prepares later
+//     tiles (softplus step size and dt*u into an LDS ring; D u and the gate in
+//     registers). Per-(b, l, d) work is done once, not once per wave. Global
+//     loads of u, delta and z run four tiles ahead.
+// The two waves sharing a SIMD take the two phases in opposite orders (see
+// iter). There is no MFMA: this is not a dense contraction. The kernel is
+// bound by the VALU (one v_exp_f32 per state update plus 4 FMA-pipe ops).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "bc_pack.h"
+#include "device_math.h"
+#include "kernels.h"
+
+namespace ssm {
+
+struct Scan {
+  const void* u;
+  const void* delta;
+  const void* z;
+  const float* A;
+  const float* D;
+  const float* bias;
+  const float* h0;     // initial state [B, d, N] of a single-pass scan, or null (zeros)
+  const float* carry;  // chunked: chunk c starts from carry[c] ([chunks][B][d][N])
+  const uint32_t* BC;  // packed B/C (see bc_pack_kernel)
+  void* y;
+  float* h_final;
+  float* hsum;         // summary pass: chunk c's final state from zero into slot c + 1;
+                       // checkpoint pass: states at every tile start, [B][tiles][NS][d]
+  float* ssum;         // summary pass: chunk c's sum of step sizes, [chunks-1][B][d]
+  int L, Lp, dim, N, chunk, batch;
+};
+
+// Per (input, output) dtype: launch the scan (and, for float32 output, the
+// checkpoint pass) of a planned shape. Defined in scan_fwd_<in><out>.hip.
+int launch_scan_bb(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st);
+int launch_scan_bf(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st);
+int launch_scan_fb(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st);
+int launch_scan_ff(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st);
+int launch_ckpt_b(const ScanArgs& a, const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_t st);
+int launch_ckpt_f(const ScanArgs& a, const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_t st);
+
+namespace {
+
+typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
+
+// s_waitcnt immediates (gfx9 encoding); counters not named are left at their
+// maxima (no wait on them).
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+
+
+// ---------------------------------------------------------------- scan
+
+
+// Out-of-range markers of the two parts of a buffer offset: the lane part
+// (channel beyond d) and the wave-uniform step part (step outside the chunk).
+// A chunk's plane is at most 2^30 bytes, so an offset with either marker,
+// or both, is beyond every descriptor's size and the access is masked.
+constexpr uint32_t kLaneOut = 0x80000000u;
+constexpr uint32_t kStepOut = 0x40000000u;
+
+// Waves whose index has this bit set take the "late" tile order (see iter).
+constexpr int kLateWaveMask = 4;
+
+// MODE kFull: the scan of one chunk (or of the whole sequence), with readout,
+// gate and store. kSummary: the chunk's recurrence from a zero state only,
+// exporting its final state and the sum of its step sizes. kCheckpoint: the
+// recurrence from h0 only, storing every wave's states at each tile start
+// (for the backward pass, which recomputes each tile from them).
+constexpr int kFull = 0, kSummary = 1, kCheckpoint = 2;
+
+template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, int MODE>
+__global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
+  constexpr int NS = S * W;        // padded state count
+  constexpr int IT = T / W;        // cooperative items per thread per tile
+  static_assert(T % W == 0, "tile must split evenly over the waves");
+  constexpr int LW = __builtin_ctz(W);
+  constexpr int NC = W >= 4 ? W / 4 : 1;            // 16-byte chunks per partial row
+  constexpr int LNC = __builtin_ctz(NC);
+  constexpr int WPS = BF16_IN ? 1 : 2;              // packed B/C words per step
+  constexpr uint32_t IN_B = BF16_IN ? 2 : 4, OUT_B = BF16_OUT ? 2 : 4;
+  constexpr bool READOUT = MODE == kFull;
+  constexpr bool SUMMARY = MODE == kSummary;
+
+  // Step sizes live in a ring of 4 tile slots (tile k in slot k & 3): tiles
+  // are prepared two at a time, every other tile. Partial readouts are
+  // double-buffered by tile parity. One barrier per tile separates every
+  // writer from every reader.
+  __shared__ float2 sDD[4][T][64];                  // (dt, dt*u) per step and channel
+  __shared__ __attribute__((aligned(16))) float sP[READOUT ? 2 : 1][T][READOUT ? 64 * W : 1];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Dm = p.dim, N = p.N;
+  const int tiles_d = (Dm + 63) / 64;
+  const int b = blockIdx.x / tiles_d;
+  const int ch = static_cast<int>(blockIdx.x % tiles_d) * 64 + lane;
+  const bool ch_ok = ch < Dm;
+  const int c = blockIdx.y;                         // sequence chunk
+  const int t0 = c * p.chunk;
+  const int len = min(p.L - t0, p.chunk);           // valid steps of this chunk
+  const int nt = min(p.Lp - t0, p.chunk) / T;       // tiles (padded steps / T)
+  // Slot of this wave's partial in the lane's row, and the order in which the
+  // row's 16-byte chunks are read back. Both are XOR swizzles chosen so that
+  // the 4-byte writes and the 16-byte reads hit distinct banks with either
+  // 32 or 64 LDS banks.
+  const int wpos = lane * W + ((w ^ (lane >> (5 - LW)) ^ (lane >> 5)) & (W - 1));
+  const int rswz = ((lane >> (3 - LNC)) ^ (lane >> 3)) & (NC - 1);
+
+  // Recurrence state of this lane: states n = w*S + s of channel ch. A
+  // single pass starts from h0 (or zeros); a chunked scan starts chunk c from
+  // its carried-in state (for chunk 0 a copy of h0, so that h_final may
+  // overwrite h0 while other chunks run); the summary pass from zeros.
+  const int64_t bdn = (static_cast<int64_t>(b) * Dm + ch) * N;
+  const float* hinit = MODE == kSummary ? nullptr
+                               : (p.carry ? p.carry + static_cast<int64_t>(c) * p.batch * Dm * N : p.h0);
+  float A2[S], h[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int n = w * S + s;
+    const bool ok = ch_ok && n < N;
+    A2[s] = ok ? p.A[static_cast<int64_t>(ch) * N + n] * kLog2e : 0.0f;
+    // Pass the loaded initial state through an ALU op here (fma(x, 1, 0) is
+    // not folded: it maps -0 to +0), so the loop never inherits a pending load
+    // on the state registers.
+    h[s] = __builtin_fmaf((ok && hinit) ? hinit[bdn + n] : 0.0f, 1.0f, 0.0f);
+  }
+  // Same ALU pass-through for the per-channel constants.
+  const float Dv = __builtin_fmaf((ch_ok && p.D) ? p.D[ch] : 0.0f, 1.0f, 0.0f);
+  const float bv = __builtin_fmaf((ch_ok && p.bias) ? p.bias[ch] : 0.0f, 1.0f, 0.0f);
+  const bool has_z = READOUT && p.z != nullptr;
+  float dt_sum = 0.0f;
+
+  // Buffer descriptors over this chunk of this batch row's [L, d] planes
+  // (at most 2^30 bytes each). Missing z reads as zeros.
+  const int64_t pb = (static_cast<int64_t>(b) * p.L + t0) * Dm;
+  const uint32_t elems = static_cast<uint32_t>(len) * static_cast<uint32_t>(Dm);
+  const rsrc_t ru_b = raw_buffer(static_cast<const char*>(p.u) + pb * IN_B, elems * IN_B);
+  const rsrc_t rd_b = raw_buffer(static_cast<const char*>(p.delta) + pb * IN_B, elems * IN_B);
+  const rsrc_t rz_b = raw_buffer(has_z ? static_cast<const char*>(p.z) + pb * IN_B : nullptr,
+                                 has_z ? elems * IN_B : 0u);
+  const rsrc_t ry_b = raw_buffer(READOUT ? static_cast<char*>(p.y) + pb * OUT_B : nullptr,
+                                 READOUT ? elems * OUT_B : 0u);
+  const uint32_t lane_in = ch_ok ? static_cast<uint32_t>(ch) * IN_B : kLaneOut;
+  const uint32_t lane_out = ch_ok ? static_cast<uint32_t>(ch) * OUT_B : kLaneOut;
+  // Wave-uniform part of the offset of cooperative item i of tile k: step
+  // k*T + w + W*i of the chunk, times the row pitch; out of range outside it.
+  auto step_off = [&](int k, int i, uint32_t elem) __attribute__((always_inline)) -> uint32_t {
+    const int t = k * T + w + W * i;
+    return static_cast<unsigned>(t) < static_cast<unsigned>(len)
+               ? static_cast<uint32_t>(t) * static_cast<uint32_t>(Dm) * elem
+               : kStepOut;
+  };
+
+  // This wave's packed B/C rows: read-only for the whole kernel (written by
+  // the pre-pass launch), so the constant address space turns these
+  // wave-uniform loads into scalar loads and the values into SGPR operands.
+  const_u32p bcw = (const_u32p)(p.BC) + ((static_cast<int64_t>(b) * NS + w * S) * p.Lp + t0) * WPS;
+  const int64_t Lp = p.Lp;
+
+  // Cooperative items of this thread: step w + W*i of each tile, channel ch.
+  // Raw inputs (storage bits) are fetched two tiles at a time into two
+  // register sets (set = tile parity); D*u and the gate of a tile wait until
+  // its readout, up to three tiles later (four sets, set = tile & 3).
+  storage_t<BF16_IN> ru[2][IT], rd[2][IT], rz[2][IT];
+  float eDu[4][IT], eG[4][IT];
+
+  auto load_raw = [&](int k, auto set) __attribute__((always_inline)) {
+    constexpr int R = decltype(set)::value;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const uint32_t off = lane_in + step_off(k, i, IN_B);
+      ru[R][i] = buffer_load_bits<BF16_IN>(ru_b, off);
+      rd[R][i] = buffer_load_bits<BF16_IN>(rd_b, off);
+      if constexpr (READOUT) rz[R][i] = buffer_load_bits<BF16_IN>(rz_b, off);
+    }
+  };
+  // Step sizes of tile k into its ring slot (and D*u, gate into registers).
+  // Branch-free: padding steps get dt = 0 (exp2(0) = 1 and no input, so the
+  // state is unchanged).
+  auto prepare = [&](int k, auto slot) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;
+    constexpr int R = SL & 1;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int tt = w + W * i;
+      const bool t_ok = k * T + tt < len;          // wave-uniform
+      const float uv = bits_to_f32<BF16_IN>(ru[R][i]);
+      const float x = bits_to_f32<BF16_IN>(rd[R][i]) + bv;
+      float dt = SOFTPLUS ? softplus_f(x) : x;
+      dt = t_ok ? dt : 0.0f;
+      if constexpr (READOUT) {
+        const float g = silu_f(bits_to_f32<BF16_IN>(rz[R][i]));
+        eDu[SL][i] = Dv * uv;
+        eG[SL][i] = has_z ? g : 1.0f;
+      }
+      sDD[SL][tt][lane] = make_float2(dt, dt * uv);
+    }
+  };
+  // Readout of one item of the tile in buffer P: the W partials, fetched
+  // (gather_load) well before they are summed as a fixed tree (gather_sum;
+  // every lane, every run, the same order).
+  constexpr int GN = W >= 4 ? NC : 1;               // 16-byte reads per item
+  constexpr int GW = W >= 4 ? 4 : W;                // floats per read
+  auto gather_load = [&](auto par, int i, float (&g)[GN][GW]) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    const int tt = w + W * i;
+    if constexpr (W >= 4) {
+#pragma unroll
+      for (int q = 0; q < NC; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(&sP[P][tt][lane * W + 4 * (q ^ rswz)]);
+        g[q][0] = v.x;
+        g[q][1] = v.y;
+        g[q][2] = v.z;
+        g[q][3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < W; ++q) g[0][q] = sP[P][tt][lane * W + q];
+    }
+  };
+  auto gather_sum = [&](const float (&g)[GN][GW]) __attribute__((always_inline)) -> float {
+    if constexpr (W >= 4) {
+      float c4[NC];
+#pragma unroll
+      for (int q = 0; q < NC; ++q) c4[q] = (g[q][0] + g[q][1]) + (g[q][2] + g[q][3]);
+#pragma unroll
+      for (int m = 1; m < NC; m <<= 1) {
+#pragma unroll
+        for (int q = 0; q < NC; q += 2 * m) c4[q] += c4[q + m];
+      }
+      return c4[0];
+    } else {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < W; ++q) acc += g[0][q];
+      return acc;
+    }
+  };
+  auto gather_item = [&](auto par, int i) __attribute__((always_inline)) -> float {
+    float g[GN][GW];
+    gather_load(par, i, g);
+    return gather_sum(g);
+  };
+
+  // Packed B/C of the tile being scanned, wave-uniform (SGPRs), one set per
+  // tile parity so the next tile's fetch overlaps this tile's recurrence.
+  uint32_t bc[2][S][T * WPS];
+  auto load_bc = [&](int k, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+#pragma unroll
+      for (int j = 0; j < T * WPS; ++j) bc[P][s][j] = bcw[(s * Lp + static_cast<int64_t>(k) * T) * WPS + j];
+    }
+  };
+
+  // Outputs of one tile are held in registers until the next odd tile, so
+  // no store is in flight between an even tile's input fetch and its use
+  // (stores and loads share one wait counter that may then not be relied on
+  // to count in order, and every wait would drain the whole queue).
+  float yv[2][IT];
+  uint32_t yo[2][IT];
+
+  auto read_dd = [&](float2 (&dd)[T], auto slot) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;
+#pragma unroll
+    for (int t = 0; t < T; ++t) dd[t] = sDD[SL][t][lane];
+  };
+  auto steps = [&](const float2 (&dd)[T], auto par, auto lo, auto hi) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+#pragma unroll
+    for (int t = decltype(lo)::value; t < decltype(hi)::value; ++t) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        float bval, cval;
+        if constexpr (BF16_IN) {
+          bval = __uint_as_float(bc[P][s][t] & 0xffff0000u);
+          cval = __uint_as_float(bc[P][s][t] << 16);
+        } else {
+          bval = __uint_as_float(bc[P][s][2 * t]);
+          cval = __uint_as_float(bc[P][s][2 * t + 1]);
+        }
+        const float abar = exp2_hw(dd[t].x * A2[s]);
+        h[s] = fmaf(abar, h[s], dd[t].y * bval);
+        if constexpr (READOUT) acc = fmaf(cval, h[s], acc);
+      }
+      if constexpr (READOUT) sP[P][t][wpos] = acc;
+      if constexpr (SUMMARY) dt_sum += dd[t].x;
+    }
+  };
+
+  // Tile k with J = k & 3 (P = k & 1). Its step sizes are already in
+  // registers (read during tile k-1) and its B/C in SGPR set P (fetched
+  // during tile k-1). The work of a tile, in the order of the "early" waves:
+  //   (1) scalar fetch of tile k+1's B/C; first half of the recurrence;
+  //   (2) LDS reads of tile k+1's step sizes and tile k-1's partials
+  //       (waited on after the second half, when the scalar fetch is long
+  //       done);
+  //   (3) second half of the recurrence;
+  //   (4) readout of tile k-1 (stored on odd tiles, two tiles at a time); on
+  //       even tiles, preparation of tiles k+2 and k+3 and the fetch of the
+  //       raw inputs of tiles k+4 and k+5.
+  // "Late" waves run (2), (4), (1), (3): the readout and the preparation
+  // first, then the whole recurrence. A wave raises its issue priority while
+  // it runs the recurrence, so the SIMD's arbiter prefers it over the other
+  // wave's cooperative work (which mostly waits on memory and LDS). The two waves that share a SIMD take
+  // different orders, so while one runs the recurrence the other runs the
+  // cooperative work, instead of both waiting on the same phase. Every
+  // dependency is on data written before the previous barrier, so both
+  // orders are valid. One barrier per tile.
+  auto lds_reads = [&](auto jj, float2 (&dd_next)[T], float (&gp)[IT][GN][GW]) __attribute__((always_inline)) {
+    constexpr int J = decltype(jj)::value;
+    constexpr int Q = 1 - (J & 1);
+    read_dd(dd_next, std::integral_constant<int, (J + 1) & 3>{});
+    if constexpr (READOUT) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) gather_load(std::integral_constant<int, Q>{}, i, gp[i]);
+    }
+  };
+  auto coop = [&](int k, auto jj, float (&gp)[IT][GN][GW]) __attribute__((always_inline)) {
+    constexpr int J = decltype(jj)::value;
+    constexpr int P = J & 1;
+    if constexpr (READOUT) {
+      // Readout of tile k-1 (out of range at k = 0: the stores are dropped).
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        yv[P][i] = (gather_sum(gp[i]) + eDu[(J + 3) & 3][i]) * eG[(J + 3) & 3][i];
+        yo[P][i] = lane_out + step_off(k - 1, i, OUT_B);
+      }
+      if constexpr (P == 1) {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+          buffer_store_f32<BF16_OUT>(yv[0][i], ry_b, yo[0][i]);
+          buffer_store_f32<BF16_OUT>(yv[1][i], ry_b, yo[1][i]);
+        }
+      }
+    }
+    if constexpr (P == 0) {
+      prepare(k + 2, std::integral_constant<int, (J + 2) & 3>{});
+      prepare(k + 3, std::integral_constant<int, (J + 3) & 3>{});
+      load_raw(k + 4, std::integral_constant<int, 0>{});
+      load_raw(k + 5, std::integral_constant<int, 1>{});
+    }
+  };
+  auto iter = [&](int k, auto jj, auto late, const float2 (&dd)[T], float2 (&dd_next)[T]) __attribute__((always_inline)) {
+    constexpr int J = decltype(jj)::value;
+    constexpr int P = J & 1;
+    constexpr int Q = 1 - P;
+    float gp[IT][GN][GW];
+    if constexpr (MODE == kCheckpoint) {
+      if (ch_ok) {
+        float* ck = p.hsum + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
+#pragma unroll
+        for (int s = 0; s < S; ++s) ck[static_cast<int64_t>(s) * Dm] = h[s];
+      }
+    }
+    if constexpr (decltype(late)::value) {
+      lds_reads(jj, dd_next, gp);
+      __builtin_amdgcn_sched_barrier(0);
+      coop(k, jj, gp);
+      __builtin_amdgcn_sched_barrier(0);
+      load_bc(k + 1 < nt ? k + 1 : k, std::integral_constant<int, Q>{});  // clamped: stays in SGPRs
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(2);
+      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, 0>{},
+            std::integral_constant<int, T / 2>{});
+      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
+            std::integral_constant<int, T>{});
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      load_bc(k + 1 < nt ? k + 1 : k, std::integral_constant<int, Q>{});  // clamped: stays in SGPRs
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(2);
+      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, 0>{},
+            std::integral_constant<int, T / 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      lds_reads(jj, dd_next, gp);
+      __builtin_amdgcn_sched_barrier(0);
+      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
+            std::integral_constant<int, T>{});
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      coop(k, jj, gp);
+    }
+    __syncthreads();
+  };
+
+  float2 ddA[T], ddB[T];
+  if (nt > 0) {
+    load_raw(0, std::integral_constant<int, 0>{});
+    load_raw(1, std::integral_constant<int, 1>{});
+    load_bc(0, std::integral_constant<int, 0>{});
+    prepare(0, std::integral_constant<int, 0>{});
+    prepare(1, std::integral_constant<int, 1>{});
+    // Retire every load so far (state, A, D, bias, tiles 0-1): the wait
+    // analysis would otherwise carry them into the loop as possibly pending.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    load_raw(2, std::integral_constant<int, 0>{});
+    load_raw(3, std::integral_constant<int, 1>{});
+    if constexpr (READOUT) {
+      // Out-of-range stores (dropped by the buffer unit) in the places of an
+      // odd tile's output stores: loop entry then sees the same queue of
+      // memory operations as the back edge, and the waits of the first tile
+      // need not cover stores.
+#pragma unroll
+      for (int i = 0; i < 2 * IT; ++i) buffer_store_f32<BF16_OUT>(0.0f, ry_b, kLaneOut + 64u * i);
+    }
+    __syncthreads();
+    read_dd(ddA, std::integral_constant<int, 0>{});
+    // As above for the LDS counter: retire the first step-size read here.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) ddA[t].x = __builtin_fmaf(ddA[t].x, 1.0f, 0.0f);
+  }
+  auto run = [&](auto late) __attribute__((always_inline)) {
+    int k = 0;
+    for (; k + 3 < nt; k += 4) {
+      iter(k, std::integral_constant<int, 0>{}, late, ddA, ddB);
+      iter(k + 1, std::integral_constant<int, 1>{}, late, ddB, ddA);
+      iter(k + 2, std::integral_constant<int, 2>{}, late, ddA, ddB);
+      iter(k + 3, std::integral_constant<int, 3>{}, late, ddB, ddA);
+    }
+    if (k < nt) iter(k, std::integral_constant<int, 0>{}, late, ddA, ddB);
+    if (k + 1 < nt) iter(k + 1, std::integral_constant<int, 1>{}, late, ddB, ddA);
+    if (k + 2 < nt) iter(k + 2, std::integral_constant<int, 2>{}, late, ddA, ddB);
+  };
+  // Two orders only where two waves of the block share each SIMD (eight
+  // waves); elsewhere the second copy of the loop would cost registers.
+  if constexpr (W == 8) {
+    if ((w & kLateWaveMask) != 0) {
+      run(std::true_type{});
+    } else {
+      run(std::false_type{});
+    }
+  } else {
+    run(std::false_type{});
+  }
+
+  if constexpr (READOUT) {
+    if (nt > 0) {
+      // Held readout of tile nt-2 (when the last tile was even), then tile nt-1.
+      const int last = nt - 1;
+      if ((last & 1) == 0) {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) buffer_store_f32<BF16_OUT>(yv[0][i], ry_b, yo[0][i]);
+      }
+      float part[IT];
+      if (last & 1) {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) part[i] = gather_item(std::integral_constant<int, 1>{}, i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) part[i] = gather_item(std::integral_constant<int, 0>{}, i);
+      }
+      const int sl = last & 3;
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const float du = sl == 0 ? eDu[0][i] : sl == 1 ? eDu[1][i] : sl == 2 ? eDu[2][i] : eDu[3][i];
+        const float g = sl == 0 ? eG[0][i] : sl == 1 ? eG[1][i] : sl == 2 ? eG[2][i] : eG[3][i];
+        buffer_store_f32<BF16_OUT>((part[i] + du) * g, ry_b, lane_out + step_off(last, i, OUT_B));
+      }
+    }
+    if (p.h_final && ch_ok && c == static_cast<int>(gridDim.y) - 1) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = w * S + s;
+        if (n < N) p.h_final[bdn + n] = h[s];
+      }
+    }
+  } else if constexpr (MODE == kSummary) {
+    if (ch_ok) {
+      const int64_t cb = static_cast<int64_t>(c) * p.batch + b;
+      const int64_t cb1 = cb + p.batch;              // slot c + 1
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = w * S + s;
+        if (n < N) p.hsum[(cb1 * Dm + ch) * N + n] = h[s];
+      }
+      if (w == 0) p.ssum[cb * Dm + ch] = dt_sum;
+    }
+  }
+}
+
+// In-order fold of the chunk summaries with the recurrence's combine rule:
+// the state entering chunk c+1 is exp(A * sum of chunk c's step sizes) times
+// the state entering chunk c, plus chunk c's final state from zero. One
+// thread per (b, d, n). Slot 0 receives the initial state (h0 or zeros);
+// slot c+1, which holds chunk c's summary state, is overwritten in place with
+// the state entering chunk c+1.
+__global__ __launch_bounds__(256) void carry_fold_kernel(const float* __restrict__ A,
+                                                         const float* __restrict__ h0,
+                                                         float* __restrict__ hsum,
+                                                         const float* __restrict__ ssum,
+                                                         int64_t bdn_total, int dim, int N,
+                                                         int folds) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= bdn_total) return;
+  const int n = static_cast<int>(i % N);
+  const int64_t bd = i / N;
+  const int ch = static_cast<int>(bd % dim);
+  const int64_t bd_total = bdn_total / N;
+  const float a2 = A[static_cast<int64_t>(ch) * N + n] * kLog2e;
+  float h = h0 ? h0[i] : 0.0f;
+  hsum[i] = h;
+  for (int c = 0; c < folds; ++c) {
+    const float decay = exp2_hw(a2 * ssum[c * bd_total + bd]);
+    float* slot = hsum + (c + 1) * bdn_total + i;
+    h = fmaf(decay, h, *slot);
+    *slot = h;
+  }
+}
+
+template <int S, int W, int T, bool BI, bool BO, bool SP>
+int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
+  static_assert(kPadSteps % T == 0, "tile must divide the padding");
+  const int64_t blocks = a.batch * pl.dim_blocks;
+  if (blocks > 0x7fffffff || pl.chunks > 65535) return hipErrorInvalidConfiguration;
+  Scan args = s;
+  void* kargs[] = {&args};
+  if (pl.chunks > 1) {
+    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, kSummary>),
+                              dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks - 1)),
+                              dim3(W * 64), kargs, 0, st);
+    if (err != 0) return err;
+    const int64_t bdn = a.batch * a.dim * a.dstate;
+    const float* A = a.A;
+    const float* h0 = a.h0;
+    float* hsum = args.hsum;
+    const float* ssum = args.ssum;
+    int dim = static_cast<int>(a.dim), N = static_cast<int>(a.dstate);
+    int folds = static_cast<int>(pl.chunks - 1);
+    void* fargs[] = {&A, &h0, &hsum, &ssum, const_cast<int64_t*>(&bdn), &dim, &N, &folds};
+    err = hipLaunchKernel(reinterpret_cast<const void*>(&carry_fold_kernel),
+                          dim3(static_cast<unsigned>((bdn + 255) / 256)), dim3(256), fargs, 0, st);
+    if (err != 0) return err;
+  }
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, kFull>),
+                         dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks)),
+                         dim3(W * 64), kargs, 0, st);
+}
+
+// Per padded state count: states per lane S, waves per block W (state
+// groups), tile length T. N = 16 uses two states per lane on eight waves:
+// half the LDS traffic per state update of one state per lane, which the LDS
+// bandwidth (128 bytes per clock per CU) needs more than the extra waves.
+template <bool BI, bool BO, bool SP>
+int launch_ns(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
+  switch (pl.NS) {
+    case 1: return launch_sw<1, 1, 16, BI, BO, SP>(a, pl, s, st);
+    case 2: return launch_sw<1, 2, 16, BI, BO, SP>(a, pl, s, st);
+    case 4: return launch_sw<1, 4, 16, BI, BO, SP>(a, pl, s, st);
+    case 8: return launch_sw<1, 8, 16, BI, BO, SP>(a, pl, s, st);
+    case 16: return launch_sw<2, 8, 8, BI, BO, SP>(a, pl, s, st);
+    case 32: return launch_sw<2, 16, 16, BI, BO, SP>(a, pl, s, st);
+    default: return launch_sw<4, 16, 16, BI, BO, SP>(a, pl, s, st);
+  }
+}
+
+template <bool BI, bool BO>
+int launch_io(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
+  return a.delta_softplus ? launch_ns<BI, BO, true>(a, pl, s, st) : launch_ns<BI, BO, false>(a, pl, s, st);
+}
+
+template <bool BI, bool SP>
+int launch_ckpt_ns(const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_t st) {
+  Scan args = s;
+  void* kargs[] = {&args};
+  const void* fn = nullptr;
+  switch (pl.NS) {
+    case 1: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 1, 16, BI, false, SP, kCheckpoint>); break;
+    case 2: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 2, 16, BI, false, SP, kCheckpoint>); break;
+    case 4: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 4, 16, BI, false, SP, kCheckpoint>); break;
+    case 8: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 8, 16, BI, false, SP, kCheckpoint>); break;
+    case 16: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<2, 8, 8, BI, false, SP, kCheckpoint>); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(pl.W * 64), kargs, 0, st);
+}
+
+}  // namespace
+
+}  // namespace ssm
