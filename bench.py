@@ -292,6 +292,47 @@ BWD_SLOTS_PER_UPDATE = 16
 BWD_SLOTS_PER_BLD = 20
 
 
+# Exact zero-order hold: the input coefficient k = (exp(dt*A) - 1) / A costs,
+# per state update, k itself [1: fma(Abar, 1/A, -1/A)] and one more product
+# (u*B, then k*(u*B), in place of (dt*u)*B); dt*u per (b,l,d) is no longer
+# needed. The series branch near dt*A = 0 that keeps k accurate there (3 ops,
+# a compare and a select) is counted as implementation overhead, not here.
+ZOH_SLOTS_PER_UPDATE = SLOTS_PER_UPDATE + 2
+ZOH_SLOTS_PER_BLD = SLOTS_PER_BLD - 1
+
+
+def bench_zoh(args, torch, binding, synth, inp):
+    """The scan of the 1.4B-shaped layer with the exact zero-order-hold option."""
+    import numpy as np
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dt = inp["in_dtype"]
+
+    def up(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t = {k: up(inp[k], dt) for k in ("u", "delta", "B", "C", "z")}
+    for k in ("A", "D", "delta_bias"):
+        t[k] = up(inp[k], "f32")
+    out_dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    y = torch.empty(w.batch, w.seqlen, w.dim, dtype=out_dtype, device=dev)
+    hf = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
+    fn = lambda: binding.ssm_selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"],  # noqa
+                                                z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True,
+                                                y=y, h_final=hf if w.final_state else None,
+                                                out_dtype=out_dtype, zoh=True)
+    us = _timed(torch, fn, args.zoh_steps, 20)
+    ups = w.updates
+    slots = ups * ZOH_SLOTS_PER_UPDATE + w.batch * w.seqlen * w.dim * ZOH_SLOTS_PER_BLD
+    ach = slots / (us * 1e-6) / 1e12
+    return {"workload": f"{w.name}, exact zero-order hold", "us_per_call": us,
+            "G_updates_per_s": ups / (us * 1e-6) / 1e9,
+            "roofline": {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_SLOTS / 1e12, "unit": "Tslot/s",
+                         "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
+
+
 def bench_bwd(args, torch, binding, synth, inp):
     """Backward of the selective scan on the 1.4B-shaped layer (float32 dy)."""
     import numpy as np
@@ -337,6 +378,8 @@ def main():
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--no-zoh", action="store_true")
+    ap.add_argument("--zoh-steps", type=int, default=50)
     ap.add_argument("--conv-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=8192)
@@ -402,6 +445,8 @@ def main():
     }
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, binding, synth)
+    if not args.no_zoh:
+        result["scan_zoh"] = bench_zoh(args, torch, binding, synth, inp)
     if not args.no_bwd:
         result["scan_bwd"] = bench_bwd(args, torch, binding, synth, inp)
     if not args.no_conv:

@@ -6,7 +6,9 @@
  * time step l (of `seqlen`):
  *
  *   dt      = softplus(delta[b,l,d] + delta_bias[d])   (or no softplus)
- *   h[n]    = exp(dt * A[d,n]) * h[n] + dt * B[b,l,n] * u[b,l,d]
+ *   h[n]    = exp(dt * A[d,n]) * h[n] + k * B[b,l,n] * u[b,l,d]
+ *   k       = dt (default), or (exp(dt * A[d,n]) - 1) / A[d,n] (exact
+ *             zero-order hold; k = dt where A[d,n] = 0)
  *   y[b,l,d] = (sum_n C[b,l,n] * h[n] + D[d] * u[b,l,d]) * silu(z[b,l,d])
  *
  * Sources (page title and section; the same pages throughout this library):
@@ -22,6 +24,9 @@
  *   - "Mamba架构：突破Transformer瓶颈的序列建模新范式" (intelliparadigm.com),
  *     section 6.2: very long sequences are processed in chunks with the state
  *     carried from chunk to chunk (h0 in, h_final out).
+ *   - "Mamba新突破：SSM架构挑战注意力机制，引领推理新范式" (ruibaoantu.com),
+ *     section 二.3: the continuous system is discretised by a zero-order hold,
+ *     whose input coefficient for a diagonal A is the closed form above.
  *
  * Readings where the pages disagree: the transition is exp(dt * A) with A <= 0
  * passed in directly (not A_log, and no extra minus sign); the input term is
@@ -68,6 +73,11 @@ extern "C" {
 #define SSM_E_UNSUPPORTED 7 /* dstate, seqlen or dim beyond the supported range  */
 #define SSM_E_HIP 8         /* the HIP runtime reported an error at launch       */
 
+/* Bits of the `flags` argument of the scan and decode entry points. Any other
+ * bit set returns SSM_E_UNSUPPORTED. */
+#define SSM_FLAG_SOFTPLUS 1 /* dt = softplus(delta + delta_bias), else delta + delta_bias */
+#define SSM_FLAG_ZOH 2      /* input coefficient k = (exp(dt A) - 1) / A, else k = dt   */
+
 /* Version of this ABI (SSM_ABI_VERSION of the header the library was built from). */
 int ssm_abi_version(void);
 
@@ -108,7 +118,7 @@ int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
  *   batch, seqlen, dim, dstate : B >= 0, 0 <= L < 2^30, 0 <= d < 2^24,
  *                                1 <= N <= 64 (else SSM_E_UNSUPPORTED).
  *   in_dtype, out_dtype        : 0 float32, 1 bfloat16.
- *   delta_softplus             : nonzero -> dt = softplus(delta + bias).
+ *   flags                      : SSM_FLAG_SOFTPLUS and/or SSM_FLAG_ZOH.
  *   u, delta  [B, L, d]  in_dtype   input and raw step size
  *   A         [d, N]     float32    diagonal state matrix (expected <= 0)
  *   B, C      [B, L, N]  in_dtype   input and output projections
@@ -128,7 +138,7 @@ int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
  * floating-point data). NaN/Inf propagate without clamping.
  */
 int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                           int in_dtype, int out_dtype, int delta_softplus,
+                           int in_dtype, int out_dtype, int flags,
                            const void* u, const void* delta, const float* A,
                            const void* B, const void* C, const float* D, const void* z,
                            const float* delta_bias, const float* h0,
@@ -141,6 +151,7 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
  * for L = 1 with h0 = state and h_final = state:
  *
  *   batch, dim, dstate         : B >= 0, d >= 0, 1 <= N <= 256.
+ *   flags                      : SSM_FLAG_SOFTPLUS and/or SSM_FLAG_ZOH.
  *   state     [B, d, N]  float32    read, then overwritten with the new state
  *   x, delta  [B, d]     in_dtype   token input and raw step size
  *   A         [d, N]     float32
@@ -152,7 +163,7 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
  *   stream                          hipStream_t
  */
 int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
-                               int in_dtype, int out_dtype, int delta_softplus,
+                               int in_dtype, int out_dtype, int flags,
                                float* state, const void* x, const void* delta,
                                const float* A, const void* B, const void* C,
                                const float* D, const void* z, const float* delta_bias,
@@ -182,8 +193,10 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *
  *   batch, seqlen, dim, dstate : as the forward, with 1 <= N <= 16 (else
  *                                SSM_E_UNSUPPORTED).
- *   in_dtype, delta_softplus, u, delta, A, B, C, D, z, delta_bias, h0 : the
- *                                forward's inputs (same layouts and rules).
+ *   in_dtype, flags, u, delta, A, B, C, D, z, delta_bias, h0 : the
+ *                                forward's inputs (same layouts and rules);
+ *                                SSM_FLAG_ZOH returns SSM_E_UNSUPPORTED (the
+ *                                gradients are those of k = dt).
  *   dy        [B, L, d]  float32    gradient of the loss w.r.t. y
  *   dh_final  [B, d, N]  float32    gradient w.r.t. h_final (optional, 0)
  *   du, ddelta [B, L, d] float32    outputs (ddelta w.r.t. the raw delta)
@@ -198,7 +211,7 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  * in a fixed order; no floating-point atomics).
  */
 int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                           int in_dtype, int delta_softplus,
+                           int in_dtype, int flags,
                            const void* u, const void* delta, const float* A,
                            const void* B, const void* C, const float* D, const void* z,
                            const float* delta_bias, const float* h0,

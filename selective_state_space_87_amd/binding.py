@@ -123,6 +123,14 @@ def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate) -> int:
     return int(_load().ssm_scan_workspace_bytes(batch, seqlen, dim, dstate))
 
 
+FLAG_SOFTPLUS = 1   # SSM_FLAG_SOFTPLUS
+FLAG_ZOH = 2        # SSM_FLAG_ZOH
+
+
+def _flags(delta_softplus, zoh):
+    return (FLAG_SOFTPLUS if delta_softplus else 0) | (FLAG_ZOH if zoh else 0)
+
+
 def ssm_scan_chunks(batch, seqlen, dim, dstate) -> int:
     """Sequence chunks the scan of this shape runs in (1 = single pass, 0 = unsupported)."""
     return int(_load().ssm_scan_chunks(batch, seqlen, dim, dstate))
@@ -131,11 +139,12 @@ def ssm_scan_chunks(batch, seqlen, dim, dstate) -> int:
 def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                            delta_softplus=False, h0=None, out_dtype=None,
                            return_final_state=False, y=None, h_final=None,
-                           workspace=None, stream=None):
+                           workspace=None, stream=None, zoh=False):
     """Selective scan forward; see ssm_selective_scan_fwd in include/ssm_scan.h.
 
     u, delta, z: [B, L, d]; B, C: [B, L, N] (all float32 or all bfloat16);
     A: [d, N], D, delta_bias: [d], h0: [B, d, N] (float32).
+    ``zoh`` selects the exact zero-order-hold input coefficient (SSM_FLAG_ZOH).
     Returns y ([B, L, d], ``out_dtype`` or the input dtype) or (y, h_final).
     """
     lib = _load()
@@ -178,7 +187,7 @@ def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         ws_size = 0
     with torch.cuda.device(dev):
         st = lib.ssm_selective_scan_fwd(
-            Bt, L, d, N, _DTYPE_CODE[u.dtype], _DTYPE_CODE[out_dtype], int(bool(delta_softplus)),
+            Bt, L, d, N, _DTYPE_CODE[u.dtype], _DTYPE_CODE[out_dtype], _flags(delta_softplus, zoh),
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), ws_size, _stream_handle(stream, dev))
     _check("ssm_selective_scan_fwd", st)
@@ -188,12 +197,12 @@ def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
 
 
 def ssm_selective_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
-                               delta_softplus=False, out_dtype=None, y=None, stream=None):
+                               delta_softplus=False, out_dtype=None, y=None, stream=None, zoh=False):
     """One decode step in place on ``state``; see ssm_selective_state_update in include/ssm_scan.h.
 
     state: [B, d, N] float32 (updated in place); x, delta, z: [B, d]; B, C: [B, N]
     (all float32 or all bfloat16); A: [d, N], D, delta_bias: [d] float32.
-    Returns y [B, d].
+    ``zoh`` as in ssm_selective_scan_fwd. Returns y [B, d].
     """
     lib = _load()
     if not isinstance(state, torch.Tensor) or state.dim() != 3:
@@ -220,7 +229,7 @@ def ssm_selective_state_update(state, x, delta, A, B, C, D=None, z=None, delta_b
     _dev_tensor("y", y, (Bt, d), (out_dtype,), dev)
     with torch.cuda.device(dev):
         st = lib.ssm_selective_state_update(
-            Bt, d, N, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype], int(bool(delta_softplus)),
+            Bt, d, N, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype], _flags(delta_softplus, zoh),
             _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), _ptr(y), _stream_handle(stream, dev))
     _check("ssm_selective_state_update", st)
@@ -350,7 +359,7 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=Non
     ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
         st = lib.ssm_selective_scan_bwd(
-            Bt, L, d, N, _DTYPE_CODE[u.dtype], int(bool(delta_softplus)),
+            Bt, L, d, N, _DTYPE_CODE[u.dtype], _flags(delta_softplus, False),
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0),
             _ptr(dy), _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
             _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g["dh0"]),

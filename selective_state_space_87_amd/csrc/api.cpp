@@ -80,7 +80,7 @@ int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
 }
 
 int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                           int in_dtype, int out_dtype, int delta_softplus,
+                           int in_dtype, int out_dtype, int flags,
                            const void* u, const void* delta, const float* A,
                            const void* B, const void* C, const float* D, const void* z,
                            const float* delta_bias, const float* h0,
@@ -89,6 +89,7 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
   if (dstate > kMaxScanState) return SSM_E_UNSUPPORTED;
   if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return SSM_E_DTYPE;
+  if ((flags & ~(SSM_FLAG_SOFTPLUS | SSM_FLAG_ZOH)) != 0) return SSM_E_UNSUPPORTED;
   int64_t bl, bld, bln, bdn, dn;
   if (!safe_mul(batch, seqlen, &bl) || !safe_mul(bl, dim, &bld) || !safe_mul(bl, dstate, &bln) ||
       !safe_mul(batch, dim, &bdn) || !safe_mul(bdn, dstate, &bdn) || !safe_mul(dim, dstate, &dn)) {
@@ -152,12 +153,13 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   a.dstate = dstate;
   a.in_bf16 = in_dtype;
   a.out_bf16 = out_dtype;
-  a.delta_softplus = delta_softplus ? 1 : 0;
+  a.delta_softplus = (flags & SSM_FLAG_SOFTPLUS) != 0;
+  a.zoh = (flags & SSM_FLAG_ZOH) != 0;
   return map_hip(ssm::launch_scan(a, stream));
 }
 
 int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
-                               int in_dtype, int out_dtype, int delta_softplus,
+                               int in_dtype, int out_dtype, int flags,
                                float* state, const void* x, const void* delta,
                                const float* A, const void* B, const void* C,
                                const float* D, const void* z, const float* delta_bias,
@@ -165,6 +167,7 @@ int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
   if (batch < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
   if (dstate > kMaxDecodeState) return SSM_E_UNSUPPORTED;
   if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return SSM_E_DTYPE;
+  if ((flags & ~(SSM_FLAG_SOFTPLUS | SSM_FLAG_ZOH)) != 0) return SSM_E_UNSUPPORTED;
   int64_t bd, bdn, bn, dn;
   if (!safe_mul(batch, dim, &bd) || !safe_mul(bd, dstate, &bdn) || !safe_mul(batch, dstate, &bn) ||
       !safe_mul(dim, dstate, &dn)) {
@@ -210,7 +213,8 @@ int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
   a.dstate = dstate;
   a.in_bf16 = in_dtype;
   a.out_bf16 = out_dtype;
-  a.delta_softplus = delta_softplus ? 1 : 0;
+  a.delta_softplus = (flags & SSM_FLAG_SOFTPLUS) != 0;
+  a.zoh = (flags & SSM_FLAG_ZOH) != 0;
   return map_hip(ssm::launch_state_update(a, stream));
 }
 
@@ -223,7 +227,7 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
 }
 
 int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                           int in_dtype, int delta_softplus,
+                           int in_dtype, int flags,
                            const void* u, const void* delta, const float* A,
                            const void* B, const void* C, const float* D, const void* z,
                            const float* delta_bias, const float* h0,
@@ -233,6 +237,8 @@ int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
   if (in_dtype != 0 && in_dtype != 1) return SSM_E_DTYPE;
+  if ((flags & ~(SSM_FLAG_SOFTPLUS | SSM_FLAG_ZOH)) != 0) return SSM_E_UNSUPPORTED;
+  if (flags & SSM_FLAG_ZOH) return SSM_E_UNSUPPORTED;  // gradients of the simplified form only
   int64_t bl, bld, bln, bdn, dn, bldn;
   if (!safe_mul(batch, seqlen, &bl) || !safe_mul(bl, dim, &bld) || !safe_mul(bl, dstate, &bln) ||
       !safe_mul(batch, dim, &bdn) || !safe_mul(bdn, dstate, &bdn) || !safe_mul(dim, dstate, &dn) ||
@@ -302,7 +308,7 @@ int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   a.dim = dim;
   a.dstate = dstate;
   a.in_bf16 = in_dtype;
-  a.delta_softplus = delta_softplus ? 1 : 0;
+  a.delta_softplus = (flags & SSM_FLAG_SOFTPLUS) != 0;
   return map_hip(ssm::launch_scan_bwd(a, stream));
 }
 

@@ -31,6 +31,23 @@ __device__ __forceinline__ float softplus_f(float x) {
   return fmaxf(x, 0.0f) + lp;
 }
 
+// 1/a (correctly rounded), or 0 for a = 0.
+__device__ __forceinline__ float inv_or_zero(float a) { return a != 0.0f ? 1.0f / a : 0.0f; }
+
+// Input coefficient of the exact zero-order hold over one step of size dt,
+// k = (e^(dt a) - 1) / a (the integral of e^(a s) over [0, dt]; k = dt at
+// a = 0), given x2 = dt a log2(e), abar = 2^x2 and ia = 1/a (0 where a = 0).
+// Away from x = 0, k = (abar - 1) ia, whose relative error is a few
+// ulp(abar) / |x|: of order 2^-17 at |x| = ln(2)/64, smaller beyond. Closer to 0 (and at
+// a = 0) the difference cancels, and k = dt (1 + x/2 + x^2/6) is used, the
+// series of expm1(x)/x, whose first dropped term x^3/24 is below 2^-24 there.
+__device__ __forceinline__ float zoh_coef(float dt, float x2, float abar, float ia) {
+  constexpr float c1 = 0.5f * kLn2, c2 = kLn2 * kLn2 / 6.0f;  // x = x2 ln 2
+  const float ks = fmaf(dt * x2, fmaf(x2, c2, c1), dt);
+  const float kb = fmaf(abar, ia, -ia);
+  return fabsf(x2) < 0x1p-6f ? ks : kb;
+}
+
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).
 __device__ __forceinline__ float silu_f(float z) {
   return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));

@@ -21,7 +21,7 @@ struct ScanArgs {
   float* h_final;
   void* workspace;
   int64_t batch, seqlen, dim, dstate;
-  int in_bf16, out_bf16, delta_softplus;
+  int in_bf16, out_bf16, delta_softplus, zoh;
 };
 
 struct UpdateArgs {
@@ -36,7 +36,7 @@ struct UpdateArgs {
   const float* delta_bias;
   void* y;
   int64_t batch, dim, dstate;
-  int in_bf16, out_bf16, delta_softplus;
+  int in_bf16, out_bf16, delta_softplus, zoh;
 };
 
 struct ScanBwdArgs {

@@ -92,7 +92,7 @@ constexpr int kLateWaveMask = 4;
 // (for the backward pass, which recomputes each tile from them).
 constexpr int kFull = 0, kSummary = 1, kCheckpoint = 2;
 
-template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, int MODE>
+template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool ZOH, int MODE>
 __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int NS = S * W;        // padded state count
   constexpr int IT = T / W;        // cooperative items per thread per tile
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // are prepared two at a time, every other tile. Partial readouts are
   // double-buffered by tile parity. One barrier per tile separates every
   // writer from every reader.
-  __shared__ float2 sDD[4][T][64];                  // (dt, dt*u) per step and channel
+  __shared__ float2 sDD[4][T][64];                  // (dt, dt*u), or (dt, u) with ZOH
   __shared__ __attribute__((aligned(16))) float sP[READOUT ? 2 : 1][T][READOUT ? 64 * W : 1];
 
   const int lane = threadIdx.x & 63;
@@ -138,11 +138,14 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   const float* hinit = MODE == kSummary ? nullptr
                                : (p.carry ? p.carry + static_cast<int64_t>(c) * p.batch * Dm * N : p.h0);
   float A2[S], h[S];
+  float iA[ZOH ? S : 1];                            // 1/A (0 where A = 0), ZOH only
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int n = w * S + s;
     const bool ok = ch_ok && n < N;
-    A2[s] = ok ? p.A[static_cast<int64_t>(ch) * N + n] * kLog2e : 0.0f;
+    const float av = ok ? p.A[static_cast<int64_t>(ch) * N + n] : 0.0f;
+    A2[s] = av * kLog2e;
+    if constexpr (ZOH) iA[s] = inv_or_zero(av);
     // Pass the loaded initial state through an ALU op here (fma(x, 1, 0) is
     // not folded: it maps -0 to +0), so the loop never inherits a pending load
     // on the state registers.
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
         eDu[SL][i] = Dv * uv;
         eG[SL][i] = has_z ? g : 1.0f;
       }
-      sDD[SL][tt][lane] = make_float2(dt, dt * uv);
+      sDD[SL][tt][lane] = make_float2(dt, ZOH ? uv : dt * uv);
     }
   };
   // Readout of one item of the tile in buffer P: the W partials, fetched
@@ -305,8 +308,11 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
           bval = __uint_as_float(bc[P][s][2 * t]);
           cval = __uint_as_float(bc[P][s][2 * t + 1]);
         }
-        const float abar = exp2_hw(dd[t].x * A2[s]);
-        h[s] = fmaf(abar, h[s], dd[t].y * bval);
+        const float x2 = dd[t].x * A2[s];
+        const float abar = exp2_hw(x2);
+        float bu = dd[t].y * bval;                  // dt*u*B, or u*B with ZOH
+        if constexpr (ZOH) bu *= zoh_coef(dd[t].x, x2, abar, iA[s]);
+        h[s] = fmaf(abar, h[s], bu);
         if constexpr (READOUT) acc = fmaf(cval, h[s], acc);
       }
       if constexpr (READOUT) sP[P][t][wpos] = acc;
@@ -537,7 +543,7 @@ __global__ __launch_bounds__(256) void carry_fold_kernel(const float* __restrict
   }
 }
 
-template <int S, int W, int T, bool BI, bool BO, bool SP>
+template <int S, int W, int T, bool BI, bool BO, bool SP, bool ZH>
 int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
   static_assert(kPadSteps % T == 0, "tile must divide the padding");
   const int64_t blocks = a.batch * pl.dim_blocks;
@@ -545,7 +551,7 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
   Scan args = s;
   void* kargs[] = {&args};
   if (pl.chunks > 1) {
-    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, kSummary>),
+    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kSummary>),
                               dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks - 1)),
                               dim3(W * 64), kargs, 0, st);
     if (err != 0) return err;
@@ -561,7 +567,7 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
                           dim3(static_cast<unsigned>((bdn + 255) / 256)), dim3(256), fargs, 0, st);
     if (err != 0) return err;
   }
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, kFull>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull>),
                          dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks)),
                          dim3(W * 64), kargs, 0, st);
 }
@@ -570,22 +576,25 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
 // groups), tile length T. N = 16 uses two states per lane on eight waves:
 // half the LDS traffic per state update of one state per lane, which the LDS
 // bandwidth (128 bytes per clock per CU) needs more than the extra waves.
-template <bool BI, bool BO, bool SP>
+template <bool BI, bool BO, bool SP, bool ZH>
 int launch_ns(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
   switch (pl.NS) {
-    case 1: return launch_sw<1, 1, 16, BI, BO, SP>(a, pl, s, st);
-    case 2: return launch_sw<1, 2, 16, BI, BO, SP>(a, pl, s, st);
-    case 4: return launch_sw<1, 4, 16, BI, BO, SP>(a, pl, s, st);
-    case 8: return launch_sw<1, 8, 16, BI, BO, SP>(a, pl, s, st);
-    case 16: return launch_sw<2, 8, 8, BI, BO, SP>(a, pl, s, st);
-    case 32: return launch_sw<2, 16, 16, BI, BO, SP>(a, pl, s, st);
-    default: return launch_sw<4, 16, 16, BI, BO, SP>(a, pl, s, st);
+    case 1: return launch_sw<1, 1, 16, BI, BO, SP, ZH>(a, pl, s, st);
+    case 2: return launch_sw<1, 2, 16, BI, BO, SP, ZH>(a, pl, s, st);
+    case 4: return launch_sw<1, 4, 16, BI, BO, SP, ZH>(a, pl, s, st);
+    case 8: return launch_sw<1, 8, 16, BI, BO, SP, ZH>(a, pl, s, st);
+    case 16: return launch_sw<2, 8, 8, BI, BO, SP, ZH>(a, pl, s, st);
+    case 32: return launch_sw<2, 16, 16, BI, BO, SP, ZH>(a, pl, s, st);
+    default: return launch_sw<4, 16, 16, BI, BO, SP, ZH>(a, pl, s, st);
   }
 }
 
 template <bool BI, bool BO>
 int launch_io(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
-  return a.delta_softplus ? launch_ns<BI, BO, true>(a, pl, s, st) : launch_ns<BI, BO, false>(a, pl, s, st);
+  if (a.zoh) return a.delta_softplus ? launch_ns<BI, BO, true, true>(a, pl, s, st)
+                                     : launch_ns<BI, BO, false, true>(a, pl, s, st);
+  return a.delta_softplus ? launch_ns<BI, BO, true, false>(a, pl, s, st)
+                          : launch_ns<BI, BO, false, false>(a, pl, s, st);
 }
 
 template <bool BI, bool SP>
@@ -594,11 +603,11 @@ int launch_ckpt_ns(const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_
   void* kargs[] = {&args};
   const void* fn = nullptr;
   switch (pl.NS) {
-    case 1: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 1, 16, BI, false, SP, kCheckpoint>); break;
-    case 2: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 2, 16, BI, false, SP, kCheckpoint>); break;
-    case 4: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 4, 16, BI, false, SP, kCheckpoint>); break;
-    case 8: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 8, 16, BI, false, SP, kCheckpoint>); break;
-    case 16: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<2, 8, 8, BI, false, SP, kCheckpoint>); break;
+    case 1: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 1, 16, BI, false, SP, false, kCheckpoint>); break;
+    case 2: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 2, 16, BI, false, SP, false, kCheckpoint>); break;
+    case 4: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 4, 16, BI, false, SP, false, kCheckpoint>); break;
+    case 8: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 8, 16, BI, false, SP, false, kCheckpoint>); break;
+    case 16: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<2, 8, 8, BI, false, SP, false, kCheckpoint>); break;
     default: return hipErrorInvalidValue;
   }
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(pl.W * 64), kargs, 0, st);

@@ -3,8 +3,10 @@
 // Per (b, d, n) ("从 Transformer 到 Mamba", ybb.press, section 6.3: fixed work
 // per token, old state and token in, new state out; the step is the scan's
 // step of section 5 for a single token):
-//   dt = softplus(delta + bias);  s[n] = exp(dt*A[n]) s[n] + dt*B[n]*x
+//   dt = softplus(delta + bias);  s[n] = exp(dt*A[n]) s[n] + k*B[n]*x
 //   y  = (sum_n C[n] s[n] + D x) * silu(z)
+// with k = dt, or the exact zero-order-hold coefficient (exp(dt*A[n]) - 1) /
+// A[n] ("Mamba新突破", ruibaoantu.com, section 二.3) when ZOH is set.
 //
 // The state [B, d, N] float32 is read once and written once: the kernel is a
 // streaming read-modify-write bound by HBM. A row (b, d) is owned by R lanes
@@ -25,7 +27,7 @@ constexpr int kThreads = 256;
 constexpr int kWideV = 16;  // states per lane when N allows
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int V, int R, bool BF16_IN, bool BF16_OUT>
+template <int V, int R, bool BF16_IN, bool BF16_OUT, bool ZOH>
 __global__ __launch_bounds__(kThreads) void state_update_kernel(const UpdateArgs a) {
   constexpr int RPB = kThreads / R;  // rows per block
   const int tid = threadIdx.x;
@@ -81,8 +83,11 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(const UpdateArgs
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float abar = exp2_hw(dt * (av[q][v] * kLog2e));
-          s[q][v] = fmaf(abar, s[q][v], du * bv[v]);
+          const float x2 = dt * (av[q][v] * kLog2e);
+          const float abar = exp2_hw(x2);
+          float bu = du * bv[v];
+          if constexpr (ZOH) bu = x * bv[v] * zoh_coef(dt, x2, abar, inv_or_zero(av[q][v]));
+          s[q][v] = fmaf(abar, s[q][v], bu);
           acc = fmaf(cv[v], s[q][v], acc);
         }
       }
@@ -93,8 +98,12 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(const UpdateArgs
     for (int64_t n0 = j; n0 < N; n0 += R) {
       if (!ok) continue;
       float* sp = a.state + row * N + n0;
-      const float abar = exp2_hw(dt * (a.A[ch * N + n0] * kLog2e));
-      const float s = fmaf(abar, *sp, du * load_elem<BF16_IN>(a.B, b * N + n0));
+      const float an = a.A[ch * N + n0];
+      const float x2 = dt * (an * kLog2e);
+      const float abar = exp2_hw(x2);
+      const float bn = load_elem<BF16_IN>(a.B, b * N + n0);
+      const float bu = ZOH ? x * bn * zoh_coef(dt, x2, abar, inv_or_zero(an)) : du * bn;
+      const float s = fmaf(abar, *sp, bu);
       *sp = s;
       acc = fmaf(load_elem<BF16_IN>(a.C, b * N + n0), s, acc);
     }
@@ -109,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(const UpdateArgs
   }
 }
 
-template <int V, int R, bool BI, bool BO>
+template <int V, int R, bool BI, bool BO, bool ZH>
 int launch_vr(const UpdateArgs& a, hipStream_t st) {
   constexpr int RPB = kThreads / R;
   const int64_t rows = a.batch * a.dim;
@@ -117,35 +126,35 @@ int launch_vr(const UpdateArgs& a, hipStream_t st) {
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   UpdateArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&state_update_kernel<V, R, BI, BO>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&state_update_kernel<V, R, BI, BO, ZH>),
                          dim3(static_cast<unsigned>(blocks)), dim3(kThreads), kargs, 0, st);
 }
 
 // Lanes per row: enough to cover N with V states each, a power of two <= 64
 // (the wide paths need N == R * V exactly; the scalar path loops).
-template <int V, bool BI, bool BO>
+template <int V, bool BI, bool BO, bool ZH>
 int launch_v(const UpdateArgs& a, hipStream_t st) {
   const int64_t need = (a.dstate + V - 1) / V;
-  if (need <= 1) return launch_vr<V, 1, BI, BO>(a, st);
-  if (need <= 2) return launch_vr<V, 2, BI, BO>(a, st);
-  if (need <= 4) return launch_vr<V, 4, BI, BO>(a, st);
-  if (need <= 8) return launch_vr<V, 8, BI, BO>(a, st);
-  if (need <= 16) return launch_vr<V, 16, BI, BO>(a, st);
-  if (need <= 32) return launch_vr<V, 32, BI, BO>(a, st);
-  return launch_vr<V, 64, BI, BO>(a, st);
+  if (need <= 1) return launch_vr<V, 1, BI, BO, ZH>(a, st);
+  if (need <= 2) return launch_vr<V, 2, BI, BO, ZH>(a, st);
+  if (need <= 4) return launch_vr<V, 4, BI, BO, ZH>(a, st);
+  if (need <= 8) return launch_vr<V, 8, BI, BO, ZH>(a, st);
+  if (need <= 16) return launch_vr<V, 16, BI, BO, ZH>(a, st);
+  if (need <= 32) return launch_vr<V, 32, BI, BO, ZH>(a, st);
+  return launch_vr<V, 64, BI, BO, ZH>(a, st);
 }
 
 // 16-byte state/A/B/C accesses need N % V == 0 and 16-byte aligned bases
 // (B and C: 16-byte aligned by the ABI; their rows then stay aligned when
 // N * element size is a multiple of 16).
-template <bool BI, bool BO>
+template <bool BI, bool BO, bool ZH>
 int launch_io(const UpdateArgs& a, hipStream_t st) {
   const bool base16 = reinterpret_cast<uintptr_t>(a.state) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(a.A) % 16 == 0;
   const bool pow2 = (a.dstate & (a.dstate - 1)) == 0;
-  if (base16 && pow2 && a.dstate >= kWideV && a.dstate / kWideV <= 64) return launch_v<kWideV, BI, BO>(a, st);
-  if (base16 && pow2 && a.dstate >= 4 && a.dstate / 4 <= 64) return launch_v<4, BI, BO>(a, st);
-  return launch_v<1, BI, BO>(a, st);
+  if (base16 && pow2 && a.dstate >= kWideV && a.dstate / kWideV <= 64) return launch_v<kWideV, BI, BO, ZH>(a, st);
+  if (base16 && pow2 && a.dstate >= 4 && a.dstate / 4 <= 64) return launch_v<4, BI, BO, ZH>(a, st);
+  return launch_v<1, BI, BO, ZH>(a, st);
 }
 
 }  // namespace
@@ -153,10 +162,12 @@ int launch_io(const UpdateArgs& a, hipStream_t st) {
 int launch_state_update(const UpdateArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.batch == 0 || a.dim == 0) return 0;
-  if (a.in_bf16) {
-    return a.out_bf16 ? launch_io<true, true>(a, st) : launch_io<true, false>(a, st);
+  if (a.zoh) {
+    if (a.in_bf16) return a.out_bf16 ? launch_io<true, true, true>(a, st) : launch_io<true, false, true>(a, st);
+    return a.out_bf16 ? launch_io<false, true, true>(a, st) : launch_io<false, false, true>(a, st);
   }
-  return a.out_bf16 ? launch_io<false, true>(a, st) : launch_io<false, false>(a, st);
+  if (a.in_bf16) return a.out_bf16 ? launch_io<true, true, false>(a, st) : launch_io<true, false, false>(a, st);
+  return a.out_bf16 ? launch_io<false, true, false>(a, st) : launch_io<false, false, false>(a, st);
 }
 
 }  // namespace ssm

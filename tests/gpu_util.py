@@ -52,16 +52,16 @@ def scan_inputs_to_device(inp):
 
 
 def run_scan(dev, inp, out_dtype="f32", h0=None, return_final_state=True, use_D=True, use_z=True,
-             use_bias=True, softplus=None):
+             use_bias=True, softplus=None, zoh=False):
     sp = inp["delta_softplus"] if softplus is None else softplus
     return binding.ssm_selective_scan_fwd(
         dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"],
         D=dev["D"] if use_D else None, z=dev["z"] if use_z else None,
         delta_bias=dev["delta_bias"] if use_bias else None, delta_softplus=sp, h0=h0,
-        out_dtype=torch_dtype(out_dtype), return_final_state=return_final_state)
+        out_dtype=torch_dtype(out_dtype), return_final_state=return_final_state, zoh=zoh)
 
 
-def oracle_scan(inp, channels=None, h0=None, use_D=True, use_z=True, use_bias=True, softplus=None):
+def oracle_scan(inp, channels=None, h0=None, use_D=True, use_z=True, use_bias=True, softplus=None, zoh=False):
     """Oracle on the exact device values; optionally only on a subset of channels."""
     f = synth.as_float64(inp)
     sl = slice(None) if channels is None else np.asarray(channels)
@@ -72,4 +72,4 @@ def oracle_scan(inp, channels=None, h0=None, use_D=True, use_z=True, use_bias=Tr
     return oracle.selective_scan(u, f["delta"][:, :, sl], f["A"][sl], f["B"], f["C"],
                                  D=f["D"][sl] if use_D else None, z=z,
                                  delta_bias=f["delta_bias"][sl] if use_bias else None,
-                                 delta_softplus=sp, h0=h0s, want_magnitude=True)
+                                 delta_softplus=sp, h0=h0s, want_magnitude=True, zoh=zoh)

@@ -219,3 +219,20 @@ def test_scan_bwd_validation(lib):
     assert bwd(lib, d=0) == OK
     need = lib.ssm_scan_bwd_workspace_bytes(2, 8, 4, 4)
     assert need > 0 and lib.ssm_scan_bwd_workspace_bytes(1, 8, 4, 17) == 0
+
+
+def test_flag_bits(lib):
+    """SSM_FLAG_SOFTPLUS and SSM_FLAG_ZOH are the only flag bits; the
+    backward takes softplus only (its gradients are those of k = dt)."""
+    soft, zoh = header_define("SSM_FLAG_SOFTPLUS"), header_define("SSM_FLAG_ZOH")
+    assert (soft, zoh) == (binding.FLAG_SOFTPLUS, binding.FLAG_ZOH) == (1, 2)
+    for bad in (4, 8, 1 << 30, -1):
+        assert scan(lib, sp=bad) == E_UNSUPPORTED
+        assert upd(lib, sp=bad) == E_UNSUPPORTED
+        assert bwd(lib, sp=bad) == E_UNSUPPORTED
+    assert bwd(lib, sp=zoh) == E_UNSUPPORTED
+    assert bwd(lib, sp=soft | zoh) == E_UNSUPPORTED
+    # the valid bits pass validation (these calls then stop at a later check)
+    assert scan(lib, sp=soft | zoh, u=None) == E_NULLPTR
+    assert upd(lib, sp=zoh, state=None) == E_NULLPTR
+    assert bwd(lib, sp=soft, dy=None) == E_NULLPTR
