@@ -333,6 +333,37 @@ def bench_zoh(args, torch, binding, synth, inp):
                          "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
 
 
+def bench_large_state(args, torch, binding, synth):
+    """The scan at N = 128 (B and C staged through LDS), on the 1.4B layer's
+    width with a shorter sequence: (4, 2048, 4096, 128), bf16 in and out."""
+    import numpy as np
+    B, L, d, N = 4, 2048, 4096, 128
+    inp = synth.make_scan_inputs(B, L, d, N, "bf16", seed=0, stream=4200)
+    dev = torch.device("cuda:0")
+
+    def up(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t = {k: up(inp[k], "bf16") for k in ("u", "delta", "B", "C", "z")}
+    for k in ("A", "D", "delta_bias"):
+        t[k] = up(inp[k], "f32")
+    y = torch.empty(B, L, d, dtype=torch.bfloat16, device=dev)
+    hf = torch.empty(B, d, N, dtype=torch.float32, device=dev)
+    fn = lambda: binding.ssm_selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"],  # noqa
+                                                z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True,
+                                                y=y, h_final=hf, out_dtype=torch.bfloat16)
+    us = _timed(torch, fn, args.large_state_steps, 10)
+    ups = B * L * d * N
+    slots = ups * SLOTS_PER_UPDATE + B * L * d * SLOTS_PER_BLD
+    ach = slots / (us * 1e-6) / 1e12
+    return {"workload": f"scan, N=128 (batch={B}, seqlen={L}, d_inner={d}, bf16 in/out, h_final)",
+            "us_per_call": us, "G_updates_per_s": ups / (us * 1e-6) / 1e9,
+            "roofline": {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_SLOTS / 1e12, "unit": "Tslot/s",
+                         "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
+
+
 def bench_bwd(args, torch, binding, synth, inp):
     """Backward of the selective scan on the 1.4B-shaped layer (float32 dy)."""
     import numpy as np
@@ -379,6 +410,8 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--no-zoh", action="store_true")
+    ap.add_argument("--no-large-state", action="store_true")
+    ap.add_argument("--large-state-steps", type=int, default=20)
     ap.add_argument("--zoh-steps", type=int, default=50)
     ap.add_argument("--conv-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -447,6 +480,8 @@ def main():
         result["decode"] = bench_decode(args, torch, binding, synth)
     if not args.no_zoh:
         result["scan_zoh"] = bench_zoh(args, torch, binding, synth, inp)
+    if not args.no_large_state:
+        result["scan_n128"] = bench_large_state(args, torch, binding, synth)
     if not args.no_bwd:
         result["scan_bwd"] = bench_bwd(args, torch, binding, synth, inp)
     if not args.no_conv:

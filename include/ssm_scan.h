@@ -104,8 +104,8 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  * Number of sequence chunks the scan of this shape runs in (1: one pass over
  * the whole sequence; 0: invalid or unsupported sizes). Chunking is chosen
  * when the batch has too few 64-channel blocks to occupy the device
- * (B * ceil(d / 64) <= 128 with L >= 2048), or when one batch row's [L, d]
- * plane exceeds 2^30 bytes at 4 bytes per element. Results of a chunked and a
+ * (N <= 32, B * ceil(d / 64) <= 128 and L >= 2048), or when one batch row's
+ * [L, d] plane exceeds 2^30 bytes at 4 bytes per element. Results of a chunked and a
  * single-pass scan agree to rounding; each is deterministic.
  */
 int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
@@ -116,7 +116,7 @@ int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
  * MambaBlock; h0/h_final per intelliparadigm.com section 6.2).
  *
  *   batch, seqlen, dim, dstate : B >= 0, 0 <= L < 2^30, 0 <= d < 2^24,
- *                                1 <= N <= 64 (else SSM_E_UNSUPPORTED).
+ *                                1 <= N <= 128 (else SSM_E_UNSUPPORTED).
  *   in_dtype, out_dtype        : 0 float32, 1 bfloat16.
  *   flags                      : SSM_FLAG_SOFTPLUS and/or SSM_FLAG_ZOH.
  *   u, delta  [B, L, d]  in_dtype   input and raw step size

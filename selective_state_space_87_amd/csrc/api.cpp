@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int64_t kMaxScanState = 64;
+constexpr int64_t kMaxScanState = ssm::kMaxScanStates;
 constexpr int64_t kMaxDecodeState = 256;
 constexpr int64_t kMaxElems = int64_t(1) << 52;
 constexpr int64_t kMaxConvWidth = 8;

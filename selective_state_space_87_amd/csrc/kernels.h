@@ -116,6 +116,8 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 // partials of dB and dC [blocks_d][B][Lp][NS], per-batch partials of dA
 // [B][d][N], dD and the bias gradient [B][d].
 constexpr int64_t kBwdMaxState = 16;
+// Largest state size of the scan (padded to a power of two: 128).
+constexpr int64_t kMaxScanStates = 128;
 struct ScanBwdPlan {
   bool ok;
   int NS, W, S;

@@ -20,13 +20,14 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   ScanPlan p{};
-  p.ok = batch >= 0 && seqlen >= 0 && dim >= 0 && dstate >= 1 && dstate <= 64 &&
+  p.ok = batch >= 0 && seqlen >= 0 && dim >= 0 && dstate >= 1 && dstate <= kMaxScanStates &&
          seqlen < (int64_t(1) << 30) && dim < (int64_t(1) << 24);
   if (!p.ok) return p;
-  // States: N padded to a power of two; N = 16 runs two states per lane on
-  // eight waves, other sizes one wave per state up to sixteen waves.
+  // States: N padded to a power of two; one wave per state up to N = 8;
+  // N = 16 two states per lane on eight waves, N = 32 two on sixteen, and
+  // from 64 on NS / 8 states per lane on eight waves (B/C staged in LDS).
   p.NS = ceil_pow2(dstate);
-  p.W = p.NS < 16 ? p.NS : (p.NS == 16 ? 8 : 16);
+  p.W = p.NS < 16 ? p.NS : (p.NS == 16 || p.NS >= 64 ? 8 : 16);
   p.S = p.NS / p.W;
   p.Lp = round_up(seqlen, kPadSteps);
   p.dim_blocks = ceil_div(dim, 64);
@@ -35,7 +36,10 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   if (batch > 0 && dim > 0 && p.Lp > 0) {
     const int64_t blocks = batch * p.dim_blocks;
     int64_t k = 1;
-    if (blocks <= kChunkWhenBlocksAtMost && p.Lp >= 2 * kChunkMinSteps) {
+    // (From 64 padded states on, a block already holds 8x the work of the
+    // N = 16 shape and its summary pass spills registers: such scans are
+    // chunked only when the plane size below requires it.)
+    if (p.NS < 64 && blocks <= kChunkWhenBlocksAtMost && p.Lp >= 2 * kChunkMinSteps) {
       k = kBlockSlots / blocks;
       if (p.Lp / kChunkMinSteps < k) k = p.Lp / kChunkMinSteps;
       if (k < 1) k = 1;
@@ -54,10 +58,11 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
     p.chunks = ceil_div(p.Lp, p.chunk);
   }
   // Workspace: packed B/C (one word per (b, n, step) for bfloat16 inputs,
-  // two for float32; sized for float32), then the chunk summaries.
+  // two for float32; sized for float32; none from 64 padded states on, where
+  // the kernel reads B and C as given), then the chunk summaries.
   size_t off = 0;
   p.off_bc = off;
-  if (batch > 0 && dim > 0 && p.Lp > 0) off += align256(size_t(2 * batch * p.NS * p.Lp) * 4);
+  if (batch > 0 && dim > 0 && p.Lp > 0 && p.NS < 64) off += align256(size_t(2 * batch * p.NS * p.Lp) * 4);
   p.off_hsum = off;
   if (p.chunks > 1) off += align256(size_t(p.chunks * batch * dim * dstate) * 4);
   p.off_ssum = off;

@@ -50,7 +50,10 @@ int launch_scan(const ScanArgs& a, void* stream) {
   s.bias = a.delta_bias;
   s.h0 = a.h0;
   s.carry = pl.chunks > 1 ? reinterpret_cast<const float*>(ws + pl.off_hsum) : nullptr;
-  s.BC = reinterpret_cast<const uint32_t*>(ws + pl.off_bc);
+  const bool bcl = bc_in_lds(pl.NS);
+  s.BC = bcl ? nullptr : reinterpret_cast<const uint32_t*>(ws + pl.off_bc);
+  s.Bm = a.B;
+  s.Cm = a.C;
   s.y = a.y;
   s.h_final = a.h_final;
   s.hsum = pl.chunks > 1 ? reinterpret_cast<float*>(ws + pl.off_hsum) : nullptr;
@@ -61,9 +64,11 @@ int launch_scan(const ScanArgs& a, void* stream) {
   s.N = static_cast<int>(a.dstate);
   s.chunk = static_cast<int>(pl.chunk);
   s.batch = static_cast<int>(a.batch);
-  const int err = launch_bc_pack(a.B, a.C, reinterpret_cast<uint32_t*>(ws + pl.off_bc), a.batch, a.seqlen,
-                                 pl.Lp, static_cast<int>(a.dstate), pl.NS, a.in_bf16 != 0, st);
-  if (err != 0) return err;
+  if (!bcl) {
+    const int err = launch_bc_pack(a.B, a.C, reinterpret_cast<uint32_t*>(ws + pl.off_bc), a.batch, a.seqlen,
+                                   pl.Lp, static_cast<int>(a.dstate), pl.NS, a.in_bf16 != 0, st);
+    if (err != 0) return err;
+  }
   if (a.in_bf16) return a.out_bf16 ? launch_scan_bb(a, pl, s, st) : launch_scan_bf(a, pl, s, st);
   return a.out_bf16 ? launch_scan_fb(a, pl, s, st) : launch_scan_ff(a, pl, s, st);
 }

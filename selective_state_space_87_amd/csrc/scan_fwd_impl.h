@@ -44,7 +44,9 @@ struct Scan {
   const float* bias;
   const float* h0;     // initial state [B, d, N] of a single-pass scan, or null (zeros)
   const float* carry;  // chunked: chunk c starts from carry[c] ([chunks][B][d][N])
-  const uint32_t* BC;  // packed B/C (see bc_pack_kernel)
+  const uint32_t* BC;  // packed B/C (see bc_pack_kernel); null when staged through LDS
+  const void* Bm;      // B and C as given, [B, L, N] (read directly when staged through LDS)
+  const void* Cm;
   void* y;
   float* h_final;
   float* hsum;         // summary pass: chunk c's final state from zero into slot c + 1;
@@ -85,6 +87,11 @@ constexpr uint32_t kStepOut = 0x40000000u;
 // Waves whose index has this bit set take the "late" tile order (see iter).
 constexpr int kLateWaveMask = 4;
 
+// From 64 padded states on, a wave's B/C words for two tiles no longer fit
+// in scalar registers: such shapes stage B and C through LDS instead (and
+// need no packing pre-pass).
+constexpr bool bc_in_lds(int NS) { return NS >= 64; }
+
 // MODE kFull: the scan of one chunk (or of the whole sequence), with readout,
 // gate and store. kSummary: the chunk's recurrence from a zero state only,
 // exporting its final state and the sum of its step sizes. kCheckpoint: the
@@ -104,6 +111,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr uint32_t IN_B = BF16_IN ? 2 : 4, OUT_B = BF16_OUT ? 2 : 4;
   constexpr bool READOUT = MODE == kFull;
   constexpr bool SUMMARY = MODE == kSummary;
+  constexpr bool BCL = bc_in_lds(NS);
+  constexpr int NT = W * 64;                        // threads
+  constexpr int EB = BCL ? (T * NS + NT - 1) / NT : 1;  // B/C elements per thread per tile
 
   // Step sizes live in a ring of 4 tile slots (tile k in slot k & 3): tiles
   // are prepared two at a time, every other tile. Partial readouts are
@@ -111,6 +121,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // writer from every reader.
   __shared__ float2 sDD[4][T][64];                  // (dt, dt*u), or (dt, u) with ZOH
   __shared__ __attribute__((aligned(16))) float sP[READOUT ? 2 : 1][T][READOUT ? 64 * W : 1];
+  // LDS-staged B/C: (B, C) per step and state, a ring of 4 tile slots like
+  // the step sizes. Every lane of a wave reads the same entry (a broadcast).
+  __shared__ __attribute__((aligned(16))) float2 sBC[BCL ? 4 : 1][BCL ? T : 1][BCL ? NS : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -157,6 +170,28 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   const bool has_z = READOUT && p.z != nullptr;
   float dt_sum = 0.0f;
 
+  // LDS-staged B/C: thread element j of a tile is e = tid + j*NT of the
+  // tile's T*N contiguous entries of B (and of C), i.e. step e / N, state
+  // e % N. States N..NS-1 are never written: zero them once (no other
+  // writer touches them, so no ordering is needed beyond the first barrier).
+  int bc_dst[EB];
+  uint32_t bc_src[EB];
+  if constexpr (BCL) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int e = tid + j * NT;
+      const bool ok = e < T * N;
+      bc_dst[j] = ok ? (e / N) * NS + (e % N) : -1;
+      bc_src[j] = ok ? static_cast<uint32_t>(e) * IN_B : kLaneOut;
+    }
+    if (N < NS) {
+      for (int e = tid; e < 4 * T * NS; e += NT) {
+        if (e % NS >= N) (&sBC[0][0][0])[e] = make_float2(0.0f, 0.0f);
+      }
+    }
+  }
+
   // Buffer descriptors over this chunk of this batch row's [L, d] planes
   // (at most 2^30 bytes each). Missing z reads as zeros.
   const int64_t pb = (static_cast<int64_t>(b) * p.L + t0) * Dm;
@@ -181,7 +216,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // This wave's packed B/C rows: read-only for the whole kernel (written by
   // the pre-pass launch), so the constant address space turns these
   // wave-uniform loads into scalar loads and the values into SGPR operands.
-  const_u32p bcw = (const_u32p)(p.BC) + ((static_cast<int64_t>(b) * NS + w * S) * p.Lp + t0) * WPS;
+  const_u32p bcw = BCL ? nullptr : (const_u32p)(p.BC) + ((static_cast<int64_t>(b) * NS + w * S) * p.Lp + t0) * WPS;
   const int64_t Lp = p.Lp;
 
   // Cooperative items of this thread: step w + W*i of each tile, channel ch.
@@ -189,6 +224,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // register sets (set = tile parity); D*u and the gate of a tile wait until
   // its readout, up to three tiles later (four sets, set = tile & 3).
   storage_t<BF16_IN> ru[2][IT], rd[2][IT], rz[2][IT];
+  storage_t<BF16_IN> rbB[BCL ? 2 : 1][EB], rbC[BCL ? 2 : 1][EB];
   float eDu[4][IT], eG[4][IT];
 
   auto load_raw = [&](int k, auto set) __attribute__((always_inline)) {
@@ -199,6 +235,21 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       ru[R][i] = buffer_load_bits<BF16_IN>(ru_b, off);
       rd[R][i] = buffer_load_bits<BF16_IN>(rd_b, off);
       if constexpr (READOUT) rz[R][i] = buffer_load_bits<BF16_IN>(rz_b, off);
+    }
+    if constexpr (BCL) {
+      // Tile k's rows of B and C: T*N contiguous elements from step t0 + k*T,
+      // fewer (down to none) past the chunk's end, where the reads give 0.
+      const int first = k * T;
+      const int rows = max(0, min(T, len - first));
+      const int64_t eo = ((static_cast<int64_t>(b) * p.L + t0 + first) * N) * IN_B;
+      const uint32_t nb = static_cast<uint32_t>(rows * N) * IN_B;
+      const rsrc_t rbb = raw_buffer(static_cast<const char*>(p.Bm) + eo, nb);
+      const rsrc_t rcb = raw_buffer(static_cast<const char*>(p.Cm) + eo, nb);
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        rbB[R][j] = buffer_load_bits<BF16_IN>(rbb, bc_src[j]);
+        rbC[R][j] = buffer_load_bits<BF16_IN>(rcb, bc_src[j]);
+      }
     }
   };
   // Step sizes of tile k into its ring slot (and D*u, gate into registers).
@@ -221,6 +272,15 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
         eG[SL][i] = has_z ? g : 1.0f;
       }
       sDD[SL][tt][lane] = make_float2(dt, ZOH ? uv : dt * uv);
+    }
+    if constexpr (BCL) {
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        if (bc_dst[j] >= 0) {
+          (&sBC[SL][0][0])[bc_dst[j]] =
+              make_float2(bits_to_f32<BF16_IN>(rbB[R][j]), bits_to_f32<BF16_IN>(rbC[R][j]));
+        }
+      }
     }
   };
   // Readout of one item of the tile in buffer P: the W partials, fetched
@@ -271,13 +331,15 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
 
   // Packed B/C of the tile being scanned, wave-uniform (SGPRs), one set per
   // tile parity so the next tile's fetch overlaps this tile's recurrence.
-  uint32_t bc[2][S][T * WPS];
+  uint32_t bc[BCL ? 1 : 2][BCL ? 1 : S][BCL ? 1 : T * WPS];
   auto load_bc = [&](int k, auto par) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
+    if constexpr (!BCL) {
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
+      for (int s = 0; s < S; ++s) {
 #pragma unroll
-      for (int j = 0; j < T * WPS; ++j) bc[P][s][j] = bcw[(s * Lp + static_cast<int64_t>(k) * T) * WPS + j];
+        for (int j = 0; j < T * WPS; ++j) bc[P][s][j] = bcw[(s * Lp + static_cast<int64_t>(k) * T) * WPS + j];
+      }
     }
   };
 
@@ -293,15 +355,21 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
 #pragma unroll
     for (int t = 0; t < T; ++t) dd[t] = sDD[SL][t][lane];
   };
-  auto steps = [&](const float2 (&dd)[T], auto par, auto lo, auto hi) __attribute__((always_inline)) {
-    constexpr int P = decltype(par)::value;
+  auto steps = [&](const float2 (&dd)[T], auto jj, auto lo, auto hi) __attribute__((always_inline)) {
+    constexpr int J = decltype(jj)::value;
+    constexpr int P = J & 1;
 #pragma unroll
     for (int t = decltype(lo)::value; t < decltype(hi)::value; ++t) {
       float acc = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         float bval, cval;
-        if constexpr (BF16_IN) {
+        if constexpr (BCL) {
+          // two states' (B, C) per 16-byte broadcast read
+          const float4 v = *reinterpret_cast<const float4*>(&sBC[J][t][w * S + (s & ~1)]);
+          bval = (s & 1) ? v.z : v.x;
+          cval = (s & 1) ? v.w : v.y;
+        } else if constexpr (BF16_IN) {
           bval = __uint_as_float(bc[P][s][t] & 0xffff0000u);
           cval = __uint_as_float(bc[P][s][t] << 16);
         } else {
@@ -394,9 +462,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(2);
-      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, 0>{},
+      steps(dd, jj, std::integral_constant<int, 0>{},
             std::integral_constant<int, T / 2>{});
-      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
+      steps(dd, jj, std::integral_constant<int, T / 2>{},
             std::integral_constant<int, T>{});
       __builtin_amdgcn_s_setprio(0);
     } else {
@@ -404,12 +472,12 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(2);
-      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, 0>{},
+      steps(dd, jj, std::integral_constant<int, 0>{},
             std::integral_constant<int, T / 2>{});
       __builtin_amdgcn_sched_barrier(0);
       lds_reads(jj, dd_next, gp);
       __builtin_amdgcn_sched_barrier(0);
-      steps(dd, std::integral_constant<int, P>{}, std::integral_constant<int, T / 2>{},
+      steps(dd, jj, std::integral_constant<int, T / 2>{},
             std::integral_constant<int, T>{});
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
@@ -585,7 +653,9 @@ int launch_ns(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
     case 8: return launch_sw<1, 8, 16, BI, BO, SP, ZH>(a, pl, s, st);
     case 16: return launch_sw<2, 8, 8, BI, BO, SP, ZH>(a, pl, s, st);
     case 32: return launch_sw<2, 16, 16, BI, BO, SP, ZH>(a, pl, s, st);
-    default: return launch_sw<4, 16, 16, BI, BO, SP, ZH>(a, pl, s, st);
+    case 64: return launch_sw<8, 8, 8, BI, BO, SP, ZH>(a, pl, s, st);   // B/C through LDS
+    case 128: return launch_sw<16, 8, 8, BI, BO, SP, ZH>(a, pl, s, st);  // B/C through LDS
+    default: return hipErrorInvalidValue;
   }
 }
 

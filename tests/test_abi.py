@@ -74,7 +74,7 @@ def test_scan_validation(lib):
     assert scan(lib, B=-1) == E_SHAPE
     assert scan(lib, L=-1) == E_SHAPE
     assert scan(lib, N=0) == E_SHAPE
-    assert scan(lib, N=65) == E_UNSUPPORTED
+    assert scan(lib, N=129) == E_UNSUPPORTED
     assert scan(lib, ind=2) == E_DTYPE
     assert scan(lib, outd=-1) == E_DTYPE
     assert scan(lib, B=1 << 40, L=1 << 20, d=1 << 10) == E_SHAPE
@@ -112,7 +112,7 @@ def test_state_update_validation(lib):
 
 def test_workspace_query(lib):
     assert lib.ssm_scan_workspace_bytes(-1, 8, 4, 4) == 0
-    assert lib.ssm_scan_workspace_bytes(1, 8, 4, 65) == 0
+    assert lib.ssm_scan_workspace_bytes(1, 8, 4, 129) == 0
     need = lib.ssm_scan_workspace_bytes(1, 262144, 2560, 16)
     if need:
         assert scan(lib, B=1, L=262144, d=2560, N=16, ws=None, wsb=0) == E_WORKSPACE
@@ -123,7 +123,7 @@ def test_size_limits(lib):
     assert scan(lib, B=1, L=1 << 30, d=4) == E_UNSUPPORTED
     assert scan(lib, B=1, L=8, d=1 << 24) == E_UNSUPPORTED
     assert lib.ssm_scan_chunks(1, 1 << 30, 4, 4) == 0
-    assert lib.ssm_scan_chunks(1, 8, 4, 65) == 0
+    assert lib.ssm_scan_chunks(1, 8, 4, 129) == 0
 
 
 def test_chunk_plan(lib):

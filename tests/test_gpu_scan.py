@@ -97,6 +97,35 @@ def test_shapes(B, L, d, N, dt):
     check_scan(f"shape {(B, L, d, N)} {dt}", inp, "bf16")
 
 
+# From 64 padded states on, B and C are staged through LDS (no packing
+# pre-pass); N = 128 runs sixteen states per lane.
+LARGE_N = [
+    (2, 100, 70, 128, "bf16"), (1, 67, 64, 128, "f32"), (1, 200, 130, 100, "f32"), (3, 40, 33, 65, "bf16"),
+    (1, 129, 200, 64, "f32"), (2, 31, 64, 64, "bf16"), (1, 1, 1, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,L,d,N,dt", LARGE_N)
+def test_large_state(B, L, d, N, dt):
+    inp = synth.make_scan_inputs(B, L, d, N, dt, seed=4, stream=4000 + N)
+    h0 = np.random.default_rng(N + 1).standard_normal((B, d, N)).astype(np.float32) * 0.5
+    check_scan(f"large N {(B, L, d, N)} {dt}", inp, "f32", h0=h0)
+    check_scan(f"large N {(B, L, d, N)} {dt}", inp, "bf16")
+
+
+def test_large_state_chunked_by_plane_size():
+    """N = 128 is chunked only when a batch row's plane passes 2^30 bytes
+    (here 65,600 x 4,096 x 4 bytes): the summary pass and the carry fold."""
+    B, L, d, N = 1, 65600, 4096, 128
+    assert binding.ssm_scan_chunks(1, 4100, 64, N) == 1
+    k = binding.ssm_scan_chunks(B, L, d, N)
+    assert k > 1
+    inp = synth.make_scan_inputs(B, L, d, N, "bf16", seed=5, stream=4500)
+    ch = np.r_[0, 1, 63, 64, 2047, 4095]
+    h0 = np.random.default_rng(45).standard_normal((B, d, N)).astype(np.float32) * 0.5
+    check_scan(f"large N chunked x{k} {(B, L, d, N)} bf16 sampled", inp, "f32", h0=h0, channels=ch)
+
+
 @pytest.mark.parametrize("opts", [
     dict(use_D=False), dict(use_z=False), dict(use_bias=False), dict(softplus=False, use_bias=False),
     dict(use_D=False, use_z=False, use_bias=False),
@@ -230,7 +259,7 @@ def test_guard_bands_and_full_coverage():
 
 CHUNKED = [
     (1, 4096, 64, 16, "f32"), (2, 5000, 100, 16, "bf16"), (1, 3000, 64, 3, "f32"),
-    (1, 2100, 130, 33, "bf16"), (1, 2048, 1, 1, "f32"), (3, 6000, 40, 8, "bf16"),
+    (1, 2100, 130, 32, "bf16"), (1, 2048, 1, 1, "f32"), (3, 6000, 40, 8, "bf16"),
 ]
 
 
