@@ -20,6 +20,7 @@ Sources, cited by tag throughout:
 
 from .conv_oracle import causal_conv1d, causal_conv1d_update  # noqa: F401
 from .scan_bwd_oracle import selective_scan_bwd  # noqa: F401
+from .ssd_oracle import ssd_quadratic, ssd_recurrent  # noqa: F401
 from .ssm_oracle import (  # noqa: F401
     softplus,
     silu,
