@@ -271,6 +271,51 @@ int ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width,
                              float* state, const void* x, const float* weight, const float* bias,
                              void* y, void* stream);
 
+/*
+ * Mamba-2 SSD layer, forward ("Mamba的隐藏代价", kongchang.com, section on the
+ * value and limits of the argument: the selective SSM recast as a structured
+ * state-space duality, y = M o (Q K^T) V with M lower triangular and
+ * semiseparable, Q from C and K from B, computed with matrix products;
+ * "从 Transformer 到 Mamba", ybb.press, section 9.1: diagonal state matrix).
+ * One scalar decay per head, B and C shared by all heads. Per batch b, step t,
+ * head h, head channel p, state n:
+ *
+ *   dt      = softplus(dt_raw[b,t,h] + dt_bias[h])     (or without softplus)
+ *   H[n,p]  = exp(dt * A[h]) * H[n,p] + dt * B[b,t,n] * x[b,t,h,p]
+ *   y[b,t,h,p] = (sum_n C[b,t,n] * H[n,p] + D[h] * x[b,t,h,p]) * silu(z[b,t,h,p])
+ *
+ * which is the selective scan above with d = H * P channels, A[h*P+p, n] =
+ * A[h] for every n and delta[b,t,h*P+p] = dt_raw[b,t,h]. It is computed in
+ * chunks of 64 steps as dense products on the matrix cores (see the source).
+ *
+ *   batch, seqlen, nheads, headdim, dstate : B >= 0, L >= 0, H >= 0,
+ *                                1 <= P <= 64, 1 <= N <= 128 (else
+ *                                SSM_E_UNSUPPORTED); B * H < 2^31.
+ *   in_dtype, out_dtype        : 0 float32, 1 bfloat16.
+ *   flags                      : SSM_FLAG_SOFTPLUS or 0 (SSM_FLAG_ZOH and any
+ *                                other bit: SSM_E_UNSUPPORTED).
+ *   x         [B, L, H, P]  in_dtype   input
+ *   dt        [B, L, H]     in_dtype   raw step size per head
+ *   A         [H]           float32    decay per head (expected <= 0)
+ *   B, C      [B, L, N]     in_dtype   input and output projections
+ *   D         [H]           float32    skip per head (optional)
+ *   z         [B, L, H, P]  in_dtype   gate branch (optional)
+ *   dt_bias   [H]           float32    step-size bias (optional)
+ *   h0        [B, H, P, N]  float32    initial state (optional)
+ *   y         [B, L, H, P]  out_dtype  output; must not overlap any input
+ *   h_final   [B, H, P, N]  float32    final state (optional); may equal h0
+ *   stream                             hipStream_t
+ *
+ * Alignment and NULL rules as for the scan (x, dt, B, C, z, y 16-byte
+ * aligned). No workspace. L = 0 writes h_final = h0 (or zeros). Bitwise
+ * deterministic.
+ */
+int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                int in_dtype, int out_dtype, int flags,
+                const void* x, const void* dt, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* dt_bias, const float* h0,
+                void* y, float* h_final, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,5 +16,6 @@ from .binding import (  # noqa: F401
     ssm_selective_scan_bwd,
     ssm_selective_scan_fwd,
     ssm_selective_state_update,
+    ssm_ssd_fwd,
     SSMError,
 )

@@ -72,6 +72,8 @@ def _load():
         lib.ssm_causal_conv1d_update.restype = i32
         lib.ssm_causal_conv1d_update.argtypes = [i64, i64, i64, i32, i32, i32,
                                                  vp, vp, vp, vp, vp, vp]
+        lib.ssm_ssd_fwd.restype = i32
+        lib.ssm_ssd_fwd.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32] + [vp] * 11 + [vp]
         _lib = lib
         return lib
 
@@ -366,3 +368,50 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=Non
             _ptr(workspace), ws_size, _stream_handle(stream, dev))
     _check("ssm_selective_scan_bwd", st)
     return g
+
+
+def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False, h0=None, out_dtype=None,
+                return_final_state=False, y=None, h_final=None, stream=None):
+    """Mamba-2 SSD layer forward; see ssm_ssd_fwd in include/ssm_scan.h.
+
+    x, z: [B, L, H, P]; dt: [B, L, H]; B, C: [B, L, N] (all float32 or all
+    bfloat16); A, D, dt_bias: [H] float32; h0: [B, H, P, N] float32.
+    Returns y ([B, L, H, P]) or (y, h_final).
+    """
+    lib = _load()
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("x must be a 4-d tensor [B, L, H, P]")
+    if x.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported input dtype {x.dtype}")
+    dev = x.device
+    Bt, L, H, P = x.shape
+    if not isinstance(B, torch.Tensor) or B.dim() != 3:
+        raise ValueError("B must be a 3-d tensor [B, L, N]")
+    N = B.shape[2]
+    ind = (x.dtype,)
+    _dev_tensor("x", x, (Bt, L, H, P), ind, dev)
+    _dev_tensor("dt", dt, (Bt, L, H), ind, dev)
+    _dev_tensor("A", A, (H,), (torch.float32,), dev)
+    _dev_tensor("B", B, (Bt, L, N), ind, dev)
+    _dev_tensor("C", C, (Bt, L, N), ind, dev)
+    _dev_tensor("D", D, (H,), (torch.float32,), dev)
+    _dev_tensor("z", z, (Bt, L, H, P), ind, dev)
+    _dev_tensor("dt_bias", dt_bias, (H,), (torch.float32,), dev)
+    _dev_tensor("h0", h0, (Bt, H, P, N), (torch.float32,), dev)
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    if y is None:
+        y = torch.empty((Bt, L, H, P), dtype=out_dtype, device=dev)
+    _dev_tensor("y", y, (Bt, L, H, P), (out_dtype,), dev)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
+    _dev_tensor("h_final", h_final, (Bt, H, P, N), (torch.float32,), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssm_ssd_fwd(Bt, L, H, P, N, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype],
+                             _flags(dt_softplus, False), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                             _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _stream_handle(stream, dev))
+    _check("ssm_ssd_fwd", st)
+    if return_final_state or h_final is not None:
+        return y, h_final
+    return y

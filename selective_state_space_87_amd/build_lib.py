@@ -30,7 +30,7 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", os.path.jo
 CXX = os.environ.get("CXX_HOST", "g++")
 
 DEVICE_SOURCES = ["scan_fwd.hip", "scan_fwd_bb.hip", "scan_fwd_bf.hip", "scan_fwd_fb.hip", "scan_fwd_ff.hip",
-                  "scan_bwd.hip", "state_update.hip", "conv1d.hip"]
+                  "scan_bwd.hip", "state_update.hip", "conv1d.hip", "ssd.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 

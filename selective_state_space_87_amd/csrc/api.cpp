@@ -402,4 +402,72 @@ int ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width,
   return map_hip(ssm::launch_conv1d_update(a, stream));
 }
 
+int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                int in_dtype, int out_dtype, int flags,
+                const void* x, const void* dt, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* dt_bias, const float* h0,
+                void* y, float* h_final, void* stream) {
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 1 || dstate < 1) return SSM_E_SHAPE;
+  if (headdim > ssm::kSsdMaxHeadDim || dstate > ssm::kSsdMaxState) return SSM_E_UNSUPPORTED;
+  if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return SSM_E_DTYPE;
+  if ((flags & ~SSM_FLAG_SOFTPLUS) != 0) return SSM_E_UNSUPPORTED;  // no zero-order-hold option here
+  int64_t bl, blh, blhp, bln, bh, bhpn;
+  if (!safe_mul(batch, seqlen, &bl) || !safe_mul(bl, nheads, &blh) || !safe_mul(blh, headdim, &blhp) ||
+      !safe_mul(bl, dstate, &bln) || !safe_mul(batch, nheads, &bh) || !safe_mul(bh, headdim, &bhpn) ||
+      !safe_mul(bhpn, dstate, &bhpn)) {
+    return SSM_E_SHAPE;
+  }
+  if (bh > 0x7fffffff) return SSM_E_UNSUPPORTED;
+  if (bh == 0) return SSM_OK;  // no head: nothing to compute or write
+  if (A == nullptr) return SSM_E_NULLPTR;
+  if (seqlen > 0 && (x == nullptr || dt == nullptr || B == nullptr || C == nullptr || y == nullptr)) {
+    return SSM_E_NULLPTR;
+  }
+  const void* vec_ptrs[] = {x, dt, B, C, z, y};
+  for (const void* q : vec_ptrs) {
+    if (q && !aligned(q, 16)) return SSM_E_ALIGN;
+  }
+  const void* f32_ptrs[] = {A, D, dt_bias, h0, h_final};
+  for (const void* q : f32_ptrs) {
+    if (q && !aligned(q, 4)) return SSM_E_ALIGN;
+  }
+  const int64_t isz = in_dtype == 1 ? 2 : 4, osz = out_dtype == 1 ? 2 : 4;
+  const Range ry = span(y, seqlen > 0 ? blhp : 0, osz);
+  const Range rhf = span(h_final, bhpn, 4);
+  const Range rh0 = span(h0, bhpn, 4);
+  const Range inputs[] = {span(x, blhp, isz), span(dt, blh, isz), span(z, blhp, isz), span(B, bln, isz),
+                          span(C, bln, isz), span(A, nheads, 4), span(D, nheads, 4), span(dt_bias, nheads, 4),
+                          rh0};
+  for (const Range& r : inputs) {
+    if (overlaps(ry, r)) return SSM_E_ALIAS;
+  }
+  if (overlaps(ry, rhf)) return SSM_E_ALIAS;
+  for (int i = 0; i < 8; ++i) {  // h_final may equal h0 exactly, nothing else
+    if (overlaps(rhf, inputs[i])) return SSM_E_ALIAS;
+  }
+  if (overlaps(rhf, rh0) && !(rhf.lo == rh0.lo && rhf.hi == rh0.hi)) return SSM_E_ALIAS;
+
+  ssm::SsdArgs a;
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.z = z;
+  a.dt_bias = dt_bias;
+  a.h0 = h0;
+  a.y = y;
+  a.h_final = h_final;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.nheads = nheads;
+  a.headdim = headdim;
+  a.dstate = dstate;
+  a.in_bf16 = in_dtype;
+  a.out_bf16 = out_dtype;
+  a.dt_softplus = (flags & SSM_FLAG_SOFTPLUS) != 0;
+  return map_hip(ssm::launch_ssd(a, stream));
+}
+
 }  // extern "C"

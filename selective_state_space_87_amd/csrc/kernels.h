@@ -86,6 +86,25 @@ struct ConvUpdateArgs {
   int in_bf16, out_bf16, silu;
 };
 
+struct SsdArgs {
+  const void* x;         // [B, L, H, P]
+  const void* dt;        // [B, L, H]
+  const float* A;        // [H]
+  const void* B;         // [B, L, N]
+  const void* C;         // [B, L, N]
+  const float* D;        // [H] or null
+  const void* z;         // [B, L, H, P] or null
+  const float* dt_bias;  // [H] or null
+  const float* h0;       // [B, H, P, N] or null
+  void* y;               // [B, L, H, P]
+  float* h_final;        // [B, H, P, N] or null
+  int64_t batch, seqlen, nheads, headdim, dstate;
+  int in_bf16, out_bf16, dt_softplus;
+};
+// Largest head size and state size of the SSD kernel.
+constexpr int64_t kSsdMaxHeadDim = 64;
+constexpr int64_t kSsdMaxState = 128;
+
 // How a scan of a given shape is run. The sequence is split into `chunks`
 // pieces of `chunk` steps (the last may be shorter) when there are too few
 // channel blocks to fill the device, or when one batch row's [L, d] plane is
@@ -141,5 +160,6 @@ int launch_scan_checkpoints(const ScanArgs& a, const uint32_t* bc, float* ckpt, 
 int scan_tile_steps(int NS);
 int launch_conv1d_fwd(const ConvArgs& a, void* stream);
 int launch_conv1d_update(const ConvUpdateArgs& a, void* stream);
+int launch_ssd(const SsdArgs& a, void* stream);
 
 }  // namespace ssm

@@ -1,0 +1,258 @@
+// Mamba-2 SSD layer (structured state-space duality) for gfx950, on MFMA.
+//
+// What is computed ("Mamba的隐藏代价", kongchang.com, section on the value and
+// limits of the argument: the selective SSM as y = M o (Q K^T) V with a lower
+// triangular semiseparable M, Q from C and K from B, run as matrix products;
+// "从 Transformer 到 Mamba", ybb.press, section 9.1: a diagonal state matrix).
+// With one scalar decay a[h] per head (the reading under which M is one
+// matrix for all states), per batch b, head h, channel p of the head, state n:
+//   dt_t = softplus(dt_raw[b,t,h] + dt_bias[h])          (or without softplus)
+//   H_t[n,p] = exp(dt_t a[h]) H_{t-1}[n,p] + dt_t B[b,t,n] x[b,t,h,p]
+//   y[b,t,h,p] = (sum_n C[b,t,n] H_t[n,p] + D[h] x[b,t,h,p]) * silu(z[b,t,h,p])
+//
+// Chunked form. The sequence is cut into chunks of Q = 64 steps. With cs_t
+// the inclusive sum of dt over the chunk's steps up to t, and H the state
+// entering the chunk, the chunk's outputs and its exit state are
+//   Y   = diag(exp(a cs_t)) C H                                (state readout)
+//       + (S X),  S[t,s] = (C_t . B_s) exp(a (cs_t - cs_s)) dt_s for s <= t
+//   H'  = exp(a cs_end) H + (B o w)^T X,  w_s = exp(a (cs_end - cs_s)) dt_s
+// four dense contractions (over N, Q, N and Q), which run on the matrix
+// cores; only the masking and decay factors are elementwise.
+//
+// Mapping. One block of four waves per (batch, head) walks its chunks in
+// order; the state [N, P] stays in MFMA accumulators for the whole sequence
+// (never written to memory between chunks), so x, dt, B, C, z and y cross HBM
+// exactly once. Wave w owns the output columns p = 16w .. 16w+15 of Y and of
+// the state, so the per-wave work is balanced; the 10 lower 16x16 tiles of S
+// are dealt round robin. Operands are staged in LDS as float32 and fed to
+// v_mfma_f32_16x16x4_f32 (float32 products, float32 accumulation: the same
+// arithmetic precision as the recurrence). Row strides are padded so that the
+// operand reads of a wave (16 rows x 4 columns, or 4 rows x 16 columns) fall
+// in distinct banks.
+#include <hip/hip_runtime.h>
+
+#include "device_math.h"
+#include "kernels.h"
+
+namespace ssm {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQ = 64;         // chunk length
+constexpr int kP = 64;         // padded head size
+constexpr int kThreads = 256;  // four waves
+constexpr int kXS = kP + 16;   // LDS row strides (floats)
+constexpr int kSS = kQ + 4;
+constexpr int kHS = kP + 16;
+
+// D (16x16) += A (16x4) B (4x16). Lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; element v of the result is D[4 (l / 16) + v][l % 16].
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int NP, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
+  constexpr int NPS = NP + 4;   // row stride of B and C in LDS
+  constexpr int NT = NP / 16;   // state row tiles
+  __shared__ float sC[kQ * NPS];
+  __shared__ float sB[kQ * NPS];
+  __shared__ float sX[kQ * kXS];
+  __shared__ float sS[kQ * kSS];
+  __shared__ float sH[NP * kHS];
+  __shared__ float sCs[kQ];  // inclusive sum of dt over the chunk
+  __shared__ float sDt[kQ];
+  __shared__ float sW[kQ];   // exp(a (cs_end - cs_s)) dt_s
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int H = static_cast<int>(p.nheads), P = static_cast<int>(p.headdim), N = static_cast<int>(p.dstate);
+  const int b = blockIdx.x / H;
+  const int hd = blockIdx.x % H;
+  const int64_t L = p.seqlen;
+  const float a2 = p.A[hd] * kLog2e;
+  const float bias = p.dt_bias ? p.dt_bias[hd] : 0.0f;
+  const float Dh = p.D ? p.D[hd] : 0.0f;
+  const int64_t HP = static_cast<int64_t>(H) * P;
+  const int64_t xb = static_cast<int64_t>(b) * L * HP + static_cast<int64_t>(hd) * P;  // + t*HP + p
+  const int64_t bcb = static_cast<int64_t>(b) * L * N;                                 // + t*N + n
+  const int64_t dtb = static_cast<int64_t>(b) * L * H + hd;                            // + t*H
+  const int64_t hsb = (static_cast<int64_t>(b) * H + hd) * P * N;                      // + p*N + n
+  const int pcol = 16 * w + lr;  // this lane's column of Y and of the state
+  const bool p_ok = pcol < P;
+
+  // State of the head: element v of row tile r is (n = 16r + 4lk + v, p = pcol).
+  f32x4 hacc[NT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int n = 16 * r + 4 * lk + v;
+      const float h = (p.h0 && p_ok && n < N) ? p.h0[hsb + static_cast<int64_t>(pcol) * N + n] : 0.0f;
+      hacc[r][v] = h;
+      sH[n * kHS + pcol] = h;
+    }
+  }
+
+  const int64_t nchunks = (L + kQ - 1) / kQ;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t t0 = c * kQ;
+    const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
+
+    // (1) The chunk's inputs into LDS (zeros past the sequence, the head
+    // size and the state size), and its step sizes and their running sums.
+    for (int i = tid; i < kQ * kP; i += kThreads) {
+      const int t = i / kP, pp = i % kP;
+      sX[t * kXS + pp] = (t < len && pp < P) ? load_elem<BF16_IN>(p.x, xb + (t0 + t) * HP + pp) : 0.0f;
+    }
+    for (int i = tid; i < kQ * NP; i += kThreads) {
+      const int t = i / NP, n = i % NP;
+      const bool ok = t < len && n < N;
+      const int64_t o = bcb + (t0 + t) * N + n;
+      sB[t * NPS + n] = ok ? load_elem<BF16_IN>(p.B, o) : 0.0f;
+      sC[t * NPS + n] = ok ? load_elem<BF16_IN>(p.C, o) : 0.0f;
+    }
+    if (w == 0) {
+      float dt = 0.0f;
+      if (lane < len) {
+        const float xr = load_elem<BF16_IN>(p.dt, dtb + (t0 + lane) * H) + bias;
+        dt = SOFTPLUS ? softplus_f(xr) : xr;
+      }
+      float cs = dt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float up = __shfl_up(cs, o, 64);
+        if (lane >= o) cs += up;
+      }
+      const float cend = __shfl(cs, 63, 64);
+      sDt[lane] = dt;
+      sCs[lane] = cs;
+      sW[lane] = exp2_hw(a2 * (cend - cs)) * dt;
+    }
+    __syncthreads();
+    const float cend = sCs[kQ - 1];
+
+    // (2a) Scores S: the lower 16x16 tiles (ti >= si), round robin over waves.
+    for (int q = w; q < 10; q += 4) {
+      const int ti = q == 0 ? 0 : (q < 3 ? 1 : (q < 6 ? 2 : 3));
+      const int si = q - ti * (ti + 1) / 2;
+      f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+      for (int k0 = 0; k0 < NP; k0 += 4) {
+        g = mfma4(sC[(16 * ti + lr) * NPS + k0 + lk], sB[(16 * si + lr) * NPS + k0 + lk], g);
+      }
+      const int s = 16 * si + lr;
+      const float css = sCs[s], dts = sDt[s];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = 16 * ti + 4 * lk + v;
+        sS[t * kSS + s] = t >= s ? g[v] * exp2_hw(a2 * (sCs[t] - css)) * dts : 0.0f;
+      }
+    }
+    // (2b) Readout of the entering state, diag(exp(a cs_t)) C H.
+    f32x4 yacc[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+      for (int k0 = 0; k0 < NP; k0 += 4) {
+        acc = mfma4(sC[(16 * ti + lr) * NPS + k0 + lk], sH[(k0 + lk) * kHS + pcol], acc);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] *= exp2_hw(a2 * sCs[16 * ti + 4 * lk + v]);
+      yacc[ti] = acc;
+    }
+    // (2c) Exit state: exp(a cs_end) H + (B o w)^T X.
+    const float dend = exp2_hw(a2 * cend);
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+      f32x4 acc = hacc[r] * dend;
+#pragma unroll 8
+      for (int k0 = 0; k0 < kQ; k0 += 4) {
+        const int s = k0 + lk;
+        acc = mfma4(sB[s * NPS + 16 * r + lr] * sW[s], sX[s * kXS + pcol], acc);
+      }
+      hacc[r] = acc;
+    }
+    __syncthreads();  // S complete; every wave is done reading the entering state
+
+    // (3) Y += S X over s <= t.
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      f32x4 acc = yacc[ti];
+      for (int k0 = 0; k0 < 16 * (ti + 1); k0 += 4) {
+        acc = mfma4(sS[(16 * ti + lr) * kSS + k0 + lk], sX[(k0 + lk) * kXS + pcol], acc);
+      }
+      yacc[ti] = acc;
+    }
+    // (4) Outputs, and the exit state for the next chunk's readout.
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = 16 * ti + 4 * lk + v;
+        if (t < len && p_ok) {
+          const int64_t o = xb + (t0 + t) * HP + pcol;
+          float yv = yacc[ti][v] + Dh * sX[t * kXS + pcol];
+          if (p.z) yv *= silu_f(load_elem<BF16_IN>(p.z, o));
+          store_elem<BF16_OUT>(p.y, o, yv);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sH[(16 * r + 4 * lk + v) * kHS + pcol] = hacc[r][v];
+    }
+    __syncthreads();  // inputs and the state are free for the next chunk
+  }
+
+  if (p.h_final && p_ok) {
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int n = 16 * r + 4 * lk + v;
+        if (n < N) p.h_final[hsb + static_cast<int64_t>(pcol) * N + n] = hacc[r][v];
+      }
+    }
+  }
+}
+
+template <int NP, bool BI, bool BO, bool SP>
+int launch_np(const SsdArgs& a, hipStream_t st) {
+  SsdArgs args = a;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&ssd_fwd_kernel<NP, BI, BO, SP>),
+                         dim3(static_cast<unsigned>(a.batch * a.nheads)), dim3(kThreads), kargs, 0, st);
+}
+
+template <bool BI, bool BO, bool SP>
+int launch_n(const SsdArgs& a, hipStream_t st) {
+  if (a.dstate <= 32) return launch_np<32, BI, BO, SP>(a, st);
+  if (a.dstate <= 64) return launch_np<64, BI, BO, SP>(a, st);
+  return launch_np<128, BI, BO, SP>(a, st);
+}
+
+template <bool BI, bool BO>
+int launch_io(const SsdArgs& a, hipStream_t st) {
+  return a.dt_softplus ? launch_n<BI, BO, true>(a, st) : launch_n<BI, BO, false>(a, st);
+}
+
+}  // namespace
+
+int launch_ssd(const SsdArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.batch == 0 || a.nheads == 0) return 0;
+  if (a.batch * a.nheads > 0x7fffffff || a.headdim > kSsdMaxHeadDim || a.dstate > kSsdMaxState) {
+    return hipErrorInvalidValue;
+  }
+  if (a.in_bf16) return a.out_bf16 ? launch_io<true, true>(a, st) : launch_io<true, false>(a, st);
+  return a.out_bf16 ? launch_io<false, true>(a, st) : launch_io<false, false>(a, st);
+}
+
+}  // namespace ssm

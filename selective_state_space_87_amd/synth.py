@@ -18,6 +18,10 @@ Recipe (the same for every workload; the sizes differ):
   weight [d, K] and bias [d] ~ U(-1/sqrt(K), 1/sqrt(K)) float32 (the range a
   Conv1d module with one input channel per group starts from); carried
   state [B, d, K-1] ~ N(0, 1) float32.
+- Mamba-2 SSD layer (heads of P channels, one decay per head): x, dt_raw,
+  z ~ N(0, 1) and B, C ~ N(0, 1) as above; A[h] = -U(1, 16) (the range
+  Mamba-2's decay starts from); D[h] = 1; dt_bias per head as delta_bias
+  per channel above.
 - bf16 tensors are float32 draws rounded to nearest-even. On the host they
   are kept as uint16 bit patterns, so both sides see the exact same values.
 
@@ -37,6 +41,7 @@ import numpy as np
 BLOCK = 4096
 TID_DT, TID_U, TID_DELTA, TID_B, TID_C, TID_Z, TID_STATE = range(7)
 TID_CONV_X, TID_CONV_W, TID_CONV_BIAS, TID_CONV_STATE = range(7, 11)
+TID_SSD_A = 11
 
 
 @dataclass(frozen=True)
@@ -193,6 +198,23 @@ def make_conv_inputs(batch, seqlen, dim, width, in_dtype="f32", seed=0, stream=4
     return dict(x=x, weight=w, bias=bias, state=state, in_dtype=in_dtype)
 
 
+def make_ssd_inputs(batch, seqlen, nheads, headdim, dstate, in_dtype="f32", dt_range=(1e-3, 1e-1),
+                    gate=True, seed=0, stream=500):
+    """SSD layer inputs: x, z [B, L, H, P], dt [B, L, H], B, C [B, L, N] in
+    ``in_dtype`` (float32 or bf16 bits); A, D, dt_bias [H] float32. Also the
+    keys in_dtype and dt_softplus (True)."""
+    d = nheads * headdim
+    x = _normal_blocks(seed, stream, TID_U, batch, seqlen, d, dtype=in_dtype).reshape(batch, seqlen, nheads, headdim)
+    dt = _normal_blocks(seed, stream, TID_DELTA, batch, seqlen, nheads, dtype=in_dtype)
+    Bm = _normal_blocks(seed, stream, TID_B, batch, seqlen, dstate, dtype=in_dtype)
+    Cm = _normal_blocks(seed, stream, TID_C, batch, seqlen, dstate, dtype=in_dtype)
+    z = (_normal_blocks(seed, stream, TID_Z, batch, seqlen, d, dtype=in_dtype).reshape(batch, seqlen, nheads, headdim)
+         if gate else None)
+    A = (-_rng(seed, stream, TID_SSD_A).uniform(1.0, 16.0, size=nheads)).astype(np.float32)
+    return dict(x=x, dt=dt, A=A, B=Bm, C=Cm, D=np.ones(nheads, np.float32), z=z,
+                dt_bias=delta_bias_for(nheads, dt_range, seed, stream), in_dtype=in_dtype, dt_softplus=True)
+
+
 def workload_inputs(i: int, seed: int = 0):
     """Inputs of the numbered workload (see WORKLOADS)."""
     w = WORKLOADS[i]
@@ -209,7 +231,7 @@ def as_float64(inp: dict) -> dict:
     out = {}
     for k, v in inp.items():
         if isinstance(v, np.ndarray):
-            if k in ("u", "delta", "B", "C", "z", "x"):
+            if k in ("u", "delta", "B", "C", "z", "x", "dt"):
                 out[k] = to_float64(v, dt)
             else:
                 out[k] = v.astype(np.float64)

@@ -236,3 +236,31 @@ def test_flag_bits(lib):
     assert scan(lib, sp=soft | zoh, u=None) == E_NULLPTR
     assert upd(lib, sp=zoh, state=None) == E_NULLPTR
     assert bwd(lib, sp=soft, dy=None) == E_NULLPTR
+
+
+def ssd(lib, B=2, L=8, H=2, P=4, N=4, ind=0, outd=0, fl=1, x=P, dt=2 * P, A=3 * P, Bm=4 * P, Cm=5 * P, D=6 * P,
+        z=7 * P, bias=8 * P, h0=9 * P, y=10 * P, hf=11 * P):
+    return lib.ssm_ssd_fwd(B, L, H, P, N, ind, outd, fl, vp(x), vp(dt), vp(A), vp(Bm), vp(Cm), vp(D), vp(z),
+                           vp(bias), vp(h0), vp(y), vp(hf), None)
+
+
+def test_ssd_validation(lib):
+    assert ssd(lib, B=-1) == E_SHAPE
+    assert ssd(lib, P=0) == E_SHAPE
+    assert ssd(lib, N=0) == E_SHAPE
+    assert ssd(lib, P=65) == E_UNSUPPORTED
+    assert ssd(lib, N=129) == E_UNSUPPORTED
+    assert ssd(lib, fl=2) == E_UNSUPPORTED          # no zero-order-hold option
+    assert ssd(lib, fl=4) == E_UNSUPPORTED
+    assert ssd(lib, ind=3) == E_DTYPE
+    assert ssd(lib, B=1 << 20, H=1 << 12) == E_UNSUPPORTED   # more than 2^31 - 1 blocks
+    assert ssd(lib, x=None) == E_NULLPTR
+    assert ssd(lib, A=None) == E_NULLPTR
+    assert ssd(lib, y=None) == E_NULLPTR
+    assert ssd(lib, dt=2 * P + 4) == E_ALIGN
+    assert ssd(lib, h0=9 * P + 2) == E_ALIGN
+    assert ssd(lib, y=P) == E_ALIAS                  # y == x
+    assert ssd(lib, y=5 * P + 16) == E_ALIAS         # y inside C
+    assert ssd(lib, hf=3 * P) == E_ALIAS             # h_final over A
+    assert ssd(lib, hf=9 * P + 4) == E_ALIAS         # partial overlap with h0
+    assert ssd(lib, H=0, x=None, A=None, y=None) == OK
