@@ -364,6 +364,52 @@ def bench_large_state(args, torch, binding, synth):
                          "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
 
 
+# Mamba-2 SSD layer, chunked matrix form with chunks of Q = 64 steps. Its
+# algorithmic work per (batch, chunk): the scores C B^T once (2 Q^2 N, shared
+# by every head), and per head S X (2 Q^2 P), the entering state's readout
+# C H (2 Q N P) and the exit state B^T X (2 Q N P). Float32 matrix cores.
+SSD_Q = 64
+MFMA_F32_PEAK = 157.3e12
+
+
+def ssd_alg_flops(B, L, H, P, N):
+    chunks = -(-L // SSD_Q)
+    return B * chunks * (2 * SSD_Q * SSD_Q * N + H * (2 * SSD_Q * SSD_Q * P + 4 * SSD_Q * N * P))
+
+
+def bench_ssd(args, torch, binding, synth):
+    """Mamba-2-shaped SSD layer: (4, 8192), 64 heads of 64 channels, N = 128, bf16 in and out."""
+    import numpy as np
+    B, L, H, P, N = 4, 8192, 64, 64, 128
+    inp = synth.make_ssd_inputs(B, L, H, P, N, "bf16", seed=0, stream=4800)
+    dev = torch.device("cuda:0")
+
+    def up(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t = {k: up(inp[k], "bf16") for k in ("x", "dt", "B", "C", "z")}
+    for k in ("A", "D", "dt_bias"):
+        t[k] = up(inp[k], "f32")
+    y = torch.empty(B, L, H, P, dtype=torch.bfloat16, device=dev)
+    hf = torch.empty(B, H, P, N, dtype=torch.float32, device=dev)
+    fn = lambda: binding.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],  # noqa
+                                     dt_bias=t["dt_bias"], dt_softplus=True, y=y, h_final=hf,
+                                     out_dtype=torch.bfloat16)
+    us = _timed(torch, fn, args.ssd_steps, 5)
+    flops = ssd_alg_flops(B, L, H, P, N)
+    alg_b = 3 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + B * H * P * N * 4 + 3 * H * 4
+    ach = flops / (us * 1e-6) / 1e12
+    return {"workload": f"Mamba-2-shaped SSD layer (batch={B}, seqlen={L}, heads={H}, headdim={P}, "
+                        f"d_state={N}, bf16 in/out, h_final), chunks of {SSD_Q}",
+            "us_per_call": us, "G_updates_per_s": B * L * H * P * N / (us * 1e-6) / 1e9,
+            "roofline": {"bound": "mfma", "achieved": ach, "peak": MFMA_F32_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": ach / (MFMA_F32_PEAK / 1e12), "traffic": None, "alg_flops_per_launch": flops,
+                         "mfma_dtype": "f32", "alg_bytes_per_launch": alg_b,
+                         "hbm_frac": alg_b / (us * 1e-6) / HBM_BPS}}
+
+
 def bench_bwd(args, torch, binding, synth, inp):
     """Backward of the selective scan on the 1.4B-shaped layer (float32 dy)."""
     import numpy as np
@@ -410,6 +456,8 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--no-zoh", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true")
+    ap.add_argument("--ssd-steps", type=int, default=20)
     ap.add_argument("--no-large-state", action="store_true")
     ap.add_argument("--large-state-steps", type=int, default=20)
     ap.add_argument("--zoh-steps", type=int, default=50)
@@ -480,6 +528,8 @@ def main():
         result["decode"] = bench_decode(args, torch, binding, synth)
     if not args.no_zoh:
         result["scan_zoh"] = bench_zoh(args, torch, binding, synth, inp)
+    if not args.no_ssd:
+        result["ssd"] = bench_ssd(args, torch, binding, synth)
     if not args.no_large_state:
         result["scan_n128"] = bench_large_state(args, torch, binding, synth)
     if not args.no_bwd:

@@ -290,7 +290,8 @@ int ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width,
  *
  *   batch, seqlen, nheads, headdim, dstate : B >= 0, L >= 0, H >= 0,
  *                                1 <= P <= 64, 1 <= N <= 128 (else
- *                                SSM_E_UNSUPPORTED); B * H < 2^31.
+ *                                SSM_E_UNSUPPORTED); B * H < 2^31,
+ *                                H * P < 2^23.
  *   in_dtype, out_dtype        : 0 float32, 1 bfloat16.
  *   flags                      : SSM_FLAG_SOFTPLUS or 0 (SSM_FLAG_ZOH and any
  *                                other bit: SSM_E_UNSUPPORTED).

@@ -418,6 +418,8 @@ int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, 
     return SSM_E_SHAPE;
   }
   if (bh > 0x7fffffff) return SSM_E_UNSUPPORTED;
+  // a chunk's rows of x, z and y are addressed with 32-bit offsets
+  if (nheads * headdim >= (int64_t(1) << 23)) return SSM_E_UNSUPPORTED;
   if (bh == 0) return SSM_OK;  // no head: nothing to compute or write
   if (A == nullptr) return SSM_E_NULLPTR;
   if (seqlen > 0 && (x == nullptr || dt == nullptr || B == nullptr || C == nullptr || y == nullptr)) {

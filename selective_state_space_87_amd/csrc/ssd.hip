@@ -39,6 +39,7 @@ namespace ssm {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 64;         // chunk length
 constexpr int kP = 64;         // padded head size
@@ -53,10 +54,43 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int NP, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS>
+// Chunk inputs in flight: the next chunk's x, B, C (and this lane's gate
+// values and, on wave 0, its step size) are loaded into registers while the
+// current chunk computes, and moved into LDS after the chunk's last barrier.
+// VEC: head size 64 and N equal to its padding, so rows are whole 16-byte
+// pieces (16-byte loads); otherwise one element per load.
+template <int NP, bool BF16_IN, bool VEC>
+struct SsdStage {
+  static constexpr int EB = BF16_IN ? 2 : 4;                        // element bytes
+  static constexpr int VE = VEC ? 16 / EB : 1;                      // elements per load
+  static constexpr int NXL = kQ * kP / (kThreads * VE);             // x loads per thread
+  static constexpr int NBL = kQ * NP / (kThreads * VE);             // B (and C) loads per thread
+  typedef std::conditional_t<VEC, u32x4, storage_t<BF16_IN>> word_t;
+  word_t xr[NXL], br[NBL], cr[NBL];
+  storage_t<BF16_IN> zr[16];
+  storage_t<BF16_IN> dtr;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void unpack_store(float* dst, u32x4 v) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dst[2 * j] = __uint_as_float(v[j] << 16);
+      dst[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = __uint_as_float(v[j]);
+  }
+}
+
+template <int NP, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool VEC>
 __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
   constexpr int NPS = NP + 4;   // row stride of B and C in LDS
   constexpr int NT = NP / 16;   // state row tiles
+  using Stage = SsdStage<NP, BF16_IN, VEC>;
+  constexpr int EB = Stage::EB, VE = Stage::VE;
   __shared__ float sC[kQ * NPS];
   __shared__ float sB[kQ * NPS];
   __shared__ float sX[kQ * kXS];
@@ -99,27 +133,97 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
   }
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
+  Stage stg;
+  // Issue the loads of chunk c (all masked to zero past the sequence: the
+  // descriptors end at the chunk's last valid row).
+  auto fetch = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t t0 = c * kQ;
+    const int len = static_cast<int>(c < nchunks ? (L - t0 < kQ ? L - t0 : kQ) : 0);
+    const char* xbase = static_cast<const char*>(p.x) + (xb + t0 * HP) * EB;
+    const rsrc_t rx = raw_buffer(xbase, len > 0 ? static_cast<uint32_t>(((len - 1) * HP + P) * EB) : 0u);
+    const rsrc_t rz = raw_buffer(p.z ? static_cast<const char*>(p.z) + (xb + t0 * HP) * EB : nullptr,
+                                 (p.z && len > 0) ? static_cast<uint32_t>(((len - 1) * HP + P) * EB) : 0u);
+    const int64_t bo = (bcb + t0 * N) * EB;
+    const uint32_t nbc = static_cast<uint32_t>(len * N * EB);
+    const rsrc_t rb = raw_buffer(static_cast<const char*>(p.B) + bo, nbc);
+    const rsrc_t rc = raw_buffer(static_cast<const char*>(p.C) + bo, nbc);
+#pragma unroll
+    for (int i = 0; i < Stage::NXL; ++i) {
+      const int e = (i * kThreads + tid) * VE;
+      const int t = e / kP, pp = e % kP;
+      const uint32_t off = static_cast<uint32_t>((t * HP + pp) * EB);
+      if constexpr (VEC) {
+        stg.xr[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      } else {
+        stg.xr[i] = buffer_load_bits<BF16_IN>(rx, pp < P ? off : kOutOfRange);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Stage::NBL; ++i) {
+      const int e = (i * kThreads + tid) * VE;
+      const int t = e / NP, n = e % NP;
+      const uint32_t off = static_cast<uint32_t>((t * N + n) * EB);
+      if constexpr (VEC) {
+        stg.br[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+        stg.cr[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+      } else {
+        stg.br[i] = buffer_load_bits<BF16_IN>(rb, n < N ? off : kOutOfRange);
+        stg.cr[i] = buffer_load_bits<BF16_IN>(rc, n < N ? off : kOutOfRange);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int t = 16 * (q >> 2) + 4 * lk + (q & 3);
+      stg.zr[q] = buffer_load_bits<BF16_IN>(rz, p_ok ? static_cast<uint32_t>((t * HP + pcol) * EB) : kOutOfRange);
+    }
+    if (w == 0) {
+      const rsrc_t rd = raw_buffer(static_cast<const char*>(p.dt) + (dtb + t0 * H) * EB,
+                                   len > 0 ? static_cast<uint32_t>(((len - 1) * H + 1) * EB) : 0u);
+      stg.dtr = buffer_load_bits<BF16_IN>(rd, static_cast<uint32_t>(lane * H * EB));
+    }
+  };
+  // Move the fetched chunk into LDS (zeros past the sequence, the head size
+  // and the state size).
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < Stage::NXL; ++i) {
+      const int e = (i * kThreads + tid) * VE;
+      const int t = e / kP, pp = e % kP;
+      if constexpr (VEC) {
+        unpack_store<BF16_IN>(&sX[t * kXS + pp], stg.xr[i]);
+      } else {
+        sX[t * kXS + pp] = bits_to_f32<BF16_IN>(stg.xr[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Stage::NBL; ++i) {
+      const int e = (i * kThreads + tid) * VE;
+      const int t = e / NP, n = e % NP;
+      if constexpr (VEC) {
+        unpack_store<BF16_IN>(&sB[t * NPS + n], stg.br[i]);
+        unpack_store<BF16_IN>(&sC[t * NPS + n], stg.cr[i]);
+      } else {
+        sB[t * NPS + n] = bits_to_f32<BF16_IN>(stg.br[i]);
+        sC[t * NPS + n] = bits_to_f32<BF16_IN>(stg.cr[i]);
+      }
+    }
+  };
+
+  fetch(0);
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * kQ;
     const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
 
-    // (1) The chunk's inputs into LDS (zeros past the sequence, the head
-    // size and the state size), and its step sizes and their running sums.
-    for (int i = tid; i < kQ * kP; i += kThreads) {
-      const int t = i / kP, pp = i % kP;
-      sX[t * kXS + pp] = (t < len && pp < P) ? load_elem<BF16_IN>(p.x, xb + (t0 + t) * HP + pp) : 0.0f;
-    }
-    for (int i = tid; i < kQ * NP; i += kThreads) {
-      const int t = i / NP, n = i % NP;
-      const bool ok = t < len && n < N;
-      const int64_t o = bcb + (t0 + t) * N + n;
-      sB[t * NPS + n] = ok ? load_elem<BF16_IN>(p.B, o) : 0.0f;
-      sC[t * NPS + n] = ok ? load_elem<BF16_IN>(p.C, o) : 0.0f;
-    }
+    // (1) The chunk's inputs into LDS, its step sizes and their running sums;
+    // then the next chunk's loads are issued.
+    stage();
+    float zg[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) zg[q] = bits_to_f32<BF16_IN>(stg.zr[q]);
     if (w == 0) {
       float dt = 0.0f;
       if (lane < len) {
-        const float xr = load_elem<BF16_IN>(p.dt, dtb + (t0 + lane) * H) + bias;
+        const float xr = bits_to_f32<BF16_IN>(stg.dtr) + bias;
         dt = SOFTPLUS ? softplus_f(xr) : xr;
       }
       float cs = dt;
@@ -134,6 +238,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
       sW[lane] = exp2_hw(a2 * (cend - cs)) * dt;
     }
     __syncthreads();
+    fetch(c + 1);
     const float cend = sCs[kQ - 1];
 
     // (2a) Scores S: the lower 16x16 tiles (ti >= si), round robin over waves.
@@ -153,41 +258,43 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
         sS[t * kSS + s] = t >= s ? g[v] * exp2_hw(a2 * (sCs[t] - css)) * dts : 0.0f;
       }
     }
+    // The contractions below run k outermost: one k-step's shared operand
+    // (a row of the state, of X) is read once for all the wave's tiles, and
+    // consecutive matrix instructions feed independent accumulators.
     // (2b) Readout of the entering state, diag(exp(a cs_t)) C H.
     f32x4 yacc[4];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-      for (int k0 = 0; k0 < NP; k0 += 4) {
-        acc = mfma4(sC[(16 * ti + lr) * NPS + k0 + lk], sH[(k0 + lk) * kHS + pcol], acc);
-      }
+    for (int ti = 0; ti < 4; ++ti) yacc[ti] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int k0 = 0; k0 < NP; k0 += 4) {
+      const float hv = sH[(k0 + lk) * kHS + pcol];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] *= exp2_hw(a2 * sCs[16 * ti + 4 * lk + v]);
-      yacc[ti] = acc;
+      for (int ti = 0; ti < 4; ++ti) yacc[ti] = mfma4(sC[(16 * ti + lr) * NPS + k0 + lk], hv, yacc[ti]);
+    }
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) yacc[ti][v] *= exp2_hw(a2 * sCs[16 * ti + 4 * lk + v]);
     }
     // (2c) Exit state: exp(a cs_end) H + (B o w)^T X.
     const float dend = exp2_hw(a2 * cend);
 #pragma unroll
-    for (int r = 0; r < NT; ++r) {
-      f32x4 acc = hacc[r] * dend;
-#pragma unroll 8
-      for (int k0 = 0; k0 < kQ; k0 += 4) {
-        const int s = k0 + lk;
-        acc = mfma4(sB[s * NPS + 16 * r + lr] * sW[s], sX[s * kXS + pcol], acc);
-      }
-      hacc[r] = acc;
+    for (int r = 0; r < NT; ++r) hacc[r] *= dend;
+#pragma unroll 2
+    for (int k0 = 0; k0 < kQ; k0 += 4) {
+      const int s = k0 + lk;
+      const float xv = sX[s * kXS + pcol], wv = sW[s];
+#pragma unroll
+      for (int r = 0; r < NT; ++r) hacc[r] = mfma4(sB[s * NPS + 16 * r + lr] * wv, xv, hacc[r]);
     }
     __syncthreads();  // S complete; every wave is done reading the entering state
 
-    // (3) Y += S X over s <= t.
+    // (3) Y += S X over s <= t (row tile ti takes the k-steps below 16 (ti + 1)).
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      f32x4 acc = yacc[ti];
-      for (int k0 = 0; k0 < 16 * (ti + 1); k0 += 4) {
-        acc = mfma4(sS[(16 * ti + lr) * kSS + k0 + lk], sX[(k0 + lk) * kXS + pcol], acc);
-      }
-      yacc[ti] = acc;
+    for (int k0 = 0; k0 < kQ; k0 += 4) {
+      const float xv = sX[(k0 + lk) * kXS + pcol];
+#pragma unroll
+      for (int ti = k0 / 16; ti < 4; ++ti) yacc[ti] = mfma4(sS[(16 * ti + lr) * kSS + k0 + lk], xv, yacc[ti]);
     }
     // (4) Outputs, and the exit state for the next chunk's readout.
 #pragma unroll
@@ -198,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
         if (t < len && p_ok) {
           const int64_t o = xb + (t0 + t) * HP + pcol;
           float yv = yacc[ti][v] + Dh * sX[t * kXS + pcol];
-          if (p.z) yv *= silu_f(load_elem<BF16_IN>(p.z, o));
+          if (p.z) yv *= silu_f(zg[4 * ti + v]);
           store_elem<BF16_OUT>(p.y, o, yv);
         }
       }
@@ -227,8 +334,10 @@ template <int NP, bool BI, bool BO, bool SP>
 int launch_np(const SsdArgs& a, hipStream_t st) {
   SsdArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&ssd_fwd_kernel<NP, BI, BO, SP>),
-                         dim3(static_cast<unsigned>(a.batch * a.nheads)), dim3(kThreads), kargs, 0, st);
+  const bool vec = a.headdim == kP && a.dstate == NP;
+  const void* fn = vec ? reinterpret_cast<const void*>(&ssd_fwd_kernel<NP, BI, BO, SP, true>)
+                       : reinterpret_cast<const void*>(&ssd_fwd_kernel<NP, BI, BO, SP, false>);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.batch * a.nheads)), dim3(kThreads), kargs, 0, st);
 }
 
 template <bool BI, bool BO, bool SP>

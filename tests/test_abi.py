@@ -264,3 +264,4 @@ def test_ssd_validation(lib):
     assert ssd(lib, hf=3 * P) == E_ALIAS             # h_final over A
     assert ssd(lib, hf=9 * P + 4) == E_ALIAS         # partial overlap with h0
     assert ssd(lib, H=0, x=None, A=None, y=None) == OK
+    assert ssd(lib, B=1, H=1 << 17, P=64) == E_UNSUPPORTED   # H * P beyond 2^23
