@@ -28,7 +28,7 @@
 // v_mfma_f32_16x16x4_f32 (float32 products, float32 accumulation: the same
 // arithmetic precision as the recurrence). Row strides are padded so that the
 // operand reads of a wave (16 rows x 4 columns, or 4 rows x 16 columns) fall
-// in distinct banks.
+// in distinct banks, or at worst two lanes to a bank.
 #include <hip/hip_runtime.h>
 
 #include "device_math.h"
@@ -44,9 +44,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kQ = 64;         // chunk length
 constexpr int kP = 64;         // padded head size
 constexpr int kThreads = 256;  // four waves
-constexpr int kXS = kP + 16;   // LDS row strides (floats)
+// LDS row strides (floats). An operand read of a wave touches 16 rows x 4
+// consecutive columns (A-type: row stride = 4 mod 64 banks spreads them) or
+// 4 rows x 16 consecutive columns (B-type: 16 mod 64). B and the state are
+// read both ways (and the state written in the accumulator layout, 4 rows
+// of 16 per v); a stride of 20 mod 64 keeps every one of those within 2-way.
+constexpr int kXS = kP + 16;
 constexpr int kSS = kQ + 4;
-constexpr int kHS = kP + 16;
+constexpr int kHS = kP + 20;
 
 // D (16x16) += A (16x4) B (4x16). Lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16]; element v of the result is D[4 (l / 16) + v][l % 16].
@@ -87,7 +92,7 @@ __device__ __forceinline__ void unpack_store(float* dst, u32x4 v) {
 
 template <int NP, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool VEC>
 __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
-  constexpr int NPS = NP + 4;   // row stride of B and C in LDS
+  constexpr int NPS = NP + 20;  // row stride of B and C in LDS (20 mod 64, or 52 for NP = 32)
   constexpr int NT = NP / 16;   // state row tiles
   using Stage = SsdStage<NP, BF16_IN, VEC>;
   constexpr int EB = Stage::EB, VE = Stage::VE;
@@ -241,31 +246,53 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
     fetch(c + 1);
     const float cend = sCs[kQ - 1];
 
-    // (2a) Scores S: the lower 16x16 tiles (ti >= si), round robin over waves.
-    for (int q = w; q < 10; q += 4) {
-      const int ti = q == 0 ? 0 : (q < 3 ? 1 : (q < 6 ? 2 : 3));
-      const int si = q - ti * (ti + 1) / 2;
-      f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-      for (int k0 = 0; k0 < NP; k0 += 4) {
-        g = mfma4(sC[(16 * ti + lr) * NPS + k0 + lk], sB[(16 * si + lr) * NPS + k0 + lk], g);
-      }
-      const int s = 16 * si + lr;
-      const float css = sCs[s], dts = sDt[s];
+    // Every contraction below runs k outermost over independent accumulators
+    // and is unrolled whole, so that a k-step's operand reads are issued well
+    // before its matrix instructions (one wave per SIMD: nothing else hides
+    // the LDS latency), and a shared operand (a row of the state, of X) is
+    // read once for all of the wave's tiles.
+    // (2a) Scores S: the 10 lower 16x16 tiles (ti >= si), q = w, w+4, w+8
+    // (the third only for waves 0 and 1).
+    auto scores = [&](auto nq) __attribute__((always_inline)) {
+      constexpr int NQ = decltype(nq)::value;
+      int ti[NQ], si[NQ];
+      f32x4 g[NQ];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = 16 * ti + 4 * lk + v;
-        sS[t * kSS + s] = t >= s ? g[v] * exp2_hw(a2 * (sCs[t] - css)) * dts : 0.0f;
+      for (int j = 0; j < NQ; ++j) {
+        const int q = w + 4 * j;
+        ti[j] = q == 0 ? 0 : (q < 3 ? 1 : (q < 6 ? 2 : 3));
+        si[j] = q - ti[j] * (ti[j] + 1) / 2;
+        g[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
+#pragma unroll
+      for (int k0 = 0; k0 < NP; k0 += 4) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+          g[j] = mfma4(sC[(16 * ti[j] + lr) * NPS + k0 + lk], sB[(16 * si[j] + lr) * NPS + k0 + lk], g[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const int s = 16 * si[j] + lr;
+        const float css = sCs[s], dts = sDt[s];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = 16 * ti[j] + 4 * lk + v;
+          const float val = g[j][v] * exp2_hw(a2 * (sCs[t] - css)) * dts;
+          sS[t * kSS + s] = t >= s ? val : 0.0f;
+        }
+      }
+    };
+    if (w < 2) {
+      scores(std::integral_constant<int, 3>{});
+    } else {
+      scores(std::integral_constant<int, 2>{});
     }
-    // The contractions below run k outermost: one k-step's shared operand
-    // (a row of the state, of X) is read once for all the wave's tiles, and
-    // consecutive matrix instructions feed independent accumulators.
     // (2b) Readout of the entering state, diag(exp(a cs_t)) C H.
     f32x4 yacc[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) yacc[ti] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
+#pragma unroll
     for (int k0 = 0; k0 < NP; k0 += 4) {
       const float hv = sH[(k0 + lk) * kHS + pcol];
 #pragma unroll
@@ -280,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
     const float dend = exp2_hw(a2 * cend);
 #pragma unroll
     for (int r = 0; r < NT; ++r) hacc[r] *= dend;
-#pragma unroll 2
+#pragma unroll
     for (int k0 = 0; k0 < kQ; k0 += 4) {
       const int s = k0 + lk;
       const float xv = sX[s * kXS + pcol], wv = sW[s];
