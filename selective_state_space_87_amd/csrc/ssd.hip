@@ -19,12 +19,14 @@
 // four dense contractions (over N, Q, N and Q), which run on the matrix
 // cores; only the masking and decay factors are elementwise.
 //
-// Mapping. One block of four waves per (batch, head) walks its chunks in
+// Mapping. One block of eight waves per (batch, head) walks its chunks in
 // order; the state [N, P] stays in MFMA accumulators for the whole sequence
 // (never written to memory between chunks), so x, dt, B, C, z and y cross HBM
-// exactly once. Wave w owns the output columns p = 16w .. 16w+15 of Y and of
-// the state, so the per-wave work is balanced; the 10 lower 16x16 tiles of S
-// are dealt round robin. Operands are staged in LDS as float32 and fed to
+// exactly once. Wave w owns the 16 columns p = 16 (w mod 4) + 0..15 of Y and
+// of the state, and half of their rows: Y row tiles {0, 3} or {1, 2} (equal
+// shares of the triangular S X) and one half of the state's row tiles; the
+// 10 lower 16x16 tiles of S are dealt round robin. Two waves share each SIMD,
+// so one's LDS waits overlap the other's matrix instructions. Operands are staged in LDS as float32 and fed to
 // v_mfma_f32_16x16x4_f32 (float32 products, float32 accumulation: the same
 // arithmetic precision as the recurrence). Row strides are padded so that the
 // operand reads of a wave (16 rows x 4 columns, or 4 rows x 16 columns) fall
@@ -43,7 +45,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 64;         // chunk length
 constexpr int kP = 64;         // padded head size
-constexpr int kThreads = 256;  // four waves
+constexpr int kWaves = 8;      // two per SIMD
+constexpr int kThreads = 64 * kWaves;
 // LDS row strides (floats). An operand read of a wave touches 16 rows x 4
 // consecutive columns (A-type: row stride = 4 mod 64 banks spreads them) or
 // 4 rows x 16 consecutive columns (B-type: 16 mod 64). B and the state are
@@ -69,10 +72,10 @@ struct SsdStage {
   static constexpr int EB = BF16_IN ? 2 : 4;                        // element bytes
   static constexpr int VE = VEC ? 16 / EB : 1;                      // elements per load
   static constexpr int NXL = kQ * kP / (kThreads * VE);             // x loads per thread
-  static constexpr int NBL = kQ * NP / (kThreads * VE);             // B (and C) loads per thread
+  static constexpr int NBL = (kQ * NP + kThreads * VE - 1) / (kThreads * VE);  // B (and C) loads per thread
   typedef std::conditional_t<VEC, u32x4, storage_t<BF16_IN>> word_t;
   word_t xr[NXL], br[NBL], cr[NBL];
-  storage_t<BF16_IN> zr[16];
+  storage_t<BF16_IN> zr[8];
   storage_t<BF16_IN> dtr;
 };
 
@@ -93,7 +96,7 @@ __device__ __forceinline__ void unpack_store(float* dst, u32x4 v) {
 template <int NP, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool VEC>
 __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
   constexpr int NPS = NP + 20;  // row stride of B and C in LDS (20 mod 64, or 52 for NP = 32)
-  constexpr int NT = NP / 16;   // state row tiles
+  constexpr int NT = NP / 32;   // state row tiles per wave (of NP / 16)
   using Stage = SsdStage<NP, BF16_IN, VEC>;
   constexpr int EB = Stage::EB, VE = Stage::VE;
   __shared__ float sC[kQ * NPS];
@@ -121,18 +124,21 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
   const int64_t bcb = static_cast<int64_t>(b) * L * N;                                 // + t*N + n
   const int64_t dtb = static_cast<int64_t>(b) * L * H + hd;                            // + t*H
   const int64_t hsb = (static_cast<int64_t>(b) * H + hd) * P * N;                      // + p*N + n
-  const int pcol = 16 * w + lr;  // this lane's column of Y and of the state
+  const int hf = w >> 2;                 // which half of the rows
+  const int pcol = 16 * (w & 3) + lr;    // this lane's column of Y and of the state
   const bool p_ok = pcol < P;
+  const int yt0 = hf, yt1 = 3 - hf;      // Y row tiles: {0, 3} or {1, 2}
+  const int r0 = hf * NT;                // first state row tile
 
-  // State of the head: element v of row tile r is (n = 16r + 4lk + v, p = pcol).
+  // State rows of this wave: element v of tile j is (n = 16 (r0 + j) + 4lk + v, p = pcol).
   f32x4 hacc[NT];
 #pragma unroll
-  for (int r = 0; r < NT; ++r) {
+  for (int j = 0; j < NT; ++j) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int n = 16 * r + 4 * lk + v;
+      const int n = 16 * (r0 + j) + 4 * lk + v;
       const float h = (p.h0 && p_ok && n < N) ? p.h0[hsb + static_cast<int64_t>(pcol) * N + n] : 0.0f;
-      hacc[r][v] = h;
+      hacc[j][v] = h;
       sH[n * kHS + pcol] = h;
     }
   }
@@ -167,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
     for (int i = 0; i < Stage::NBL; ++i) {
       const int e = (i * kThreads + tid) * VE;
       const int t = e / NP, n = e % NP;
-      const uint32_t off = static_cast<uint32_t>((t * N + n) * EB);
+      const bool in = e < kQ * NP;       // (a thread's last load may fall past the tile)
+      const uint32_t off = in ? static_cast<uint32_t>((t * N + n) * EB) : kOutOfRange;
       if constexpr (VEC) {
         stg.br[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
         stg.cr[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
@@ -177,8 +184,8 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int t = 16 * (q >> 2) + 4 * lk + (q & 3);
+    for (int q = 0; q < 8; ++q) {
+      const int t = 16 * ((q >> 2) ? yt1 : yt0) + 4 * lk + (q & 3);
       stg.zr[q] = buffer_load_bits<BF16_IN>(rz, p_ok ? static_cast<uint32_t>((t * HP + pcol) * EB) : kOutOfRange);
     }
     if (w == 0) {
@@ -204,6 +211,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
     for (int i = 0; i < Stage::NBL; ++i) {
       const int e = (i * kThreads + tid) * VE;
       const int t = e / NP, n = e % NP;
+      if (e >= kQ * NP) break;
       if constexpr (VEC) {
         unpack_store<BF16_IN>(&sB[t * NPS + n], stg.br[i]);
         unpack_store<BF16_IN>(&sC[t * NPS + n], stg.cr[i]);
@@ -222,9 +230,9 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
     // (1) The chunk's inputs into LDS, its step sizes and their running sums;
     // then the next chunk's loads are issued.
     stage();
-    float zg[16];
+    float zg[8];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) zg[q] = bits_to_f32<BF16_IN>(stg.zr[q]);
+    for (int q = 0; q < 8; ++q) zg[q] = bits_to_f32<BF16_IN>(stg.zr[q]);
     if (w == 0) {
       float dt = 0.0f;
       if (lane < len) {
@@ -251,15 +259,15 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
     // before its matrix instructions (one wave per SIMD: nothing else hides
     // the LDS latency), and a shared operand (a row of the state, of X) is
     // read once for all of the wave's tiles.
-    // (2a) Scores S: the 10 lower 16x16 tiles (ti >= si), q = w, w+4, w+8
-    // (the third only for waves 0 and 1).
+    // (2a) Scores S: the 10 lower 16x16 tiles (ti >= si), q = w and w+8
+    // (the second only for waves 0 and 1).
     auto scores = [&](auto nq) __attribute__((always_inline)) {
       constexpr int NQ = decltype(nq)::value;
       int ti[NQ], si[NQ];
       f32x4 g[NQ];
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
-        const int q = w + 4 * j;
+        const int q = w + kWaves * j;
         ti[j] = q == 0 ? 0 : (q < 3 ? 1 : (q < 6 ? 2 : 3));
         si[j] = q - ti[j] * (ti[j] + 1) / 2;
         g[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -283,75 +291,84 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
         }
       }
     };
-    if (w < 2) {
-      scores(std::integral_constant<int, 3>{});
-    } else {
+    if (w < 10 - kWaves) {
       scores(std::integral_constant<int, 2>{});
+    } else {
+      scores(std::integral_constant<int, 1>{});
     }
     // (2b) Readout of the entering state, diag(exp(a cs_t)) C H.
-    f32x4 yacc[4];
+    const int yt[2] = {yt0, yt1};
+    f32x4 yacc[2];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) yacc[ti] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 2; ++j) yacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k0 = 0; k0 < NP; k0 += 4) {
       const float hv = sH[(k0 + lk) * kHS + pcol];
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) yacc[ti] = mfma4(sC[(16 * ti + lr) * NPS + k0 + lk], hv, yacc[ti]);
+      for (int j = 0; j < 2; ++j) yacc[j] = mfma4(sC[(16 * yt[j] + lr) * NPS + k0 + lk], hv, yacc[j]);
     }
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) yacc[ti][v] *= exp2_hw(a2 * sCs[16 * ti + 4 * lk + v]);
+      for (int v = 0; v < 4; ++v) yacc[j][v] *= exp2_hw(a2 * sCs[16 * yt[j] + 4 * lk + v]);
     }
     // (2c) Exit state: exp(a cs_end) H + (B o w)^T X.
     const float dend = exp2_hw(a2 * cend);
 #pragma unroll
-    for (int r = 0; r < NT; ++r) hacc[r] *= dend;
+    for (int j = 0; j < NT; ++j) hacc[j] *= dend;
 #pragma unroll
     for (int k0 = 0; k0 < kQ; k0 += 4) {
       const int s = k0 + lk;
       const float xv = sX[s * kXS + pcol], wv = sW[s];
 #pragma unroll
-      for (int r = 0; r < NT; ++r) hacc[r] = mfma4(sB[s * NPS + 16 * r + lr] * wv, xv, hacc[r]);
+      for (int j = 0; j < NT; ++j) hacc[j] = mfma4(sB[s * NPS + 16 * (r0 + j) + lr] * wv, xv, hacc[j]);
     }
     __syncthreads();  // S complete; every wave is done reading the entering state
 
     // (3) Y += S X over s <= t (row tile ti takes the k-steps below 16 (ti + 1)).
+    auto diag = [&](auto ta, auto tb) __attribute__((always_inline)) {
+      constexpr int TA = decltype(ta)::value, TB = decltype(tb)::value;
 #pragma unroll
-    for (int k0 = 0; k0 < kQ; k0 += 4) {
-      const float xv = sX[(k0 + lk) * kXS + pcol];
-#pragma unroll
-      for (int ti = k0 / 16; ti < 4; ++ti) yacc[ti] = mfma4(sS[(16 * ti + lr) * kSS + k0 + lk], xv, yacc[ti]);
+      for (int k0 = 0; k0 < 16 * (TB + 1); k0 += 4) {
+        const float xv = sX[(k0 + lk) * kXS + pcol];
+        if (k0 < 16 * (TA + 1)) yacc[0] = mfma4(sS[(16 * TA + lr) * kSS + k0 + lk], xv, yacc[0]);
+        yacc[1] = mfma4(sS[(16 * TB + lr) * kSS + k0 + lk], xv, yacc[1]);
+      }
+    };
+    if (hf == 0) {
+      diag(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+    } else {
+      diag(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
     }
     // (4) Outputs, and the exit state for the next chunk's readout.
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int t = 16 * ti + 4 * lk + v;
+        const int t = 16 * yt[j] + 4 * lk + v;
         if (t < len && p_ok) {
           const int64_t o = xb + (t0 + t) * HP + pcol;
-          float yv = yacc[ti][v] + Dh * sX[t * kXS + pcol];
-          if (p.z) yv *= silu_f(zg[4 * ti + v]);
+          float yv = yacc[j][v] + Dh * sX[t * kXS + pcol];
+          if (p.z) yv *= silu_f(zg[4 * j + v]);
           store_elem<BF16_OUT>(p.y, o, yv);
         }
       }
     }
 #pragma unroll
-    for (int r = 0; r < NT; ++r) {
+    for (int j = 0; j < NT; ++j) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sH[(16 * r + 4 * lk + v) * kHS + pcol] = hacc[r][v];
+      for (int v = 0; v < 4; ++v) sH[(16 * (r0 + j) + 4 * lk + v) * kHS + pcol] = hacc[j][v];
     }
     __syncthreads();  // inputs and the state are free for the next chunk
   }
 
   if (p.h_final && p_ok) {
 #pragma unroll
-    for (int r = 0; r < NT; ++r) {
+    for (int j = 0; j < NT; ++j) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int n = 16 * r + 4 * lk + v;
-        if (n < N) p.h_final[hsb + static_cast<int64_t>(pcol) * N + n] = hacc[r][v];
+        const int n = 16 * (r0 + j) + 4 * lk + v;
+        if (n < N) p.h_final[hsb + static_cast<int64_t>(pcol) * N + n] = hacc[j][v];
       }
     }
   }
