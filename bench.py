@@ -401,11 +401,12 @@ def bench_ssd(args, torch, binding, synth):
     flops = ssd_alg_flops(B, L, H, P, N)
     alg_b = 3 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + B * H * P * N * 4 + 3 * H * 4
     ach = flops / (us * 1e-6) / 1e12
+    traffic = counter_traffic("ssd_mamba2_counters.md", kernel_source_hash())
     return {"workload": f"Mamba-2-shaped SSD layer (batch={B}, seqlen={L}, heads={H}, headdim={P}, "
                         f"d_state={N}, bf16 in/out, h_final), chunks of {SSD_Q}",
             "us_per_call": us, "G_updates_per_s": B * L * H * P * N / (us * 1e-6) / 1e9,
             "roofline": {"bound": "mfma", "achieved": ach, "peak": MFMA_F32_PEAK / 1e12, "unit": "TFLOP/s",
-                         "frac": ach / (MFMA_F32_PEAK / 1e12), "traffic": None, "alg_flops_per_launch": flops,
+                         "frac": ach / (MFMA_F32_PEAK / 1e12), "traffic": traffic, "alg_flops_per_launch": flops,
                          "mfma_dtype": "f32", "alg_bytes_per_launch": alg_b,
                          "hbm_frac": alg_b / (us * 1e-6) / HBM_BPS}}
 
