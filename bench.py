@@ -367,9 +367,12 @@ def bench_large_state(args, torch, binding, synth):
 # Mamba-2 SSD layer, chunked matrix form with chunks of Q = 64 steps. Its
 # algorithmic work per (batch, chunk): the scores C B^T once (2 Q^2 N, shared
 # by every head), and per head S X (2 Q^2 P), the entering state's readout
-# C H (2 Q N P) and the exit state B^T X (2 Q N P). Float32 matrix cores.
+# C H (2 Q N P) and the exit state B^T X (2 Q N P). With bfloat16 inputs the
+# products run on the bfloat16 matrix cores (2.5 PFLOP/s dense), where these
+# flops take a third of the time the algorithmic HBM bytes take at 8 TB/s:
+# the layer's roofline is HBM.
 SSD_Q = 64
-MFMA_F32_PEAK = 157.3e12
+MFMA_BF16_PEAK = 2.5e15
 
 
 def ssd_alg_flops(B, L, H, P, N):
@@ -400,15 +403,15 @@ def bench_ssd(args, torch, binding, synth):
     us = _timed(torch, fn, args.ssd_steps, 5)
     flops = ssd_alg_flops(B, L, H, P, N)
     alg_b = 3 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + B * H * P * N * 4 + 3 * H * 4
-    ach = flops / (us * 1e-6) / 1e12
+    tflops = flops / (us * 1e-6) / 1e12
     traffic = counter_traffic("ssd_mamba2_counters.md", kernel_source_hash())
+    rl = hbm_roofline(alg_b, us, traffic)
+    rl.update({"alg_flops_per_launch": flops, "mfma_dtype": "bf16", "mfma_TFLOPs": tflops,
+               "mfma_peak_TFLOPs": MFMA_BF16_PEAK / 1e12, "mfma_frac": tflops / (MFMA_BF16_PEAK / 1e12)})
     return {"workload": f"Mamba-2-shaped SSD layer (batch={B}, seqlen={L}, heads={H}, headdim={P}, "
                         f"d_state={N}, bf16 in/out, h_final), chunks of {SSD_Q}",
             "us_per_call": us, "G_updates_per_s": B * L * H * P * N / (us * 1e-6) / 1e9,
-            "roofline": {"bound": "mfma", "achieved": ach, "peak": MFMA_F32_PEAK / 1e12, "unit": "TFLOP/s",
-                         "frac": ach / (MFMA_F32_PEAK / 1e12), "traffic": traffic, "alg_flops_per_launch": flops,
-                         "mfma_dtype": "f32", "alg_bytes_per_launch": alg_b,
-                         "hbm_frac": alg_b / (us * 1e-6) / HBM_BPS}}
+            "roofline": rl}
 
 
 def bench_bwd(args, torch, binding, synth, inp):

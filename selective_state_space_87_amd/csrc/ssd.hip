@@ -374,6 +374,330 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
   }
 }
 
+// bfloat16 inputs with P = 64 and N a power of two (>= 32): the same chunked
+// form on v_mfma_f32_16x16x32_bf16, eight times the float32 instruction's
+// work per cycle. x, B and C are exact in bfloat16, and every product has
+// one of them as an operand; the other operand (the decayed scores, the
+// state, the w-scaled B) is float32 and enters as the sum of two bfloat16
+// halves, hi = bf16(v) and lo = bf16(v - hi), so each product is taken to
+// about 16 bits (two instructions where the float32 path needs eight).
+//   scores   G = C B^T                     C, B exact            1 x
+//   readout  C H                           H = Hhi + Hlo          2 x
+//   diagonal S X                           S = Shi + Slo          2 x
+//   state    (B o w)^T X                   B o w = hi + lo        2 x
+// Operands are read as 16-byte runs of 8 consecutive k: every LDS array is
+// laid out with the contraction index contiguous (x and the w-scaled B are
+// stored transposed), rows padded by 8 elements (16 bytes).
+// D (16x16) += A (16x32) B (32x16) on bfloat16: lane l supplies
+// A[l % 16][8 (l / 16) .. +7] and B[8 (l / 16) .. +7][l % 16]; the result is
+// laid out as for the float32 instruction.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16_bits(v);
+  lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+}
+
+template <int NP, bool BF16_OUT, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
+  constexpr int CS = NP + 8;     // row stride of C, B [Q][NP] and H^T [P][NP] (elements)
+  constexpr int QS = kQ + 8;     // row stride of x^T [P][Q], S [Q][Q], (B o w)^T [NP][Q]
+  constexpr int NT = NP / 32;    // state row tiles per wave
+  constexpr int NBL = (kQ * NP + kThreads * 8 - 1) / (kThreads * 8);  // B (and C) loads per thread
+  constexpr int NBT = (NP * (kQ / 8) + kThreads - 1) / kThreads;      // (B o w)^T runs per thread
+  __shared__ __attribute__((aligned(16))) uint16_t sC[kQ * CS];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * CS];
+  __shared__ __attribute__((aligned(16))) uint16_t sBt[2][NP * QS];  // (B o w)^T, hi and lo
+  __shared__ __attribute__((aligned(16))) uint16_t sXt[kP * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t sS[2][kQ * QS];   // S, hi and lo
+  __shared__ __attribute__((aligned(16))) uint16_t sHt[2][kP * CS];  // H^T, hi and lo
+  __shared__ float sCs[kQ];
+  __shared__ float sDt[kQ];
+  __shared__ float sW[kQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int H = static_cast<int>(p.nheads), N = static_cast<int>(p.dstate);
+  const int b = blockIdx.x / H;
+  const int hd = blockIdx.x % H;
+  const int64_t L = p.seqlen;
+  const float a2 = p.A[hd] * kLog2e;
+  const float bias = p.dt_bias ? p.dt_bias[hd] : 0.0f;
+  const float Dh = p.D ? p.D[hd] : 0.0f;
+  const int64_t HP = static_cast<int64_t>(H) * kP;
+  const int64_t xb = static_cast<int64_t>(b) * L * HP + static_cast<int64_t>(hd) * kP;
+  const int64_t bcb = static_cast<int64_t>(b) * L * N;
+  const int64_t dtb = static_cast<int64_t>(b) * L * H + hd;
+  const int64_t hsb = (static_cast<int64_t>(b) * H + hd) * kP * N;
+  const int hf = w >> 2;
+  const int pcol = 16 * (w & 3) + lr;
+  const int yt0 = hf, yt1 = 3 - hf;
+  const int r0 = hf * NT;
+
+  // S above the diagonal blocks is read (k-steps of 32 cover it) but never
+  // written: zero it once.
+  for (int i = tid; i < 2 * kQ * QS; i += kThreads) (&sS[0][0])[i] = 0;
+  f32x4 hacc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int n = 16 * (r0 + j) + 4 * lk + v;
+      const float h = p.h0 ? p.h0[hsb + static_cast<int64_t>(pcol) * N + n] : 0.0f;
+      hacc[j][v] = h;
+      split_bf16(h, sHt[0][pcol * CS + n], sHt[1][pcol * CS + n]);
+    }
+  }
+
+  const int64_t nchunks = (L + kQ - 1) / kQ;
+  u32x4 xr, br[NBL], cr[NBL];
+  uint16_t zr[8], dtr = 0;
+  auto fetch = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t t0 = c * kQ;
+    const int len = static_cast<int>(c < nchunks ? (L - t0 < kQ ? L - t0 : kQ) : 0);
+    const uint32_t xbytes = len > 0 ? static_cast<uint32_t>(((len - 1) * HP + kP) * 2) : 0u;
+    const rsrc_t rx = raw_buffer(static_cast<const char*>(p.x) + (xb + t0 * HP) * 2, xbytes);
+    const rsrc_t rz = raw_buffer(p.z ? static_cast<const char*>(p.z) + (xb + t0 * HP) * 2 : nullptr,
+                                 p.z ? xbytes : 0u);
+    const int64_t bo = (bcb + t0 * N) * 2;
+    const uint32_t nbc = static_cast<uint32_t>(len * N * 2);
+    const rsrc_t rb = raw_buffer(static_cast<const char*>(p.B) + bo, nbc);
+    const rsrc_t rc = raw_buffer(static_cast<const char*>(p.C) + bo, nbc);
+    {
+      const int e = tid * 8;  // one 8-element run of x per thread
+      const int t = e / kP, pp = e % kP;
+      xr = __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<uint32_t>((t * HP + pp) * 2), 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      const int e = (i * kThreads + tid) * 8;
+      const uint32_t off = e < kQ * NP ? static_cast<uint32_t>(e * 2) : kOutOfRange;  // N == NP here
+      br[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+      cr[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int t = 16 * ((q >> 2) ? yt1 : yt0) + 4 * lk + (q & 3);
+      zr[q] = buffer_load_bits<true>(rz, static_cast<uint32_t>((t * HP + pcol) * 2));
+    }
+    if (w == 0) {
+      const rsrc_t rd = raw_buffer(static_cast<const char*>(p.dt) + (dtb + t0 * H) * 2,
+                                   len > 0 ? static_cast<uint32_t>(((len - 1) * H + 1) * 2) : 0u);
+      dtr = buffer_load_bits<true>(rd, static_cast<uint32_t>(lane * H * 2));
+    }
+  };
+
+  fetch(0);
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t t0 = c * kQ;
+    const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
+
+    // (1) Stage the chunk: B and C as they come (row-major, exact), x
+    // transposed; the step sizes, their running sums and the weights w.
+    {
+      const int e = tid * 8;
+      const int t = e / kP, pp = e % kP;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sXt[(pp + 2 * j) * QS + t] = static_cast<uint16_t>(xr[j] & 0xffffu);
+        sXt[(pp + 2 * j + 1) * QS + t] = static_cast<uint16_t>(xr[j] >> 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      const int e = (i * kThreads + tid) * 8;
+      if (e >= kQ * NP) break;
+      const int t = e / NP, n = e % NP;
+      *reinterpret_cast<u32x4*>(&sB[t * CS + n]) = br[i];
+      *reinterpret_cast<u32x4*>(&sC[t * CS + n]) = cr[i];
+    }
+    float zg[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) zg[q] = bf16_bits_to_f32(zr[q]);
+    if (w == 0) {
+      float dt = 0.0f;
+      if (lane < len) {
+        const float xv = bf16_bits_to_f32(dtr) + bias;
+        dt = SOFTPLUS ? softplus_f(xv) : xv;
+      }
+      float cs = dt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float up = __shfl_up(cs, o, 64);
+        if (lane >= o) cs += up;
+      }
+      const float cend = __shfl(cs, 63, 64);
+      sDt[lane] = dt;
+      sCs[lane] = cs;
+      sW[lane] = exp2_hw(a2 * (cend - cs)) * dt;
+    }
+    __syncthreads();
+    fetch(c + 1);
+    const float cend = sCs[kQ - 1];
+
+    // (2a) (B o w)^T, split: run (n, s0 .. s0+7) per item.
+#pragma unroll
+    for (int i = 0; i < NBT; ++i) {
+      const int item = i * kThreads + tid;
+      if (item >= NP * (kQ / 8)) break;
+      const int n = item % NP, s0 = 8 * (item / NP);
+      uint16_t hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) split_bf16(bf16_bits_to_f32(sB[(s0 + j) * CS + n]) * sW[s0 + j], hi[j], lo[j]);
+      u32x4 vh, vl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vh[j] = static_cast<uint32_t>(hi[2 * j]) | (static_cast<uint32_t>(hi[2 * j + 1]) << 16);
+        vl[j] = static_cast<uint32_t>(lo[2 * j]) | (static_cast<uint32_t>(lo[2 * j + 1]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(&sBt[0][n * QS + s0]) = vh;
+      *reinterpret_cast<u32x4*>(&sBt[1][n * QS + s0]) = vl;
+    }
+    // (2b) Scores: lower tiles q = w, w + 8; S = G decayed and scaled, split.
+    auto scores = [&](auto nq) __attribute__((always_inline)) {
+      constexpr int NQ = decltype(nq)::value;
+      int ti[NQ], si[NQ];
+      f32x4 g[NQ];
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const int q = w + kWaves * j;
+        ti[j] = q == 0 ? 0 : (q < 3 ? 1 : (q < 6 ? 2 : 3));
+        si[j] = q - ti[j] * (ti[j] + 1) / 2;
+        g[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int k0 = 0; k0 < NP; k0 += 32) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+          g[j] = mfma32(lds8(&sC[(16 * ti[j] + lr) * CS + k0 + 8 * lk]), lds8(&sB[(16 * si[j] + lr) * CS + k0 + 8 * lk]),
+                        g[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const int s = 16 * si[j] + lr;
+        const float css = sCs[s], dts = sDt[s];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = 16 * ti[j] + 4 * lk + v;
+          const float val = g[j][v] * exp2_hw(a2 * (sCs[t] - css)) * dts;
+          split_bf16(t >= s ? val : 0.0f, sS[0][t * QS + s], sS[1][t * QS + s]);
+        }
+      }
+    };
+    if (w < 10 - kWaves) {
+      scores(std::integral_constant<int, 2>{});
+    } else {
+      scores(std::integral_constant<int, 1>{});
+    }
+    // (2c) Readout of the entering state, diag(exp(a cs_t)) C H.
+    const int yt[2] = {yt0, yt1};
+    f32x4 yacc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) yacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k0 = 0; k0 < NP; k0 += 32) {
+      const bf16x8 hh = lds8(&sHt[0][pcol * CS + k0 + 8 * lk]);
+      const bf16x8 hl = lds8(&sHt[1][pcol * CS + k0 + 8 * lk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 cv = lds8(&sC[(16 * yt[j] + lr) * CS + k0 + 8 * lk]);
+        yacc[j] = mfma32(cv, hh, yacc[j]);
+        yacc[j] = mfma32(cv, hl, yacc[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) yacc[j][v] *= exp2_hw(a2 * sCs[16 * yt[j] + 4 * lk + v]);
+    }
+    __syncthreads();  // S and (B o w)^T complete; every wave is done reading H^T
+
+    // (3) Y += S X over s <= t, in k-steps of 32 (tiles 0 and 2 also read
+    // the zero block above the diagonal).
+    auto diag = [&](auto ta, auto tb) __attribute__((always_inline)) {
+      constexpr int TA = decltype(ta)::value, TB = decltype(tb)::value;
+#pragma unroll
+      for (int k0 = 0; k0 < 16 * (TB + 1); k0 += 32) {
+        const bf16x8 xv = lds8(&sXt[pcol * QS + k0 + 8 * lk]);
+        if (k0 < 16 * (TA + 1)) {
+          yacc[0] = mfma32(lds8(&sS[0][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
+          yacc[0] = mfma32(lds8(&sS[1][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
+        }
+        yacc[1] = mfma32(lds8(&sS[0][(16 * TB + lr) * QS + k0 + 8 * lk]), xv, yacc[1]);
+        yacc[1] = mfma32(lds8(&sS[1][(16 * TB + lr) * QS + k0 + 8 * lk]), xv, yacc[1]);
+      }
+    };
+    if (hf == 0) {
+      diag(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+    } else {
+      diag(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+    }
+    // (4) Exit state: exp(a cs_end) H + (B o w)^T X.
+    const float dend = exp2_hw(a2 * cend);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) hacc[j] *= dend;
+#pragma unroll
+    for (int k0 = 0; k0 < kQ; k0 += 32) {
+      const bf16x8 xv = lds8(&sXt[pcol * QS + k0 + 8 * lk]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int n = 16 * (r0 + j) + lr;
+        hacc[j] = mfma32(lds8(&sBt[0][n * QS + k0 + 8 * lk]), xv, hacc[j]);
+        hacc[j] = mfma32(lds8(&sBt[1][n * QS + k0 + 8 * lk]), xv, hacc[j]);
+      }
+    }
+    // (5) Outputs, and the exit state (split) for the next chunk's readout.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = 16 * yt[j] + 4 * lk + v;
+        if (t < len) {
+          const int64_t o = xb + (t0 + t) * HP + pcol;
+          float yv = yacc[j][v] + Dh * bf16_bits_to_f32(sXt[pcol * QS + t]);
+          if (p.z) yv *= silu_f(zg[4 * j + v]);
+          store_elem<BF16_OUT>(p.y, o, yv);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = 16 * (r0 + j) + 4 * lk;
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) split_bf16(hacc[j][v], hi[v], lo[v]);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2*>(&sHt[0][pcol * CS + n]) =
+          u32x2{static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
+                static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
+      *reinterpret_cast<u32x2*>(&sHt[1][pcol * CS + n]) =
+          u32x2{static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16),
+                static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
+    }
+    __syncthreads();  // inputs and the state are free for the next chunk
+  }
+
+  if (p.h_final) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int n = 16 * (r0 + j) + 4 * lk + v;
+        p.h_final[hsb + static_cast<int64_t>(pcol) * N + n] = hacc[j][v];
+      }
+    }
+  }
+}
+
 template <int NP, bool BI, bool BO, bool SP>
 int launch_np(const SsdArgs& a, hipStream_t st) {
   SsdArgs args = a;
@@ -381,6 +705,9 @@ int launch_np(const SsdArgs& a, hipStream_t st) {
   const bool vec = a.headdim == kP && a.dstate == NP;
   const void* fn = vec ? reinterpret_cast<const void*>(&ssd_fwd_kernel<NP, BI, BO, SP, true>)
                        : reinterpret_cast<const void*>(&ssd_fwd_kernel<NP, BI, BO, SP, false>);
+  if constexpr (BI) {
+    if (vec) fn = reinterpret_cast<const void*>(&ssd_bf16_kernel<NP, BO, SP>);
+  }
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.batch * a.nheads)), dim3(kThreads), kargs, 0, st);
 }
 

@@ -80,22 +80,44 @@ def test_ssd_shapes(B, L, H, P, N, dt):
     check(f"ssd {(B, L, H, P, N)} {dt}", inp, "bf16")
 
 
+# bfloat16 inputs with P = 64 and N a power of two >= 32 run on the bfloat16
+# matrix instructions (float32 operands split into two bfloat16 halves).
+BF16_MFMA_SHAPES = [(2, 130, 3, 64, 64), (1, 65, 2, 64, 32), (3, 257, 2, 64, 128), (1, 1, 1, 64, 32)]
+
+
+@pytest.mark.parametrize("B,L,H,P,N", BF16_MFMA_SHAPES)
+def test_ssd_bf16_matrix_path(B, L, H, P, N):
+    inp = synth.make_ssd_inputs(B, L, H, P, N, "bf16", seed=49, stream=4900 + N)
+    h0 = (np.random.default_rng(N + 7).standard_normal((B, H, P, N)) * 0.5).astype(np.float32)
+    check(f"ssd bf16 mfma {(B, L, H, P, N)}", inp, "f32", h0=h0)
+    check(f"ssd bf16 mfma {(B, L, H, P, N)}", inp, "bf16")
+    # its float32 products are taken to about 16 bits: far inside the
+    # bfloat16-input bar, and close to the float32-input one
+    y, hf = run_ssd(to_dev(inp), "f32", h0=upload(h0, "f32"))
+    ref, href, ymag, hmag = oracle_ssd(inp, h0=h0)
+    report(f"ssd bf16 mfma {(B, L, H, P, N)} y at 2e-4", oracle.scaled_error(download(y), ref, ymag), 2e-4)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("opts", [dict(use_D=False), dict(use_z=False), dict(use_bias=False),
                                   dict(softplus=False, use_bias=False)])
-def test_ssd_options(opts):
-    inp = synth.make_ssd_inputs(2, 150, 3, 64, 64, "f32", seed=42, stream=4200)
-    if opts.get("softplus") is False:
+def test_ssd_options(opts, dt):
+    inp = synth.make_ssd_inputs(2, 150, 3, 64, 64, dt, seed=42, stream=4200)
+    if opts.get("softplus") is False:   # positive raw steps, in the storage dtype
         inp = dict(inp)
-        inp["dt"] = np.abs(inp["dt"]) * np.float32(0.05)
-    check(f"ssd options {opts}", inp, "f32", **opts)
+        raw = synth.bf16_bits_to_f32(inp["dt"]) if dt == "bf16" else inp["dt"]
+        small = np.abs(raw) * np.float32(0.05)
+        inp["dt"] = synth.f32_to_bf16_bits(small) if dt == "bf16" else small
+    check(f"ssd options {opts} {dt}", inp, "f32", **opts)
 
 
-def test_ssd_zero_and_strong_decay():
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ssd_zero_and_strong_decay(dt):
     """A = 0 (no decay: running sums over the whole sequence) and A = -200
     (the state forgets within a step) on separate heads."""
-    inp = dict(synth.make_ssd_inputs(1, 300, 3, 64, 32, "f32", seed=43, stream=4300))
+    inp = dict(synth.make_ssd_inputs(1, 300, 3, 64, 32, dt, seed=43, stream=4300))
     inp["A"] = np.array([0.0, -200.0, -1.0], np.float32)
-    check("ssd A in {0, -200, -1}", inp, "f32")
+    check(f"ssd A in {{0, -200, -1}} {dt}", inp, "f32")
 
 
 def test_ssd_empty_sequence_and_in_place_state():
