@@ -58,7 +58,7 @@ const char* ssm_status_string(int status) {
     case SSM_E_ALIGN: return "pointer not aligned as documented";
     case SSM_E_WORKSPACE: return "workspace missing or smaller than ssm_scan_workspace_bytes()";
     case SSM_E_ALIAS: return "an output overlaps an input it may not overlap";
-    case SSM_E_UNSUPPORTED: return "dstate outside the supported range";
+    case SSM_E_UNSUPPORTED: return "size or option outside the supported range";
     case SSM_E_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }

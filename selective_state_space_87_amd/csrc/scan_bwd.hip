@@ -62,28 +62,66 @@ struct ScanBwd {
 
 __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
+// Value of lane (this lane xor M), M in {1, 2, 4, 8}, without a trip through
+// LDS addressing: DPP quad permutes for 1 and 2, a row rotate by 8 (which is
+// xor 8 inside a row of 16), and the swizzle unit's xor mode for 4.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "xor distance 1, 2, 4 or 8");
+  if constexpr (M == 1 || M == 2) {
+    return quad_xor<M>(v);
+  } else if constexpr (M == 8) {
+    return dpp_f<0x128>(v);  // row_ror:8
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x101F));
+  }
+}
+
 // Sum over the wave's 64 lanes of each of G values (G a power of two, at most
 // 64), transposed: on return lane l holds the total of value (l >> (6 - log2 G))
 // ... in the order fixed by the butterfly (see below). Each stage keeps half
 // of the lane's values (the half selected by the lane's bit) and adds the
-// partner's copy of that half.
+// partner's copy of that half. At distances 32 and 16 one lane-swap
+// instruction does a whole stage for a pair: v_permlane32_swap (v_permlane16_
+// swap) of (a, c) exchanges a's upper-half lanes with c's lower-half lanes,
+// after which a + c is, on a lower lane, a plus the partner's a, and on an
+// upper lane, c plus the partner's c.
 template <int G>
 __device__ __forceinline__ float lane_transpose_sum(float (&v)[G], int lane) {
   static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "power of two up to 64");
-  int m = 32;
-  static_for<0, __builtin_ctz(G)>([&](auto st) {
+  constexpr int STAGES = __builtin_ctz(G);
+  static_for<0, STAGES>([&](auto st) {
+    constexpr int M = 32 >> decltype(st)::value;        // xor distance of this stage
     constexpr int H = G >> (decltype(st)::value + 1);  // values kept after this stage
-    const bool upper = (lane & m) != 0;
+    const bool upper = (lane & M) != 0;
 #pragma unroll
     for (int i = 0; i < H; ++i) {
-      const float keep = upper ? v[i + H] : v[i];
-      const float send = upper ? v[i] : v[i + H];
-      v[i] = keep + __shfl_xor(send, m);
+      if constexpr (M >= 16) {
+        const uint32_t a = __float_as_uint(v[i]), c = __float_as_uint(v[i + H]);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 r;
+        if constexpr (M == 32) {
+          r = __builtin_amdgcn_permlane32_swap(a, c, false, false);
+        } else {
+          r = __builtin_amdgcn_permlane16_swap(a, c, false, false);
+        }
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      } else {
+        const float keep = upper ? v[i + H] : v[i];
+        const float send = upper ? v[i] : v[i + H];
+        v[i] = keep + lane_xor<M>(send);
+      }
     }
-    m >>= 1;
   });
   float r = v[0];
-  for (; m >= 1; m >>= 1) r += __shfl_xor(r, m);
+  static_for<STAGES, 6>([&](auto st) {
+    constexpr int M = 32 >> decltype(st)::value;
+    if constexpr (M >= 16) {
+      r += __shfl_xor(r, M);
+    } else {
+      r += lane_xor<M>(r);
+    }
+  });
   return r;
 }
 
