@@ -285,14 +285,16 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       dpv[t] = q.z;
       uvv[t] = q.w;
     }
-    float av[T][S], ahv[T][S], hs[T][S];
+    float av[T][S], ahv[T][S], hs[T][S], bvs[T][S], cvs[T][S];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       float acc = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         float bval, cval;
-        bc_of(w * S + s, t, bval, cval);
+        bc_of(w * S + s, t, bval, cval);   // kept for the adjoint below
+        bvs[t][s] = bval;
+        cvs[t][s] = cval;
         av[t][s] = exp2_hw(dtv[t] * A2[s]);
         ahv[t][s] = av[t][s] * hh[s];
         hh[s] = fmaf(dtu[t], bval, ahv[t][s]);
@@ -307,8 +309,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       float ddt_acc = 0.0f, du_acc = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        float bval, cval;
-        bc_of(w * S + s, t, bval, cval);
+        const float bval = bvs[t][s], cval = cvs[t][s];
         const float lam = fmaf(dpv[t], cval, mu[s]);
         gv[t * S + s] = lam * dtu[t];                 // -> dB (sum over channels)
         gv[T * S + t * S + s] = dpv[t] * hs[t][s];    // -> dC (sum over channels)
