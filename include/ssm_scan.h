@@ -70,7 +70,7 @@ extern "C" {
 #define SSM_E_ALIGN 4       /* pointer not aligned as documented                 */
 #define SSM_E_WORKSPACE 5   /* workspace missing or smaller than required        */
 #define SSM_E_ALIAS 6       /* an output overlaps an input it may not overlap    */
-#define SSM_E_UNSUPPORTED 7 /* dstate, seqlen or dim beyond the supported range  */
+#define SSM_E_UNSUPPORTED 7 /* a size or an option outside the supported range */
 #define SSM_E_HIP 8         /* the HIP runtime reported an error at launch       */
 
 /* Bits of the `flags` argument of the scan and decode entry points. Any other

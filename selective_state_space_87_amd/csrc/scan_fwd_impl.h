@@ -4,18 +4,23 @@
 // Recurrence ("从 Transformer 到 Mamba", ybb.press, sections 3.1 and 5):
 //   dt = softplus(delta + bias); h[n] = exp(dt*A[n]) h[n] + dt*B[n]*u;
 //   y = (sum_n C[n] h[n] + D u) * silu(z)      (gate as in section 5's block)
+// With ZOH the input term is k*B[n]*u, k = (exp(dt*A[n]) - 1) / A[n] (the
+// zero-order hold of "Mamba新突破", ruibaoantu.com, section 二.3).
 //
 // Work decomposition. A block owns 64 channels (b, d0..d0+63) of one batch
 // row (and one sequence chunk) and all N states of each: lane l of every wave
 // is channel d0+l, and wave w owns states n = w*S .. w*S+S-1, kept in VGPRs
-// for the whole chunk; every state chain is walked once, in order. N = 16
-// runs two states per lane on eight waves; smaller N one state per wave.
+// for the whole chunk; every state chain is walked once, in order. Padded N
+// up to 8 runs one state per wave; 16 two states per lane on eight waves; 32
+// two on sixteen; 64 and 128 run N/8 per lane on eight waves.
 //
 // Time is processed in tiles of T steps (8 at N = 16). Per tile:
 //   * recurrence: each wave advances its states through the tile. B[t, n] and
 //     C[t, n] are the same for every lane of the wave: a pre-pass packs them
 //     per state, time-major, and the wave reads a tile of them with scalar
-//     loads into SGPRs. The wave's share of the readout, sum_s C h, goes to an
+//     loads into SGPRs (from 64 padded states on, where they no longer fit,
+//     the block stages them through LDS instead and every lane reads the
+//     same entry). The wave's share of the readout, sum_s C h, goes to an
 //     LDS ring (XOR-swizzled: conflict-free writes and 16-byte reads).
 //   * cooperative: the block finishes an earlier tile (sum of the partial
 //     readouts in a fixed order, + D u, * silu(z), store) and prepares later
