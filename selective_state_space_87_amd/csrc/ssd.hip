@@ -56,6 +56,24 @@ constexpr int kXS = kP + 16;
 constexpr int kSS = kQ + 4;
 constexpr int kHS = kP + 20;
 
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP: shifts by 1, 2,
+// 4 and 8 inside each row of 16 lanes (lanes without a source add 0), then
+// the last lane of each row broadcast into the next row (row_bcast:15) and
+// lane 31 into the upper two rows (row_bcast:31).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_src(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+  v += dpp_src<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_src<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_src<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_src<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_src<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_src<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // D (16x16) += A (16x4) B (4x16). Lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16]; element v of the result is D[4 (l / 16) + v][l % 16].
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -239,13 +257,8 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
         const float xr = bits_to_f32<BF16_IN>(stg.dtr) + bias;
         dt = SOFTPLUS ? softplus_f(xr) : xr;
       }
-      float cs = dt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float up = __shfl_up(cs, o, 64);
-        if (lane >= o) cs += up;
-      }
-      const float cend = __shfl(cs, 63, 64);
+      const float cs = wave_inclusive_sum(dt);
+      const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
       sDt[lane] = dt;
       sCs[lane] = cs;
       sW[lane] = exp2_hw(a2 * (cend - cs)) * dt;
@@ -528,13 +541,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
         const float xv = bf16_bits_to_f32(dtr) + bias;
         dt = SOFTPLUS ? softplus_f(xv) : xv;
       }
-      float cs = dt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float up = __shfl_up(cs, o, 64);
-        if (lane >= o) cs += up;
-      }
-      const float cend = __shfl(cs, 63, 64);
+      const float cs = wave_inclusive_sum(dt);
+      const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
       sDt[lane] = dt;
       sCs[lane] = cs;
       sW[lane] = exp2_hw(a2 * (cend - cs)) * dt;
