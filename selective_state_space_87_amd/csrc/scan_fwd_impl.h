@@ -452,10 +452,14 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     constexpr int Q = 1 - P;
     float gp[IT][GN][GW];
     if constexpr (MODE == kCheckpoint) {
-      if (ch_ok) {
-        float* ck = p.hsum + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
+      // Branch-free through a descriptor over this wave's rows of tile k
+      // (lanes beyond d are dropped by the buffer unit): a branch here would
+      // leave the wait analysis unable to count the memory queue in order.
+      const rsrc_t rck = raw_buffer(p.hsum + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm,
+                                    static_cast<uint32_t>(S * Dm * 4));
 #pragma unroll
-        for (int s = 0; s < S; ++s) ck[static_cast<int64_t>(s) * Dm] = h[s];
+      for (int s = 0; s < S; ++s) {
+        buffer_store_f32<false>(h[s], rck, ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kLaneOut);
       }
     }
     if constexpr (decltype(late)::value) {
