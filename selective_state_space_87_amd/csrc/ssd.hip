@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t sC[kQ * CS];
   __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * CS];
   __shared__ __attribute__((aligned(16))) uint16_t sBt[2][NP * QS];  // (B o w)^T, hi and lo
-  __shared__ __attribute__((aligned(16))) uint16_t sXt[kP * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t sXt[2][kP * QS];  // x^T, by chunk parity
   __shared__ __attribute__((aligned(16))) uint16_t sS[2][kQ * QS];   // S, hi and lo
   __shared__ __attribute__((aligned(16))) uint16_t sHt[2][kP * CS];  // H^T, hi and lo
   __shared__ float sCs[kQ];
@@ -508,20 +508,24 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
     }
   };
 
-  fetch(0);
-  for (int64_t c = 0; c < nchunks; ++c) {
+  // Stage chunk c from the fetched registers: B and C as they come
+  // (row-major, exact), x transposed (into the buffer of c's parity), the
+  // gate values, and (wave 0) the step sizes, their running sums and the
+  // weights w. B, C and the step arrays are dead once a chunk's first half
+  // is done, so the next chunk is staged right after the middle barrier,
+  // while the current one finishes: two barriers per chunk.
+  float zg[8];
+  auto stage = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * kQ;
     const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
-
-    // (1) Stage the chunk: B and C as they come (row-major, exact), x
-    // transposed; the step sizes, their running sums and the weights w.
+    uint16_t* xt = sXt[c & 1];
     {
       const int e = tid * 8;
       const int t = e / kP, pp = e % kP;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sXt[(pp + 2 * j) * QS + t] = static_cast<uint16_t>(xr[j] & 0xffffu);
-        sXt[(pp + 2 * j + 1) * QS + t] = static_cast<uint16_t>(xr[j] >> 16);
+        xt[(pp + 2 * j) * QS + t] = static_cast<uint16_t>(xr[j] & 0xffffu);
+        xt[(pp + 2 * j + 1) * QS + t] = static_cast<uint16_t>(xr[j] >> 16);
       }
     }
 #pragma unroll
@@ -532,7 +536,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       *reinterpret_cast<u32x4*>(&sB[t * CS + n]) = br[i];
       *reinterpret_cast<u32x4*>(&sC[t * CS + n]) = cr[i];
     }
-    float zg[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) zg[q] = bf16_bits_to_f32(zr[q]);
     if (w == 0) {
@@ -542,13 +545,23 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
         dt = SOFTPLUS ? softplus_f(xv) : xv;
       }
       const float cs = wave_inclusive_sum(dt);
-      const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
+      const float ce = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
       sDt[lane] = dt;
       sCs[lane] = cs;
-      sW[lane] = exp2_hw(a2 * (cend - cs)) * dt;
+      sW[lane] = exp2_hw(a2 * (ce - cs)) * dt;
     }
+  };
+
+  if (nchunks > 0) {
+    fetch(0);
+    stage(0);
     __syncthreads();
-    fetch(c + 1);
+    fetch(1);
+  }
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t t0 = c * kQ;
+    const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
+    const uint16_t* xt = sXt[c & 1];
     const float cend = sCs[kQ - 1];
 
     // (2a) (B o w)^T, split: run (n, s0 .. s0+7) per item.
@@ -635,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       constexpr int TA = decltype(ta)::value, TB = decltype(tb)::value;
 #pragma unroll
       for (int k0 = 0; k0 < 16 * (TB + 1); k0 += 32) {
-        const bf16x8 xv = lds8(&sXt[pcol * QS + k0 + 8 * lk]);
+        const bf16x8 xv = lds8(&xt[pcol * QS + k0 + 8 * lk]);
         if (k0 < 16 * (TA + 1)) {
           yacc[0] = mfma32(lds8(&sS[0][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
           yacc[0] = mfma32(lds8(&sS[1][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
@@ -655,7 +668,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
     for (int j = 0; j < NT; ++j) hacc[j] *= dend;
 #pragma unroll
     for (int k0 = 0; k0 < kQ; k0 += 32) {
-      const bf16x8 xv = lds8(&sXt[pcol * QS + k0 + 8 * lk]);
+      const bf16x8 xv = lds8(&xt[pcol * QS + k0 + 8 * lk]);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const int n = 16 * (r0 + j) + lr;
@@ -671,7 +684,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
         const int t = 16 * yt[j] + 4 * lk + v;
         if (t < len) {
           const int64_t o = xb + (t0 + t) * HP + pcol;
-          float yv = yacc[j][v] + Dh * bf16_bits_to_f32(sXt[pcol * QS + t]);
+          float yv = yacc[j][v] + Dh * bf16_bits_to_f32(xt[pcol * QS + t]);
           if (p.z) yv *= silu_f(zg[4 * j + v]);
           store_elem<BF16_OUT>(p.y, o, yv);
         }
@@ -691,7 +704,9 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
           u32x2{static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16),
                 static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
     }
-    __syncthreads();  // inputs and the state are free for the next chunk
+    if (c + 1 < nchunks) stage(c + 1);
+    __syncthreads();  // the next chunk is staged and the state written
+    fetch(c + 2);
   }
 
   if (p.h_final) {
