@@ -157,3 +157,25 @@ def test_ssd_mamba2_layer_sampled_heads():
     inp = synth.make_ssd_inputs(4, 8192, 64, 64, 128, "bf16", seed=0, stream=4800)
     check("ssd (4,8192,64,64,128) bf16 sampled heads", inp, "f32", heads=[0, 31, 63])
     check("ssd (4,8192,64,64,128) bf16-out sampled heads", inp, "bf16", heads=[5])
+
+
+def test_ssd_bf16_path_in_place_state_and_determinism():
+    """The bfloat16 matrix path (P = 64, N = 128): h_final written over h0,
+    results bitwise repeatable, and two calls joined by the state."""
+    inp = synth.make_ssd_inputs(2, 200, 3, 64, 128, "bf16", seed=50, stream=5000)
+    d = to_dev(inp)
+    h0n = (np.random.default_rng(51).standard_normal((2, 3, 64, 128)) * 0.5).astype(np.float32)
+    h = upload(h0n, "f32")
+    y, _ = run_ssd(d, h0=h, h_final=h)
+    ref, href, ymag, hmag = oracle_ssd(inp, h0=h0n)
+    report("ssd bf16 in place y", oracle.scaled_error(download(y), ref, ymag), tol_for("bf16", "f32"))
+    report("ssd bf16 in place h", oracle.scaled_error(download(h), href, hmag), tol_for("bf16", "f32"))
+    y1, h1 = run_ssd(d, h0=upload(h0n, "f32"))
+    y2, h2 = run_ssd(d, h0=upload(h0n, "f32"))
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    first = {k: (v[:, :77].contiguous() if k in ("x", "dt", "B", "C", "z") else v) for k, v in d.items()}
+    rest = {k: (v[:, 77:].contiguous() if k in ("x", "dt", "B", "C", "z") else v) for k, v in d.items()}
+    ya, ha = run_ssd(first, h0=upload(h0n, "f32"))
+    yb, hb = run_ssd(rest, h0=ha)
+    report("ssd bf16 split y", oracle.scaled_error(download(torch.cat([ya, yb], 1)), ref, ymag), tol_for("bf16", "f32"))
+    report("ssd bf16 split h", oracle.scaled_error(download(hb), href, hmag), tol_for("bf16", "f32"))
