@@ -265,3 +265,26 @@ def test_ssd_validation(lib):
     assert ssd(lib, hf=9 * P + 4) == E_ALIAS         # partial overlap with h0
     assert ssd(lib, H=0, x=None, A=None, y=None) == OK
     assert ssd(lib, B=1, H=1 << 17, P=64) == E_UNSUPPORTED   # H * P beyond 2^23
+
+
+def test_header_is_plain_c():
+    """The ABI header compiles as C99 (and C++17) on its own, with warnings as errors."""
+    import shutil
+    import subprocess
+    for cc, args in (("gcc", ["-std=c99", "-x", "c"]), ("g++", ["-std=c++17", "-x", "c++"])):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Wextra", "-pedantic", "-Werror", *args, HEADER],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more, it says so and exits 2
+    before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout
