@@ -412,6 +412,12 @@ __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// Element (p, s) of x^T [P][Q + 8]. The 8-element runs of s are permuted per
+// 16 rows of p (run index XOR (p / 16) mod 4): a wave's transposing stores,
+// 8 rows 8 apart, then fall on distinct banks, while an operand read (16
+// consecutive rows, one run each) keeps its conflict-free pattern.
+__device__ __forceinline__ int xt_at(int pp, int s) { return pp * (kQ + 8) + (s ^ (8 * ((pp >> 4) & 3))); }
+
 __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
   hi = f32_to_bf16_bits(v);
   lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
@@ -421,7 +427,13 @@ template <int NP, bool BF16_OUT, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   constexpr int CS = NP + 8;     // row stride of C, B [Q][NP] and H^T [P][NP] (elements)
   constexpr int QS = kQ + 8;     // row stride of x^T [P][Q], S [Q][Q], (B o w)^T [NP][Q]
-  constexpr int NT = NP / 32;    // state row tiles per wave
+  // The exit state's 16 x 16 tiles (NP / 16 along n, 4 along p) are dealt
+  // to the waves in blocks of SN x SPC; a block reads SN + SPC operand runs
+  // per k-step for SN x SPC products, so blocks are square where they can be.
+  constexpr int SN = NP >= 64 ? 2 : 1;
+  constexpr int SPC = NP == 128 ? 2 : 1;
+  constexpr int NGRP = NP / 16 / SN;
+  static_assert(NGRP * (4 / SPC) == kWaves, "state tiles must cover the waves");
   constexpr int NBL = (kQ * NP + kThreads * 8 - 1) / (kThreads * 8);  // B (and C) loads per thread
   constexpr int NBT = (NP * (kQ / 8) + kThreads - 1) / kThreads;      // (B o w)^T runs per thread
   __shared__ __attribute__((aligned(16))) uint16_t sC[kQ * CS];
@@ -453,20 +465,21 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   const int hf = w >> 2;
   const int pcol = 16 * (w & 3) + lr;
   const int yt0 = hf, yt1 = 3 - hf;
-  const int r0 = hf * NT;
+  const int nb = SN * (w % NGRP), pb = SPC * (w / NGRP);  // this wave's state block
 
   // S above the diagonal blocks is read (k-steps of 32 cover it) but never
   // written: zero it once.
   for (int i = tid; i < 2 * kQ * QS; i += kThreads) (&sS[0][0])[i] = 0;
-  f32x4 hacc[NT];
+  f32x4 hacc[SN * SPC];  // tile (jn, jp) at jn * SPC + jp
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
+  for (int j = 0; j < SN * SPC; ++j) {
+    const int pc = 16 * (pb + j % SPC) + lr;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int n = 16 * (r0 + j) + 4 * lk + v;
-      const float h = p.h0 ? p.h0[hsb + static_cast<int64_t>(pcol) * N + n] : 0.0f;
+      const int n = 16 * (nb + j / SPC) + 4 * lk + v;
+      const float h = p.h0 ? p.h0[hsb + static_cast<int64_t>(pc) * N + n] : 0.0f;
       hacc[j][v] = h;
-      split_bf16(h, sHt[0][pcol * CS + n], sHt[1][pcol * CS + n]);
+      split_bf16(h, sHt[0][pc * CS + n], sHt[1][pc * CS + n]);
     }
   }
 
@@ -501,11 +514,12 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       const int t = 16 * ((q >> 2) ? yt1 : yt0) + 4 * lk + (q & 3);
       zr[q] = buffer_load_bits<true>(rz, static_cast<uint32_t>((t * HP + pcol) * 2));
     }
-    if (w == 0) {
-      const rsrc_t rd = raw_buffer(static_cast<const char*>(p.dt) + (dtb + t0 * H) * 2,
-                                   len > 0 ? static_cast<uint32_t>(((len - 1) * H + 1) * 2) : 0u);
-      dtr = buffer_load_bits<true>(rd, static_cast<uint32_t>(lane * H * 2));
-    }
+    // Every wave loads the step sizes (wave 0 uses them): memory operations
+    // outside branches keep the waits before the staging counted exactly,
+    // so the output stores of the chunk stay in flight across it.
+    const rsrc_t rd = raw_buffer(static_cast<const char*>(p.dt) + (dtb + t0 * H) * 2,
+                                 len > 0 ? static_cast<uint32_t>(((len - 1) * H + 1) * 2) : 0u);
+    dtr = buffer_load_bits<true>(rd, static_cast<uint32_t>(lane * H * 2));
   };
 
   // Stage chunk c from the fetched registers: B and C as they come
@@ -524,8 +538,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       const int t = e / kP, pp = e % kP;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        xt[(pp + 2 * j) * QS + t] = static_cast<uint16_t>(xr[j] & 0xffffu);
-        xt[(pp + 2 * j + 1) * QS + t] = static_cast<uint16_t>(xr[j] >> 16);
+        xt[xt_at(pp + 2 * j, t)] = static_cast<uint16_t>(xr[j] & 0xffffu);
+        xt[xt_at(pp + 2 * j + 1, t)] = static_cast<uint16_t>(xr[j] >> 16);
       }
     }
 #pragma unroll
@@ -648,7 +662,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       constexpr int TA = decltype(ta)::value, TB = decltype(tb)::value;
 #pragma unroll
       for (int k0 = 0; k0 < 16 * (TB + 1); k0 += 32) {
-        const bf16x8 xv = lds8(&xt[pcol * QS + k0 + 8 * lk]);
+        const bf16x8 xv = lds8(&xt[xt_at(pcol, k0 + 8 * lk)]);
         if (k0 < 16 * (TA + 1)) {
           yacc[0] = mfma32(lds8(&sS[0][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
           yacc[0] = mfma32(lds8(&sS[1][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
@@ -665,42 +679,52 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
     // (4) Exit state: exp(a cs_end) H + (B o w)^T X.
     const float dend = exp2_hw(a2 * cend);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) hacc[j] *= dend;
+    for (int j = 0; j < SN * SPC; ++j) hacc[j] *= dend;
 #pragma unroll
     for (int k0 = 0; k0 < kQ; k0 += 32) {
-      const bf16x8 xv = lds8(&xt[pcol * QS + k0 + 8 * lk]);
+      bf16x8 xv[SPC];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int n = 16 * (r0 + j) + lr;
-        hacc[j] = mfma32(lds8(&sBt[0][n * QS + k0 + 8 * lk]), xv, hacc[j]);
-        hacc[j] = mfma32(lds8(&sBt[1][n * QS + k0 + 8 * lk]), xv, hacc[j]);
+      for (int jp = 0; jp < SPC; ++jp) xv[jp] = lds8(&xt[xt_at(16 * (pb + jp) + lr, k0 + 8 * lk)]);
+#pragma unroll
+      for (int jn = 0; jn < SN; ++jn) {
+        const int n = 16 * (nb + jn) + lr;
+        const bf16x8 bh = lds8(&sBt[0][n * QS + k0 + 8 * lk]);
+        const bf16x8 bl = lds8(&sBt[1][n * QS + k0 + 8 * lk]);
+#pragma unroll
+        for (int jp = 0; jp < SPC; ++jp) {
+          hacc[jn * SPC + jp] = mfma32(bh, xv[jp], hacc[jn * SPC + jp]);
+          hacc[jn * SPC + jp] = mfma32(bl, xv[jp], hacc[jn * SPC + jp]);
+        }
       }
     }
-    // (5) Outputs, and the exit state (split) for the next chunk's readout.
+    // (5) Outputs (rows past the sequence masked by the buffer's range, no
+    // branch), and the exit state (split) for the next chunk's readout.
+    {
+      constexpr int OB = BF16_OUT ? 2 : 4;
+      const rsrc_t ry = raw_buffer(static_cast<char*>(p.y) + (xb + t0 * HP) * OB,
+                                   static_cast<uint32_t>(((len - 1) * HP + kP) * OB));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = 16 * yt[j] + 4 * lk + v;
-        if (t < len) {
-          const int64_t o = xb + (t0 + t) * HP + pcol;
-          float yv = yacc[j][v] + Dh * bf16_bits_to_f32(xt[pcol * QS + t]);
+        for (int v = 0; v < 4; ++v) {
+          const int t = 16 * yt[j] + 4 * lk + v;
+          float yv = yacc[j][v] + Dh * bf16_bits_to_f32(xt[xt_at(pcol, t)]);
           if (p.z) yv *= silu_f(zg[4 * j + v]);
-          store_elem<BF16_OUT>(p.y, o, yv);
+          buffer_store_f32<BF16_OUT>(yv, ry, t < len ? static_cast<uint32_t>((t * HP + pcol) * OB) : kOutOfRange);
         }
       }
     }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int n = 16 * (r0 + j) + 4 * lk;
+    for (int j = 0; j < SN * SPC; ++j) {
+      const int n = 16 * (nb + j / SPC) + 4 * lk, pc = 16 * (pb + j % SPC) + lr;
       uint16_t hi[4], lo[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) split_bf16(hacc[j][v], hi[v], lo[v]);
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      *reinterpret_cast<u32x2*>(&sHt[0][pcol * CS + n]) =
+      *reinterpret_cast<u32x2*>(&sHt[0][pc * CS + n]) =
           u32x2{static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
                 static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
-      *reinterpret_cast<u32x2*>(&sHt[1][pcol * CS + n]) =
+      *reinterpret_cast<u32x2*>(&sHt[1][pc * CS + n]) =
           u32x2{static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16),
                 static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
     }
@@ -711,11 +735,12 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
 
   if (p.h_final) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+    for (int j = 0; j < SN * SPC; ++j) {
+      const int pc = 16 * (pb + j % SPC) + lr;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int n = 16 * (r0 + j) + 4 * lk + v;
-        p.h_final[hsb + static_cast<int64_t>(pcol) * N + n] = hacc[j][v];
+        const int n = 16 * (nb + j / SPC) + 4 * lk + v;
+        p.h_final[hsb + static_cast<int64_t>(pc) * N + n] = hacc[j][v];
       }
     }
   }
