@@ -442,9 +442,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t sXt[2][kP * QS];  // x^T, by chunk parity
   __shared__ __attribute__((aligned(16))) uint16_t sS[2][kQ * QS];   // S, hi and lo
   __shared__ __attribute__((aligned(16))) uint16_t sHt[2][kP * CS];  // H^T, hi and lo
-  __shared__ float sCs[kQ];
-  __shared__ float sDt[kQ];
+  __shared__ __attribute__((aligned(16))) float sCs[kQ];
+  __shared__ __attribute__((aligned(16))) float sDt[kQ];
   __shared__ float sW[kQ];
+  __shared__ __attribute__((aligned(16))) float sYw[kWaves][32 * 16];  // each wave's two Y tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -465,6 +466,11 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   const int hf = w >> 2;
   const int pcol = 16 * (w & 3) + lr;
   const int yt0 = hf, yt1 = 3 - hf;
+  // Output layout: lane -> row orow of the wave's two Y tiles (sequence
+  // position ot) and 8 consecutive channels from op.
+  const int orow = lane >> 1;
+  const int ot = 16 * ((orow >> 4) ? yt1 : yt0) + (orow & 15);
+  const int op = 16 * (w & 3) + 8 * (lane & 1);
   const int nb = SN * (w % NGRP), pb = SPC * (w / NGRP);  // this wave's state block
 
   // S above the diagonal blocks is read (k-steps of 32 cover it) but never
@@ -484,8 +490,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   }
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
-  u32x4 xr, br[NBL], cr[NBL];
-  uint16_t zr[8], dtr = 0;
+  u32x4 xr, br[NBL], cr[NBL], zr;
+  uint16_t dtr = 0;
   auto fetch = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * kQ;
     const int len = static_cast<int>(c < nchunks ? (L - t0 < kQ ? L - t0 : kQ) : 0);
@@ -509,11 +515,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       br[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
       cr[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int t = 16 * ((q >> 2) ? yt1 : yt0) + 4 * lk + (q & 3);
-      zr[q] = buffer_load_bits<true>(rz, static_cast<uint32_t>((t * HP + pcol) * 2));
-    }
+    // the gate values of this lane's outputs: 8 channels of row ot
+    zr = __builtin_amdgcn_raw_buffer_load_b128(rz, static_cast<uint32_t>((ot * HP + op) * 2), 0, 0);
     // Every wave loads the step sizes (wave 0 uses them): memory operations
     // outside branches keep the waits before the staging counted exactly,
     // so the output stores of the chunk stay in flight across it.
@@ -528,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   // weights w. B, C and the step arrays are dead once a chunk's first half
   // is done, so the next chunk is staged right after the middle barrier,
   // while the current one finishes: two barriers per chunk.
-  float zg[8];
+  u32x4 zq;
   auto stage = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * kQ;
     const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
@@ -550,8 +553,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       *reinterpret_cast<u32x4*>(&sB[t * CS + n]) = br[i];
       *reinterpret_cast<u32x4*>(&sC[t * CS + n]) = cr[i];
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) zg[q] = bf16_bits_to_f32(zr[q]);
+    zq = zr;
     if (w == 0) {
       float dt = 0.0f;
       if (lane < len) {
@@ -597,6 +599,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       *reinterpret_cast<u32x4*>(&sBt[1][n * QS + s0]) = vl;
     }
     // (2b) Scores: lower tiles q = w, w + 8; S = G decayed and scaled, split.
+    // Computed transposed, G^T = B C^T, so that a lane holds 4 consecutive s
+    // of one row t of S and writes them as one 8-byte run per half.
     auto scores = [&](auto nq) __attribute__((always_inline)) {
       constexpr int NQ = decltype(nq)::value;
       int ti[NQ], si[NQ];
@@ -612,20 +616,31 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       for (int k0 = 0; k0 < NP; k0 += 32) {
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
-          g[j] = mfma32(lds8(&sC[(16 * ti[j] + lr) * CS + k0 + 8 * lk]), lds8(&sB[(16 * si[j] + lr) * CS + k0 + 8 * lk]),
+          g[j] = mfma32(lds8(&sB[(16 * si[j] + lr) * CS + k0 + 8 * lk]), lds8(&sC[(16 * ti[j] + lr) * CS + k0 + 8 * lk]),
                         g[j]);
         }
       }
+      // g[j][v] = C_t . B_s at t = 16 ti + lr, s = 16 si + 4 lk + v
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
-        const int s = 16 * si[j] + lr;
-        const float css = sCs[s], dts = sDt[s];
+        const int t = 16 * ti[j] + lr, s0 = 16 * si[j] + 4 * lk;
+        const float cst = sCs[t];
+        const f32x4 css = *reinterpret_cast<const f32x4*>(&sCs[s0]);
+        const f32x4 dts = *reinterpret_cast<const f32x4*>(&sDt[s0]);
+        uint16_t hi[4], lo[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int t = 16 * ti[j] + 4 * lk + v;
-          const float val = g[j][v] * exp2_hw(a2 * (sCs[t] - css)) * dts;
-          split_bf16(t >= s ? val : 0.0f, sS[0][t * QS + s], sS[1][t * QS + s]);
+          const float val = g[j][v] * exp2_hw(a2 * (cst - css[v])) * dts[v];
+          // D x enters S X as D on the diagonal of S
+          split_bf16(t > s0 + v ? val : (t == s0 + v ? val + Dh : 0.0f), hi[v], lo[v]);
         }
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2*>(&sS[0][t * QS + s0]) =
+            u32x2{static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
+                  static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
+        *reinterpret_cast<u32x2*>(&sS[1][t * QS + s0]) =
+            u32x2{static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16),
+                  static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
       }
     };
     if (w < 10 - kWaves) {
@@ -697,21 +712,51 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
         }
       }
     }
-    // (5) Outputs (rows past the sequence masked by the buffer's range, no
-    // branch), and the exit state (split) for the next chunk's readout.
+    // (5) Outputs. Each wave passes its two Y tiles through its own LDS
+    // scratch so that a lane ends with 8 consecutive channels of one row:
+    // the gate values come in and y goes out as 16-byte runs (rows past the
+    // sequence masked by the buffer's range, no branch). Then the exit state
+    // (split) for the next chunk's readout.
     {
-      constexpr int OB = BF16_OUT ? 2 : 4;
-      const rsrc_t ry = raw_buffer(static_cast<char*>(p.y) + (xb + t0 * HP) * OB,
-                                   static_cast<uint32_t>(((len - 1) * HP + kP) * OB));
+      float* sy = sYw[w];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int t = 16 * yt[j] + 4 * lk + v;
-          float yv = yacc[j][v] + Dh * bf16_bits_to_f32(xt[xt_at(pcol, t)]);
-          if (p.z) yv *= silu_f(zg[4 * j + v]);
-          buffer_store_f32<BF16_OUT>(yv, ry, t < len ? static_cast<uint32_t>((t * HP + pcol) * OB) : kOutOfRange);
+        for (int v = 0; v < 4; ++v) sy[(16 * j + 4 * lk + v) * 16 + lr] = yacc[j][v];
+      }
+      // other lanes' writes of this wave: LDS executes a wave's accesses in
+      // order; the fences keep the compiler from reordering across lanes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const f32x4 ya = *reinterpret_cast<const f32x4*>(&sy[orow * 16 + 8 * (lane & 1)]);
+      const f32x4 yb = *reinterpret_cast<const f32x4*>(&sy[orow * 16 + 8 * (lane & 1) + 4]);
+      float yv[8] = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
+      if (p.z) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t zw = zq[q >> 1];
+          yv[q] *= silu_f(__uint_as_float((q & 1) ? (zw & 0xffff0000u) : (zw << 16)));
         }
+      }
+      constexpr int OB = BF16_OUT ? 2 : 4;
+      const rsrc_t ry = raw_buffer(static_cast<char*>(p.y) + (xb + t0 * HP) * OB,
+                                   static_cast<uint32_t>(((len - 1) * HP + kP) * OB));
+      const bool in = ot < len;
+      const uint32_t off = static_cast<uint32_t>((ot * HP + op) * OB);
+      if constexpr (BF16_OUT) {
+        u32x4 pk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pk[j] = static_cast<uint32_t>(f32_to_bf16_bits(yv[2 * j])) |
+                  (static_cast<uint32_t>(f32_to_bf16_bits(yv[2 * j + 1])) << 16);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(pk, ry, in ? off : kOutOfRange, 0, 0);
+      } else {
+        const u32x4 lo4 = {__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]), __float_as_uint(yv[3])};
+        const u32x4 hi4 = {__float_as_uint(yv[4]), __float_as_uint(yv[5]), __float_as_uint(yv[6]), __float_as_uint(yv[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(lo4, ry, in ? off : kOutOfRange, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(hi4, ry, in ? off + 16u : kOutOfRange, 0, 0);
       }
     }
 #pragma unroll
