@@ -401,6 +401,11 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
 // Operands are read as 16-byte runs of 8 consecutive k: every LDS array is
 // laid out with the contraction index contiguous (x and the w-scaled B are
 // stored transposed), rows padded by 8 elements (16 bytes).
+// With N >= 64 the block has sixteen waves (four per SIMD, at most 128
+// registers each), so that one wave's LDS and transcendental latencies hide
+// behind three others' work; the LDS arrays (up to 157 KiB at N = 128) allow
+// one block per compute unit either way. D x enters the diagonal product as D
+// added to the diagonal of S.
 // D (16x16) += A (16x32) B (32x16) on bfloat16: lane l supplies
 // A[l % 16][8 (l / 16) .. +7] and B[8 (l / 16) .. +7][l % 16]; the result is
 // laid out as for the float32 instruction.
@@ -423,19 +428,29 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
 }
 
-template <int NP, bool BF16_OUT, bool SOFTPLUS>
-__global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
+template <int NP, int WV, bool BF16_OUT, bool SOFTPLUS>
+__global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
+  constexpr int NTH = 64 * WV;   // threads of the block (WV waves: 8, or 16 for NP >= 64)
   constexpr int CS = NP + 8;     // row stride of C, B [Q][NP] and H^T [P][NP] (elements)
   constexpr int QS = kQ + 8;     // row stride of x^T [P][Q], S [Q][Q], (B o w)^T [NP][Q]
+  // Y (and its readout) is 4 x 4 tiles of 16 x 16 (t by p); a wave takes YW
+  // tiles of one column p: t-tiles {w/4, 3 - w/4} with 8 waves (equal
+  // shares of the triangular S X), t-tile w/4 with 16.
+  constexpr int YW = 16 / WV;
   // The exit state's 16 x 16 tiles (NP / 16 along n, 4 along p) are dealt
   // to the waves in blocks of SN x SPC; a block reads SN + SPC operand runs
   // per k-step for SN x SPC products, so blocks are square where they can be.
-  constexpr int SN = NP >= 64 ? 2 : 1;
+  constexpr int SN = (WV == 8 && NP >= 64) ? 2 : 1;
   constexpr int SPC = NP == 128 ? 2 : 1;
   constexpr int NGRP = NP / 16 / SN;
-  static_assert(NGRP * (4 / SPC) == kWaves, "state tiles must cover the waves");
-  constexpr int NBL = (kQ * NP + kThreads * 8 - 1) / (kThreads * 8);  // B (and C) loads per thread
-  constexpr int NBT = (NP * (kQ / 8) + kThreads - 1) / kThreads;      // (B o w)^T runs per thread
+  static_assert(NGRP * (4 / SPC) == WV, "state tiles must cover the waves");
+  constexpr int XE = kQ * kP / NTH;                             // x elements staged per thread
+  constexpr int CPL = 4 * YW;                                   // output channels per lane
+  constexpr int NBL = (kQ * NP + NTH * 8 - 1) / (NTH * 8);      // B (and C) loads per thread
+  constexpr int NBT = (NP * (kQ / 8) + NTH - 1) / NTH;          // (B o w)^T runs per thread
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef std::conditional_t<XE == 8, u32x4, u32x2> xw_t;       // a thread's run of x
+  typedef std::conditional_t<CPL == 8, u32x4, u32x2> zw_t;      // a lane's gate values
   __shared__ __attribute__((aligned(16))) uint16_t sC[kQ * CS];
   __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * CS];
   __shared__ __attribute__((aligned(16))) uint16_t sBt[2][NP * QS];  // (B o w)^T, hi and lo
@@ -445,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   __shared__ __attribute__((aligned(16))) float sCs[kQ];
   __shared__ __attribute__((aligned(16))) float sDt[kQ];
   __shared__ float sW[kQ];
-  __shared__ __attribute__((aligned(16))) float sYw[kWaves][32 * 16];  // each wave's two Y tiles
+  __shared__ __attribute__((aligned(16))) float sYw[WV][YW * 256];  // each wave's Y tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -463,19 +478,21 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   const int64_t bcb = static_cast<int64_t>(b) * L * N;
   const int64_t dtb = static_cast<int64_t>(b) * L * H + hd;
   const int64_t hsb = (static_cast<int64_t>(b) * H + hd) * kP * N;
-  const int hf = w >> 2;
   const int pcol = 16 * (w & 3) + lr;
-  const int yt0 = hf, yt1 = 3 - hf;
-  // Output layout: lane -> row orow of the wave's two Y tiles (sequence
-  // position ot) and 8 consecutive channels from op.
-  const int orow = lane >> 1;
-  const int ot = 16 * ((orow >> 4) ? yt1 : yt0) + (orow & 15);
-  const int op = 16 * (w & 3) + 8 * (lane & 1);
+  int yt[YW];
+  yt[0] = w >> 2;
+  if constexpr (YW == 2) yt[1] = 3 - (w >> 2);
+  // Output layout: lane -> row orow of the wave's Y tiles (sequence
+  // position ot) and CPL consecutive channels from op.
+  constexpr int LPR = 16 / CPL;  // lanes per row
+  const int orow = lane / LPR;
+  const int ot = 16 * yt[YW == 2 ? (orow >> 4) : 0] + (orow & 15);
+  const int op = 16 * (w & 3) + CPL * (lane % LPR);
   const int nb = SN * (w % NGRP), pb = SPC * (w / NGRP);  // this wave's state block
 
   // S above the diagonal blocks is read (k-steps of 32 cover it) but never
   // written: zero it once.
-  for (int i = tid; i < 2 * kQ * QS; i += kThreads) (&sS[0][0])[i] = 0;
+  for (int i = tid; i < 2 * kQ * QS; i += NTH) (&sS[0][0])[i] = 0;
   f32x4 hacc[SN * SPC];  // tile (jn, jp) at jn * SPC + jp
 #pragma unroll
   for (int j = 0; j < SN * SPC; ++j) {
@@ -490,7 +507,9 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   }
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
-  u32x4 xr, br[NBL], cr[NBL], zr;
+  u32x4 br[NBL], cr[NBL];
+  xw_t xr;
+  zw_t zr;
   uint16_t dtr = 0;
   auto fetch = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * kQ;
@@ -504,19 +523,29 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
     const rsrc_t rb = raw_buffer(static_cast<const char*>(p.B) + bo, nbc);
     const rsrc_t rc = raw_buffer(static_cast<const char*>(p.C) + bo, nbc);
     {
-      const int e = tid * 8;  // one 8-element run of x per thread
+      const int e = tid * XE;  // one XE-element run of x per thread
       const int t = e / kP, pp = e % kP;
-      xr = __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<uint32_t>((t * HP + pp) * 2), 0, 0);
+      const uint32_t off = static_cast<uint32_t>((t * HP + pp) * 2);
+      if constexpr (XE == 8) {
+        xr = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      } else {
+        xr = __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NBL; ++i) {
-      const int e = (i * kThreads + tid) * 8;
+      const int e = (i * NTH + tid) * 8;
       const uint32_t off = e < kQ * NP ? static_cast<uint32_t>(e * 2) : kOutOfRange;  // N == NP here
       br[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
       cr[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
     }
-    // the gate values of this lane's outputs: 8 channels of row ot
-    zr = __builtin_amdgcn_raw_buffer_load_b128(rz, static_cast<uint32_t>((ot * HP + op) * 2), 0, 0);
+    // the gate values of this lane's outputs: CPL channels of row ot
+    const uint32_t zoff = static_cast<uint32_t>((ot * HP + op) * 2);
+    if constexpr (CPL == 8) {
+      zr = __builtin_amdgcn_raw_buffer_load_b128(rz, zoff, 0, 0);
+    } else {
+      zr = __builtin_amdgcn_raw_buffer_load_b64(rz, zoff, 0, 0);
+    }
     // Every wave loads the step sizes (wave 0 uses them): memory operations
     // outside branches keep the waits before the staging counted exactly,
     // so the output stores of the chunk stay in flight across it.
@@ -531,23 +560,23 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
   // weights w. B, C and the step arrays are dead once a chunk's first half
   // is done, so the next chunk is staged right after the middle barrier,
   // while the current one finishes: two barriers per chunk.
-  u32x4 zq;
+  zw_t zq;
   auto stage = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * kQ;
     const int len = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
     uint16_t* xt = sXt[c & 1];
     {
-      const int e = tid * 8;
+      const int e = tid * XE;
       const int t = e / kP, pp = e % kP;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < XE / 2; ++j) {
         xt[xt_at(pp + 2 * j, t)] = static_cast<uint16_t>(xr[j] & 0xffffu);
         xt[xt_at(pp + 2 * j + 1, t)] = static_cast<uint16_t>(xr[j] >> 16);
       }
     }
 #pragma unroll
     for (int i = 0; i < NBL; ++i) {
-      const int e = (i * kThreads + tid) * 8;
+      const int e = (i * NTH + tid) * 8;
       if (e >= kQ * NP) break;
       const int t = e / NP, n = e % NP;
       *reinterpret_cast<u32x4*>(&sB[t * CS + n]) = br[i];
@@ -583,7 +612,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
     // (2a) (B o w)^T, split: run (n, s0 .. s0+7) per item.
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
-      const int item = i * kThreads + tid;
+      const int item = i * NTH + tid;
       if (item >= NP * (kQ / 8)) break;
       const int n = item % NP, s0 = 8 * (item / NP);
       uint16_t hi[8], lo[8];
@@ -598,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       *reinterpret_cast<u32x4*>(&sBt[0][n * QS + s0]) = vh;
       *reinterpret_cast<u32x4*>(&sBt[1][n * QS + s0]) = vl;
     }
-    // (2b) Scores: lower tiles q = w, w + 8; S = G decayed and scaled, split.
+    // (2b) Scores: lower tiles q = w, w + WV; S = G decayed and scaled, split.
     // Computed transposed, G^T = B C^T, so that a lane holds 4 consecutive s
     // of one row t of S and writes them as one 8-byte run per half.
     auto scores = [&](auto nq) __attribute__((always_inline)) {
@@ -607,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       f32x4 g[NQ];
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
-        const int q = w + kWaves * j;
+        const int q = w + WV * j;
         ti[j] = q == 0 ? 0 : (q < 3 ? 1 : (q < 6 ? 2 : 3));
         si[j] = q - ti[j] * (ti[j] + 1) / 2;
         g[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -634,7 +663,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
           // D x enters S X as D on the diagonal of S
           split_bf16(t > s0 + v ? val : (t == s0 + v ? val + Dh : 0.0f), hi[v], lo[v]);
         }
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         *reinterpret_cast<u32x2*>(&sS[0][t * QS + s0]) =
             u32x2{static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
                   static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
@@ -643,29 +671,32 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
                   static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
       }
     };
-    if (w < 10 - kWaves) {
-      scores(std::integral_constant<int, 2>{});
-    } else {
+    if constexpr (WV < 10) {
+      if (w < 10 - WV) {
+        scores(std::integral_constant<int, 2>{});
+      } else {
+        scores(std::integral_constant<int, 1>{});
+      }
+    } else if (w < 10) {
       scores(std::integral_constant<int, 1>{});
     }
     // (2c) Readout of the entering state, diag(exp(a cs_t)) C H.
-    const int yt[2] = {yt0, yt1};
-    f32x4 yacc[2];
+    f32x4 yacc[YW];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) yacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < YW; ++j) yacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k0 = 0; k0 < NP; k0 += 32) {
       const bf16x8 hh = lds8(&sHt[0][pcol * CS + k0 + 8 * lk]);
       const bf16x8 hl = lds8(&sHt[1][pcol * CS + k0 + 8 * lk]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < YW; ++j) {
         const bf16x8 cv = lds8(&sC[(16 * yt[j] + lr) * CS + k0 + 8 * lk]);
         yacc[j] = mfma32(cv, hh, yacc[j]);
         yacc[j] = mfma32(cv, hl, yacc[j]);
       }
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < YW; ++j) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) yacc[j][v] *= exp2_hw(a2 * sCs[16 * yt[j] + 4 * lk + v]);
     }
@@ -682,14 +713,30 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
           yacc[0] = mfma32(lds8(&sS[0][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
           yacc[0] = mfma32(lds8(&sS[1][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
         }
-        yacc[1] = mfma32(lds8(&sS[0][(16 * TB + lr) * QS + k0 + 8 * lk]), xv, yacc[1]);
-        yacc[1] = mfma32(lds8(&sS[1][(16 * TB + lr) * QS + k0 + 8 * lk]), xv, yacc[1]);
+        yacc[YW - 1] = mfma32(lds8(&sS[0][(16 * TB + lr) * QS + k0 + 8 * lk]), xv, yacc[YW - 1]);
+        yacc[YW - 1] = mfma32(lds8(&sS[1][(16 * TB + lr) * QS + k0 + 8 * lk]), xv, yacc[YW - 1]);
       }
     };
-    if (hf == 0) {
-      diag(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+    if constexpr (YW == 2) {
+      if (yt[0] == 0) {
+        diag(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+      } else {
+        diag(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+      }
     } else {
-      diag(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+      // one tile: TA = TB (the first product pair is the only one)
+      if (yt[0] < 2) {
+        const bf16x8 xv = lds8(&xt[xt_at(pcol, 8 * lk)]);
+        yacc[0] = mfma32(lds8(&sS[0][(16 * yt[0] + lr) * QS + 8 * lk]), xv, yacc[0]);
+        yacc[0] = mfma32(lds8(&sS[1][(16 * yt[0] + lr) * QS + 8 * lk]), xv, yacc[0]);
+      } else {
+#pragma unroll
+        for (int k0 = 0; k0 < kQ; k0 += 32) {
+          const bf16x8 xv = lds8(&xt[xt_at(pcol, k0 + 8 * lk)]);
+          yacc[0] = mfma32(lds8(&sS[0][(16 * yt[0] + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
+          yacc[0] = mfma32(lds8(&sS[1][(16 * yt[0] + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
+        }
+      }
     }
     // (4) Exit state: exp(a cs_end) H + (B o w)^T X.
     const float dend = exp2_hw(a2 * cend);
@@ -712,15 +759,15 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
         }
       }
     }
-    // (5) Outputs. Each wave passes its two Y tiles through its own LDS
-    // scratch so that a lane ends with 8 consecutive channels of one row:
-    // the gate values come in and y goes out as 16-byte runs (rows past the
+    // (5) Outputs. Each wave passes its Y tiles through its own LDS scratch
+    // so that a lane ends with CPL consecutive channels of one row: the gate
+    // values come in and y goes out as 8- or 16-byte runs (rows past the
     // sequence masked by the buffer's range, no branch). Then the exit state
     // (split) for the next chunk's readout.
     {
       float* sy = sYw[w];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < YW; ++j) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) sy[(16 * j + 4 * lk + v) * 16 + lr] = yacc[j][v];
       }
@@ -729,12 +776,16 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const f32x4 ya = *reinterpret_cast<const f32x4*>(&sy[orow * 16 + 8 * (lane & 1)]);
-      const f32x4 yb = *reinterpret_cast<const f32x4*>(&sy[orow * 16 + 8 * (lane & 1) + 4]);
-      float yv[8] = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
+      float yv[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL / 4; ++i) {
+        const f32x4 y4 = *reinterpret_cast<const f32x4*>(&sy[orow * 16 + CPL * (lane % LPR) + 4 * i]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) yv[4 * i + v] = y4[v];
+      }
       if (p.z) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < CPL; ++q) {
           const uint32_t zw = zq[q >> 1];
           yv[q] *= silu_f(__uint_as_float((q & 1) ? (zw & 0xffff0000u) : (zw << 16)));
         }
@@ -745,18 +796,24 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       const bool in = ot < len;
       const uint32_t off = static_cast<uint32_t>((ot * HP + op) * OB);
       if constexpr (BF16_OUT) {
-        u32x4 pk;
+        zw_t pk;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < CPL / 2; ++j) {
           pk[j] = static_cast<uint32_t>(f32_to_bf16_bits(yv[2 * j])) |
                   (static_cast<uint32_t>(f32_to_bf16_bits(yv[2 * j + 1])) << 16);
         }
-        __builtin_amdgcn_raw_buffer_store_b128(pk, ry, in ? off : kOutOfRange, 0, 0);
+        if constexpr (CPL == 8) {
+          __builtin_amdgcn_raw_buffer_store_b128(pk, ry, in ? off : kOutOfRange, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b64(pk, ry, in ? off : kOutOfRange, 0, 0);
+        }
       } else {
-        const u32x4 lo4 = {__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]), __float_as_uint(yv[3])};
-        const u32x4 hi4 = {__float_as_uint(yv[4]), __float_as_uint(yv[5]), __float_as_uint(yv[6]), __float_as_uint(yv[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(lo4, ry, in ? off : kOutOfRange, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(hi4, ry, in ? off + 16u : kOutOfRange, 0, 0);
+#pragma unroll
+        for (int i = 0; i < CPL / 4; ++i) {
+          const u32x4 y4 = {__float_as_uint(yv[4 * i]), __float_as_uint(yv[4 * i + 1]), __float_as_uint(yv[4 * i + 2]),
+                            __float_as_uint(yv[4 * i + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(y4, ry, in ? off + 16u * i : kOutOfRange, 0, 0);
+        }
       }
     }
 #pragma unroll
@@ -765,7 +822,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bf16_kernel(const SsdArgs p) {
       uint16_t hi[4], lo[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) split_bf16(hacc[j][v], hi[v], lo[v]);
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       *reinterpret_cast<u32x2*>(&sHt[0][pc * CS + n]) =
           u32x2{static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
                 static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
@@ -798,10 +854,15 @@ int launch_np(const SsdArgs& a, hipStream_t st) {
   const bool vec = a.headdim == kP && a.dstate == NP;
   const void* fn = vec ? reinterpret_cast<const void*>(&ssd_fwd_kernel<NP, BI, BO, SP, true>)
                        : reinterpret_cast<const void*>(&ssd_fwd_kernel<NP, BI, BO, SP, false>);
+  unsigned threads = kThreads;
   if constexpr (BI) {
-    if (vec) fn = reinterpret_cast<const void*>(&ssd_bf16_kernel<NP, BO, SP>);
+    constexpr int WV = NP >= 64 ? 16 : 8;
+    if (vec) {
+      fn = reinterpret_cast<const void*>(&ssd_bf16_kernel<NP, WV, BO, SP>);
+      threads = 64 * WV;
+    }
   }
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.batch * a.nheads)), dim3(kThreads), kargs, 0, st);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.batch * a.nheads)), dim3(threads), kargs, 0, st);
 }
 
 template <bool BI, bool BO, bool SP>
