@@ -440,26 +440,30 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
   // The exit state's 16 x 16 tiles (NP / 16 along n, 4 along p) are dealt
   // to the waves in blocks of SN x SPC; a block reads SN + SPC operand runs
   // per k-step for SN x SPC products, so blocks are square where they can be.
-  constexpr int SN = (WV == 8 && NP >= 64) ? 2 : 1;
-  constexpr int SPC = NP == 128 ? 2 : 1;
+  // (a k-step reads one run of B^T per n-tile and two of (w x)^T per p-tile)
+  constexpr int SN = ((WV == 8 && NP >= 64) || (WV == 16 && NP == 128)) ? 2 : 1;
+  constexpr int SPC = (WV == 8 && NP == 128) ? 2 : 1;
   constexpr int NGRP = NP / 16 / SN;
   static_assert(NGRP * (4 / SPC) == WV, "state tiles must cover the waves");
   constexpr int XE = kQ * kP / NTH;                             // x elements staged per thread
   constexpr int CPL = 4 * YW;                                   // output channels per lane
   constexpr int NBL = (kQ * NP + NTH * 8 - 1) / (NTH * 8);      // B (and C) loads per thread
-  constexpr int NBT = (NP * (kQ / 8) + NTH - 1) / NTH;          // (B o w)^T runs per thread
+  constexpr int NBT = (NP * (kQ / 8) + NTH - 1) / NTH;          // B^T runs per thread
+  constexpr int XW0 = NTH - kP * (kQ / 8);                      // first thread of the (w x)^T runs
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef std::conditional_t<XE == 8, u32x4, u32x2> xw_t;       // a thread's run of x
   typedef std::conditional_t<CPL == 8, u32x4, u32x2> zw_t;      // a lane's gate values
   __shared__ __attribute__((aligned(16))) uint16_t sC[kQ * CS];
   __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * CS];
-  __shared__ __attribute__((aligned(16))) uint16_t sBt[2][NP * QS];  // (B o w)^T, hi and lo
+  __shared__ __attribute__((aligned(16))) uint16_t sBt[NP * QS];     // B^T (exact)
+  __shared__ __attribute__((aligned(16))) uint16_t sXw[2][kP * QS];  // (w x)^T, hi and lo
   __shared__ __attribute__((aligned(16))) uint16_t sXt[2][kP * QS];  // x^T, by chunk parity
   __shared__ __attribute__((aligned(16))) uint16_t sS[2][kQ * QS];   // S, hi and lo
   __shared__ __attribute__((aligned(16))) uint16_t sHt[2][kP * CS];  // H^T, hi and lo
   __shared__ __attribute__((aligned(16))) float sCs[kQ];
   __shared__ __attribute__((aligned(16))) float sDt[kQ];
   __shared__ float sW[kQ];
+  __shared__ __attribute__((aligned(16))) float sE[kQ];  // exp(a cs_t)
   __shared__ __attribute__((aligned(16))) float sYw[WV][YW * 256];  // each wave's Y tiles
 
   const int tid = threadIdx.x;
@@ -594,6 +598,7 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       sDt[lane] = dt;
       sCs[lane] = cs;
       sW[lane] = exp2_hw(a2 * (ce - cs)) * dt;
+      sE[lane] = exp2_hw(a2 * cs);
     }
   };
 
@@ -609,23 +614,40 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
     const uint16_t* xt = sXt[c & 1];
     const float cend = sCs[kQ - 1];
 
-    // (2a) (B o w)^T, split: run (n, s0 .. s0+7) per item.
+    // (2a) The exit state's operands, (B o w)^T X = B^T (w x): B^T as it is
+    // (exact; run (n, s0 .. s0+7) per item) and the w-scaled x^T, split
+    // (run (p, s0 .. s0+7) per item, on the last kP * Q / 8 threads).
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
       const int item = i * NTH + tid;
       if (item >= NP * (kQ / 8)) break;
       const int n = item % NP, s0 = 8 * (item / NP);
+      u32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = static_cast<uint32_t>(sB[(s0 + 2 * j) * CS + n]) |
+               (static_cast<uint32_t>(sB[(s0 + 2 * j + 1) * CS + n]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(&sBt[n * QS + s0]) = v;
+    }
+    if (tid >= XW0) {
+      const int item = tid - XW0;
+      const int pp = item % kP, s0 = 8 * (item / kP);
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(&xt[xt_at(pp, s0)]);
       uint16_t hi[8], lo[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split_bf16(bf16_bits_to_f32(sB[(s0 + j) * CS + n]) * sW[s0 + j], hi[j], lo[j]);
+      for (int j = 0; j < 4; ++j) {
+        split_bf16(__uint_as_float(xv[j] << 16) * sW[s0 + 2 * j], hi[2 * j], lo[2 * j]);
+        split_bf16(__uint_as_float(xv[j] & 0xffff0000u) * sW[s0 + 2 * j + 1], hi[2 * j + 1], lo[2 * j + 1]);
+      }
       u32x4 vh, vl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         vh[j] = static_cast<uint32_t>(hi[2 * j]) | (static_cast<uint32_t>(hi[2 * j + 1]) << 16);
         vl[j] = static_cast<uint32_t>(lo[2 * j]) | (static_cast<uint32_t>(lo[2 * j + 1]) << 16);
       }
-      *reinterpret_cast<u32x4*>(&sBt[0][n * QS + s0]) = vh;
-      *reinterpret_cast<u32x4*>(&sBt[1][n * QS + s0]) = vl;
+      *reinterpret_cast<u32x4*>(&sXw[0][xt_at(pp, s0)]) = vh;
+      *reinterpret_cast<u32x4*>(&sXw[1][xt_at(pp, s0)]) = vl;
     }
     // (2b) Scores: lower tiles q = w, w + WV; S = G decayed and scaled, split.
     // Computed transposed, G^T = B C^T, so that a lane holds 4 consecutive s
@@ -696,10 +718,7 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < YW; ++j) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) yacc[j][v] *= exp2_hw(a2 * sCs[16 * yt[j] + 4 * lk + v]);
-    }
+    for (int j = 0; j < YW; ++j) yacc[j] *= *reinterpret_cast<const f32x4*>(&sE[16 * yt[j] + 4 * lk]);
     __syncthreads();  // S and (B o w)^T complete; every wave is done reading H^T
 
     // (3) Y += S X over s <= t, in k-steps of 32 (tiles 0 and 2 also read
@@ -738,24 +757,25 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
         }
       }
     }
-    // (4) Exit state: exp(a cs_end) H + (B o w)^T X.
+    // (4) Exit state: exp(a cs_end) H + B^T (w x).
     const float dend = exp2_hw(a2 * cend);
 #pragma unroll
     for (int j = 0; j < SN * SPC; ++j) hacc[j] *= dend;
 #pragma unroll
     for (int k0 = 0; k0 < kQ; k0 += 32) {
-      bf16x8 xv[SPC];
+      bf16x8 xh[SPC], xl[SPC];
 #pragma unroll
-      for (int jp = 0; jp < SPC; ++jp) xv[jp] = lds8(&xt[xt_at(16 * (pb + jp) + lr, k0 + 8 * lk)]);
+      for (int jp = 0; jp < SPC; ++jp) {
+        xh[jp] = lds8(&sXw[0][xt_at(16 * (pb + jp) + lr, k0 + 8 * lk)]);
+        xl[jp] = lds8(&sXw[1][xt_at(16 * (pb + jp) + lr, k0 + 8 * lk)]);
+      }
 #pragma unroll
       for (int jn = 0; jn < SN; ++jn) {
-        const int n = 16 * (nb + jn) + lr;
-        const bf16x8 bh = lds8(&sBt[0][n * QS + k0 + 8 * lk]);
-        const bf16x8 bl = lds8(&sBt[1][n * QS + k0 + 8 * lk]);
+        const bf16x8 bv = lds8(&sBt[(16 * (nb + jn) + lr) * QS + k0 + 8 * lk]);
 #pragma unroll
         for (int jp = 0; jp < SPC; ++jp) {
-          hacc[jn * SPC + jp] = mfma32(bh, xv[jp], hacc[jn * SPC + jp]);
-          hacc[jn * SPC + jp] = mfma32(bl, xv[jp], hacc[jn * SPC + jp]);
+          hacc[jn * SPC + jp] = mfma32(bv, xh[jp], hacc[jn * SPC + jp]);
+          hacc[jn * SPC + jp] = mfma32(bv, xl[jp], hacc[jn * SPC + jp]);
         }
       }
     }
