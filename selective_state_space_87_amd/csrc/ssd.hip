@@ -397,9 +397,9 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
 //   scores   G = C B^T                     C, B exact            1 x
 //   readout  C H                           H = Hhi + Hlo          2 x
 //   diagonal S X                           S = Shi + Slo          2 x
-//   state    (B o w)^T X                   B o w = hi + lo        2 x
+//   state    (B o w)^T X = B^T (w x)       w x = hi + lo          2 x
 // Operands are read as 16-byte runs of 8 consecutive k: every LDS array is
-// laid out with the contraction index contiguous (x and the w-scaled B are
+// laid out with the contraction index contiguous (x, w x and B are also
 // stored transposed), rows padded by 8 elements (16 bytes).
 // With N >= 64 the block has sixteen waves (four per SIMD, at most 128
 // registers each), so that one wave's LDS and transcendental latencies hide
