@@ -172,8 +172,31 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   constexpr int BCW = (NS * T * WPS + W * 64 - 1) / (W * 64);  // packed B/C words per thread
   auto item_step = [&](int i) __attribute__((always_inline)) { return w + W * i; };
   auto item_ok = [&](int t) __attribute__((always_inline)) { return ch_ok && t >= 0 && t < L; };
-  auto raw_in = [&](const void* ptr, int t) __attribute__((always_inline)) -> uint32_t {
-    return item_ok(t) ? load_bits<BF16_IN>(ptr, (plane + t) * Dm + ch) : 0u;
+  // Every global access of the tile loop is a raw buffer access whose
+  // masked lanes get an out-of-range offset (loads read 0, stores are
+  // dropped): with no per-lane branch around a memory operation, the waits
+  // for the next tile's loads count exactly and leave this tile's stores in
+  // flight instead of draining the memory queue. Per-batch planes are below
+  // 2^30 bytes, so every range fits the descriptor.
+  constexpr int EB = BF16_IN ? 2 : 4;
+  const uint32_t in_bytes = static_cast<uint32_t>(static_cast<int64_t>(L) * Dm * EB);
+  const uint32_t f_bytes = static_cast<uint32_t>(static_cast<int64_t>(L) * Dm * 4);
+  const rsrc_t ru_b = raw_buffer(static_cast<const char*>(p.u) + plane * Dm * EB, in_bytes);
+  const rsrc_t rd_b = raw_buffer(static_cast<const char*>(p.delta) + plane * Dm * EB, in_bytes);
+  const rsrc_t rz_b = raw_buffer(has_z ? static_cast<const char*>(p.z) + plane * Dm * EB : nullptr,
+                                 has_z ? in_bytes : 0u);
+  const rsrc_t rdy_b = raw_buffer(p.dy + plane * Dm, f_bytes);
+  const rsrc_t rbc_b = raw_buffer(bcb, static_cast<uint32_t>(static_cast<int64_t>(NS) * Lp * WPS * 4));
+  // An offset is a per-lane channel part plus a wave-uniform step part, each
+  // with its own out-of-range marker (their sums never wrap and always lie
+  // beyond a plane), so the masking needs no per-lane control flow.
+  constexpr uint32_t kLaneOff = 0x80000000u, kStepOff = 0x40000000u;
+  auto item_off = [&](int t, int eb) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t lane_part = ch_ok ? static_cast<uint32_t>(ch * eb) : kLaneOff;
+    const uint32_t step = static_cast<unsigned>(t) < static_cast<unsigned>(L)
+                              ? static_cast<uint32_t>(t) * static_cast<uint32_t>(Dm) * eb
+                              : kStepOff;
+    return lane_part + step;
   };
   uint32_t r_u[IT], r_d[IT], r_z[IT], r_bc[BCW];
   float r_dy[IT];
@@ -181,16 +204,18 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int t = k * T + item_step(i);
-      r_u[i] = raw_in(p.u, t);
-      r_d[i] = raw_in(p.delta, t);
-      r_z[i] = has_z ? raw_in(p.z, t) : 0u;
-      r_dy[i] = item_ok(t) ? p.dy[(plane + t) * Dm + ch] : 0.0f;
+      const uint32_t off = item_off(t, EB);
+      r_u[i] = buffer_load_bits<BF16_IN>(ru_b, off);
+      r_d[i] = buffer_load_bits<BF16_IN>(rd_b, off);
+      r_z[i] = buffer_load_bits<BF16_IN>(rz_b, off);
+      r_dy[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdy_b, item_off(t, 4), 0, 0));
     }
 #pragma unroll
     for (int j = 0; j < BCW; ++j) {
       const int idx = threadIdx.x + j * W * 64;
       const int n = idx / (T * WPS), q = idx % (T * WPS);
-      r_bc[j] = idx < NS * T * WPS ? bcb[(static_cast<int64_t>(n) * Lp + k * T) * WPS + q] : 0u;
+      const uint32_t off = idx < NS * T * WPS ? static_cast<uint32_t>(((n * Lp + k * T) * WPS + q) * 4) : kOutOfRange;
+      r_bc[j] = __builtin_amdgcn_raw_buffer_load_b32(rbc_b, off, 0, 0);
     }
   };
   auto stage_bc = [&]() __attribute__((always_inline)) {
@@ -233,15 +258,26 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   float r_ck[S];
   auto fetch2 = [&](int k) __attribute__((always_inline)) {
     fetch_items(k);
-    const float* ck = p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm + ch;
+    const rsrc_t rck = raw_buffer(p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm,
+                                  static_cast<uint32_t>(S * Dm * 4));
 #pragma unroll
-    for (int s = 0; s < S; ++s) r_ck[s] = ch_ok ? ck[static_cast<int64_t>(s) * Dm] : 0.0f;
+    for (int s = 0; s < S; ++s) {
+      r_ck[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rck, ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kOutOfRange, 0, 0));
+    }
   };
+  const rsrc_t rdu_b = raw_buffer(p.du + plane * Dm, f_bytes);
+  const rsrc_t rdd_b = raw_buffer(p.ddelta + plane * Dm, f_bytes);
+  const rsrc_t rdz_b = raw_buffer(has_z && p.dz ? p.dz + plane * Dm : nullptr, has_z && p.dz ? f_bytes : 0u);
+  const uint32_t part_bytes = static_cast<uint32_t>(static_cast<int64_t>(Lp) * NS * 4);
+  const int64_t part_row = (static_cast<int64_t>(blk) * p.batch + b) * Lp * NS;
+  const rsrc_t rdB_b = raw_buffer(p.dBp + part_row, part_bytes);
+  const rsrc_t rdC_b = raw_buffer(p.dCp + part_row, part_bytes);
   auto stage2 = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = item_step(i);
-      if (tt < T) {
+      if (T >= W || tt < T) {   // (always, for T >= W)
         float x;
         const float dt = step_size(k, i, x);
         const float uv = bits_to_f32<BF16_IN>(r_u[i]);
@@ -327,19 +363,19 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       const float r = lane_transpose_sum<G>(gv, lane);
       constexpr int LG = __builtin_ctz(G);
       const int j = lane >> (6 - LG);
-      if ((lane & ((1 << (6 - LG)) - 1)) == 0) {
-        const int which = j / (T * S), rem = j % (T * S);
-        const int t = k * T + rem / S, n = w * S + rem % S;
-        float* dst = which == 0 ? p.dBp : p.dCp;
-        dst[((static_cast<int64_t>(blk) * p.batch + b) * Lp + t) * NS + n] = r;
-      }
+      const bool lead = (lane & ((1 << (6 - LG)) - 1)) == 0;
+      const int which = j / (T * S), rem = j % (T * S);
+      const int t = k * T + rem / S, n = w * S + rem % S;
+      const uint32_t off = static_cast<uint32_t>((t * NS + n) * 4);
+      buffer_store_f32<false>(r, rdB_b, lead && which == 0 ? off : kOutOfRange);
+      buffer_store_f32<false>(r, rdC_b, lead && which == 1 ? off : kOutOfRange);
     }
     __syncthreads();
     // -- epilogue of tile k (per item), then staging of tile k-1
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = item_step(i);
-      if (tt < T) {
+      if (T >= W || tt < T) {   // (always, for T >= W)
         const int t = k * T + tt;
         float pre = 0.0f, ddt = 0.0f, dus = 0.0f;
 #pragma unroll
@@ -348,16 +384,15 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
           ddt += sG[tt][lane * W + q];
           dus += sU[tt][lane * W + q];
         }
-        if (ch_ok && t < L) {
-          const int64_t o = (plane + t) * Dm + ch;
-          pre = fmaf(Dv, e_u[i], pre);
-          if (has_z && p.dz) p.dz[o] = e_dy[i] * pre * e_dsilu[i];
-          const float dd = ddt * e_dsp[i];
-          p.ddelta[o] = dd;
-          p.du[o] = fmaf(e_dp[i], Dv, dus);
-          dD_acc = fmaf(e_dp[i], e_u[i], dD_acc);
-          dbias_acc += dd;
-        }
+        const bool ok = ch_ok && t < L;
+        const uint32_t off = ok ? static_cast<uint32_t>((t * Dm + ch) * 4) : kOutOfRange;
+        pre = fmaf(Dv, e_u[i], pre);
+        buffer_store_f32<false>(e_dy[i] * pre * e_dsilu[i], rdz_b, off);
+        const float dd = ddt * e_dsp[i];
+        buffer_store_f32<false>(dd, rdd_b, off);
+        buffer_store_f32<false>(fmaf(e_dp[i], Dv, dus), rdu_b, off);
+        dD_acc = fmaf(ok ? e_dp[i] : 0.0f, e_u[i], dD_acc);
+        dbias_acc += ok ? dd : 0.0f;
       }
     }
     if (k > 0) stage2(k - 1);
