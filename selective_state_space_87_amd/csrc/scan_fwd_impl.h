@@ -244,8 +244,10 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     if constexpr (BCL) {
       // Tile k's rows of B and C: T*N contiguous elements from step t0 + k*T,
       // fewer (down to none) past the chunk's end, where the reads give 0.
+      // (the row count is wave-uniform; readfirstlane keeps it, and so the
+      // descriptors, in scalar registers, which buffer loads require)
       const int first = k * T;
-      const int rows = max(0, min(T, len - first));
+      const int rows = __builtin_amdgcn_readfirstlane(max(0, min(T, len - first)));
       const int64_t eo = ((static_cast<int64_t>(b) * p.L + t0 + first) * N) * IN_B;
       const uint32_t nb = static_cast<uint32_t>(rows * N) * IN_B;
       const rsrc_t rbb = raw_buffer(static_cast<const char*>(p.Bm) + eo, nb);
