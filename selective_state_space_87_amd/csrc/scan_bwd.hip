@@ -342,20 +342,24 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
     float gv[G];
 #pragma unroll
     for (int t = T - 1; t >= 0; --t) {
-      float ddt_acc = 0.0f, du_acc = 0.0f;
+      // Per step, over this wave's states: slb = sum lam B and
+      // sla = sum lam A a h, so that the step's partials are
+      // ddt = sla + u slb and du = dt slb (the factors common to all states
+      // applied once per step).
+      float slb = 0.0f, sla = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const float bval = bvs[t][s], cval = cvs[t][s];
-        const float lam = fmaf(dpv[t], cval, mu[s]);
+        const float lam = fmaf(dpv[t], cvs[t][s], mu[s]);
         gv[t * S + s] = lam * dtu[t];                 // -> dB (sum over channels)
         gv[T * S + t * S + s] = dpv[t] * hs[t][s];    // -> dC (sum over channels)
-        ddt_acc = fmaf(lam, fmaf(A1[s], ahv[t][s], bval * uvv[t]), ddt_acc);
-        du_acc = fmaf(lam, dtv[t] * bval, du_acc);
-        dA_acc[s] = fmaf(lam * dtv[t], ahv[t][s], dA_acc[s]);
+        slb = fmaf(lam, bvs[t][s], slb);
+        const float la = lam * ahv[t][s];
+        sla = fmaf(la, A1[s], sla);
+        dA_acc[s] = fmaf(la, dtv[t], dA_acc[s]);
         mu[s] = av[t][s] * lam;
       }
-      sG[t][lane * W + w] = ddt_acc;
-      sU[t][lane * W + w] = du_acc;
+      sG[t][lane * W + w] = fmaf(slb, uvv[t], sla);
+      sU[t][lane * W + w] = slb * dtv[t];
     }
     // dB / dC partials of this block: value j = lane >> (6 - log2 G) after the
     // transposed butterfly; one lane of each group writes it.
