@@ -203,7 +203,9 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   auto fetch_items = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const int t = k * T + item_step(i);
+      // (waves past the tile's steps, with more waves than steps, have no item)
+      const bool live = T >= W || item_step(i) < T;
+      const int t = live ? k * T + item_step(i) : -1;
       const uint32_t off = item_off(t, EB);
       r_u[i] = buffer_load_bits<BF16_IN>(ru_b, off);
       r_d[i] = buffer_load_bits<BF16_IN>(rd_b, off);
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   }
   float dD_acc = 0.0f, dbias_acc = 0.0f;
   // Items of the tile being finished (kept from its staging to its epilogue).
-  float e_dy[IT], e_dsilu[IT], e_dsp[IT], e_u[IT], e_dp[IT];
+  float e_dy[IT] = {}, e_dsilu[IT] = {}, e_dsp[IT] = {}, e_u[IT] = {}, e_dp[IT] = {};
   // Checkpoint of the next tile to process, fetched one tile ahead.
   float r_ck[S];
   auto fetch2 = [&](int k) __attribute__((always_inline)) {
@@ -301,6 +303,11 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
     stage_bc();
   };
 
+  // Slot of this wave's partial for this lane's channel among the W of the
+  // channel (which the epilogue sums in any order): the wave index is XORed
+  // with the lane's high bits, so a wave's 64 stores fall on distinct banks
+  // (slot lane * W + w alone put every (64 / W)-th lane on one bank).
+  const int pslot = lane * W + (w ^ ((lane / (64 / W)) & (W - 1)));
   if (nt > 0) {
     fetch2(nt - 1);
     stage2(nt - 1);
@@ -337,7 +344,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         hs[t][s] = hh[s];
         acc = fmaf(cval, hh[s], acc);
       }
-      sP[t][lane * W + w] = acc;
+      sP[t][pslot] = acc;
     }
     float gv[G];
 #pragma unroll
@@ -358,8 +365,8 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         dA_acc[s] = fmaf(la, dtv[t], dA_acc[s]);
         mu[s] = av[t][s] * lam;
       }
-      sG[t][lane * W + w] = fmaf(slb, uvv[t], sla);
-      sU[t][lane * W + w] = slb * dtv[t];
+      sG[t][pslot] = fmaf(slb, uvv[t], sla);
+      sU[t][pslot] = slb * dtv[t];
     }
     // dB / dC partials of this block: value j = lane >> (6 - log2 G) after the
     // transposed butterfly; one lane of each group writes it.
@@ -379,16 +386,20 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = item_step(i);
-      if (T >= W || tt < T) {   // (always, for T >= W)
+      // Without branching around the stores: waves with no item read any
+      // row and store nothing.
+      const bool live = T >= W || tt < T;
+      {
+        const int tr = live ? tt : 0;
         const int t = k * T + tt;
         float pre = 0.0f, ddt = 0.0f, dus = 0.0f;
 #pragma unroll
         for (int q = 0; q < W; ++q) {
-          pre += sP[tt][lane * W + q];
-          ddt += sG[tt][lane * W + q];
-          dus += sU[tt][lane * W + q];
+          pre += sP[tr][lane * W + q];
+          ddt += sG[tr][lane * W + q];
+          dus += sU[tr][lane * W + q];
         }
-        const bool ok = ch_ok && t < L;
+        const bool ok = live && ch_ok && t < L;
         const uint32_t off = ok ? static_cast<uint32_t>((t * Dm + ch) * 4) : kOutOfRange;
         pre = fmaf(Dv, e_u[i], pre);
         buffer_store_f32<false>(e_dy[i] * pre * e_dsilu[i], rdz_b, off);
