@@ -133,11 +133,17 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   constexpr int G = 2 * T * S;              // values per lane reduced over channels
   static_assert(G <= 64, "backward supports at most 32 (step, state) pairs per wave");
 
-  __shared__ float4 sQ[T][64];                       // (dt, dt*u, dp, u) per step, channel
-  __shared__ uint32_t sBC[NS][T * WPS];              // packed B/C of the tile
-  __shared__ float sP[T][64 * W];                    // readout partials (pre-gate output)
-  __shared__ float sG[T][64 * W];                    // ddt partials
-  __shared__ float sU[T][64 * W];                    // du partials
+  // The next tile is staged (into the other of two buffers) while this one
+  // is computed, so that one barrier per tile separates the tiles. The
+  // per-wave partials are double-buffered too where LDS allows (NB = 2);
+  // otherwise a second barrier keeps the next tile's partials from
+  // overwriting this tile's before the epilogue has read them.
+  constexpr int NB = 2 * 3 * T * 64 * W * 4 + 2 * T * 64 * 16 <= 150 * 1024 ? 2 : 1;
+  __shared__ float4 sQ[2][T][64];                    // (dt, dt*u, dp, u) per step, channel
+  __shared__ uint32_t sBC[2][NS][T * WPS];           // packed B/C of the tile
+  __shared__ float sP[NB][T][64 * W];                // readout partials (pre-gate output)
+  __shared__ float sG[NB][T][64 * W];                // ddt partials
+  __shared__ float sU[NB][T][64 * W];                // du partials
   __shared__ float sRed[2][W][64];                   // final per-channel sums
 
   const int lane = threadIdx.x & 63;
@@ -220,21 +226,21 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       r_bc[j] = __builtin_amdgcn_raw_buffer_load_b32(rbc_b, off, 0, 0);
     }
   };
-  auto stage_bc = [&]() __attribute__((always_inline)) {
+  auto stage_bc = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < BCW; ++j) {
       const int idx = threadIdx.x + j * W * 64;
-      if (idx < NS * T * WPS) sBC[idx / (T * WPS)][idx % (T * WPS)] = r_bc[j];
+      if (idx < NS * T * WPS) sBC[qb][idx / (T * WPS)][idx % (T * WPS)] = r_bc[j];
     }
   };
-  auto bc_of = [&](int n, int t, float& bval, float& cval) __attribute__((always_inline)) {
+  auto bc_of = [&](int qb, int n, int t, float& bval, float& cval) __attribute__((always_inline)) {
     if constexpr (BF16_IN) {
-      const uint32_t wd = sBC[n][t];
+      const uint32_t wd = sBC[qb][n][t];
       bval = __uint_as_float(wd & 0xffff0000u);
       cval = __uint_as_float(wd << 16);
     } else {
-      bval = __uint_as_float(sBC[n][2 * t]);
-      cval = __uint_as_float(sBC[n][2 * t + 1]);
+      bval = __uint_as_float(sBC[qb][n][2 * t]);
+      cval = __uint_as_float(sBC[qb][n][2 * t + 1]);
     }
   };
   // Step size of item i of tile k from the fetched raw delta (0 beyond L).
@@ -254,7 +260,9 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
     dA_acc[s] = 0.0f;
   }
   float dD_acc = 0.0f, dbias_acc = 0.0f;
-  // Items of the tile being finished (kept from its staging to its epilogue).
+  // Items of the next tile (set by its staging) and of the tile being
+  // finished (kept from its staging to its epilogue).
+  float n_dy[IT] = {}, n_dsilu[IT] = {}, n_dsp[IT] = {}, n_u[IT] = {}, n_dp[IT] = {};
   float e_dy[IT] = {}, e_dsilu[IT] = {}, e_dsp[IT] = {}, e_u[IT] = {}, e_dp[IT] = {};
   // Checkpoint of the next tile to process, fetched one tile ahead.
   float r_ck[S];
@@ -276,6 +284,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   const rsrc_t rdB_b = raw_buffer(p.dBp + part_row, part_bytes);
   const rsrc_t rdC_b = raw_buffer(p.dCp + part_row, part_bytes);
   auto stage2 = [&](int k) __attribute__((always_inline)) {
+    const int qb = k & 1;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = item_step(i);
@@ -292,15 +301,15 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
           dsilu = sg * fmaf(zv, 1.0f - sg, 1.0f);
         }
         const float dp = dyv * g;
-        e_dy[i] = dyv;
-        e_dsilu[i] = dsilu;
-        e_dsp[i] = SOFTPLUS ? sigmoid_f(x) : 1.0f;
-        e_u[i] = uv;
-        e_dp[i] = dp;
-        sQ[tt][lane] = make_float4(dt, dt * uv, dp, uv);
+        n_dy[i] = dyv;
+        n_dsilu[i] = dsilu;
+        n_dsp[i] = SOFTPLUS ? sigmoid_f(x) : 1.0f;
+        n_u[i] = uv;
+        n_dp[i] = dp;
+        sQ[qb][tt][lane] = make_float4(dt, dt * uv, dp, uv);
       }
     }
-    stage_bc();
+    stage_bc(qb);
   };
 
   // Slot of this wave's partial for this lane's channel among the W of the
@@ -314,6 +323,15 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   }
   __syncthreads();
   for (int k = nt - 1; k >= 0; --k) {
+    const int qb = k & 1, pb = NB == 2 ? (k & 1) : 0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      e_dy[i] = n_dy[i];
+      e_dsilu[i] = n_dsilu[i];
+      e_dsp[i] = n_dsp[i];
+      e_u[i] = n_u[i];
+      e_dp[i] = n_dp[i];
+    }
     float hh[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) hh[s] = r_ck[s];
@@ -322,7 +340,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
     float dtv[T], dtu[T], dpv[T], uvv[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const float4 q = sQ[t][lane];
+      const float4 q = sQ[qb][t][lane];
       dtv[t] = q.x;
       dtu[t] = q.y;
       dpv[t] = q.z;
@@ -335,7 +353,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         float bval, cval;
-        bc_of(w * S + s, t, bval, cval);   // kept for the adjoint below
+        bc_of(qb, w * S + s, t, bval, cval);   // kept for the adjoint below
         bvs[t][s] = bval;
         cvs[t][s] = cval;
         av[t][s] = exp2_hw(dtv[t] * A2[s]);
@@ -344,7 +362,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         hs[t][s] = hh[s];
         acc = fmaf(cval, hh[s], acc);
       }
-      sP[t][pslot] = acc;
+      sP[pb][t][pslot] = acc;
     }
     float gv[G];
 #pragma unroll
@@ -365,8 +383,8 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         dA_acc[s] = fmaf(la, dtv[t], dA_acc[s]);
         mu[s] = av[t][s] * lam;
       }
-      sG[t][pslot] = fmaf(slb, uvv[t], sla);
-      sU[t][pslot] = slb * dtv[t];
+      sG[pb][t][pslot] = fmaf(slb, uvv[t], sla);
+      sU[pb][t][pslot] = slb * dtv[t];
     }
     // dB / dC partials of this block: value j = lane >> (6 - log2 G) after the
     // transposed butterfly; one lane of each group writes it.
@@ -381,8 +399,9 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       buffer_store_f32<false>(r, rdB_b, lead && which == 0 ? off : kOutOfRange);
       buffer_store_f32<false>(r, rdC_b, lead && which == 1 ? off : kOutOfRange);
     }
+    // -- staging of tile k-1 (the other buffers), then the epilogue of tile k
+    if (k > 0) stage2(k - 1);
     __syncthreads();
-    // -- epilogue of tile k (per item), then staging of tile k-1
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = item_step(i);
@@ -395,9 +414,9 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         float pre = 0.0f, ddt = 0.0f, dus = 0.0f;
 #pragma unroll
         for (int q = 0; q < W; ++q) {
-          pre += sP[tr][lane * W + q];
-          ddt += sG[tr][lane * W + q];
-          dus += sU[tr][lane * W + q];
+          pre += sP[pb][tr][lane * W + q];
+          ddt += sG[pb][tr][lane * W + q];
+          dus += sU[pb][tr][lane * W + q];
         }
         const bool ok = live && ch_ok && t < L;
         const uint32_t off = ok ? static_cast<uint32_t>((t * Dm + ch) * 4) : kOutOfRange;
@@ -410,8 +429,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         dbias_acc += ok ? dd : 0.0f;
       }
     }
-    if (k > 0) stage2(k - 1);
-    __syncthreads();
+    if constexpr (NB == 1) __syncthreads();
   }
 
   // ---------------------------------------------------------------- per-block outputs
