@@ -130,6 +130,26 @@ def test_bwd_mamba14b_layer_sampled_channels():
     compare("bwd 1.4b layer sampled", g, ref, mag, tol_for("bf16", "f32"), channels=ch, skip=("dB", "dC"))
 
 
+def test_bwd_mamba14b_layer_dB_dC_from_sampled_channels():
+    """Full 1.4B-shaped layer, same launch, with dy zero outside a few
+    channels (and no dh_final): every other channel's adjoint is exactly 0,
+    so its dB and dC contributions are exactly 0, and the full-size dB and
+    dC (sums over all channels) equal the oracle's sums over the sampled
+    channels."""
+    inp = synth.workload_inputs(2)
+    B, L, d, N = 4, 8192, 4096, 16
+    ch = np.r_[3, 64, 1000, 4095]
+    dy = np.zeros((B, L, d), np.float32)
+    dy[:, :, ch] = (np.random.default_rng(31).standard_normal((B, L, ch.size)) * 0.1).astype(np.float32)
+    g = run_bwd(inp, dy, None)
+    ref, mag = oracle_bwd(inp, dy, None, channels=ch)
+    for k in ("dB", "dC"):
+        report(f"bwd 1.4b layer {k} (dy on {ch.size} channels)",
+               oracle.scaled_error(download(g[k]), ref[k], mag[k]), tol_for("bf16", "f32"))
+    compare("bwd 1.4b layer, dy on sampled channels", g, ref, mag, tol_for("bf16", "f32"), channels=ch,
+            skip=("dB", "dC"))
+
+
 def test_bwd_empty_sequence_and_deterministic():
     B, d, N = 2, 40, 16
     inp = synth.make_scan_inputs(B, 0, d, N, "f32", seed=27, stream=2700)
