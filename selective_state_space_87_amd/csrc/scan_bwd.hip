@@ -317,25 +317,10 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   // with the lane's high bits, so a wave's 64 stores fall on distinct banks
   // (slot lane * W + w alone put every (64 / W)-th lane on one bank).
   const int pslot = lane * W + (w ^ ((lane / (64 / W)) & (W - 1)));
-  if (nt > 0) {
-    fetch2(nt - 1);
-    stage2(nt - 1);
-  }
-  __syncthreads();
-  for (int k = nt - 1; k >= 0; --k) {
+  // Recompute tile k from its checkpoint (hh) and run the adjoint through
+  // it: the per-wave partials go to sP/sG/sU, the dB/dC partials to memory.
+  auto compute_tile = [&](int k, float (&hh)[S]) __attribute__((always_inline)) {
     const int qb = k & 1, pb = NB == 2 ? (k & 1) : 0;
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      e_dy[i] = n_dy[i];
-      e_dsilu[i] = n_dsilu[i];
-      e_dsp[i] = n_dsp[i];
-      e_u[i] = n_u[i];
-      e_dp[i] = n_dp[i];
-    }
-    float hh[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) hh[s] = r_ck[s];
-    if (k > 0) fetch2(k - 1);
     // -- waves: recompute the tile, then the adjoint recurrence
     float dtv[T], dtu[T], dpv[T], uvv[T];
 #pragma unroll
@@ -399,9 +384,11 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       buffer_store_f32<false>(r, rdB_b, lead && which == 0 ? off : kOutOfRange);
       buffer_store_f32<false>(r, rdC_b, lead && which == 1 ? off : kOutOfRange);
     }
-    // -- staging of tile k-1 (the other buffers), then the epilogue of tile k
-    if (k > 0) stage2(k - 1);
-    __syncthreads();
+  };
+  // Per-item epilogue of tile kt (its partials complete, its items in e_*).
+  // For kt past the last tile every store is masked.
+  auto epilogue = [&](int kt) __attribute__((always_inline)) {
+    const int pbuf = NB == 2 ? (kt & 1) : 0;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int tt = item_step(i);
@@ -410,13 +397,13 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       const bool live = T >= W || tt < T;
       {
         const int tr = live ? tt : 0;
-        const int t = k * T + tt;
+        const int t = kt * T + tt;
         float pre = 0.0f, ddt = 0.0f, dus = 0.0f;
 #pragma unroll
         for (int q = 0; q < W; ++q) {
-          pre += sP[pb][tr][lane * W + q];
-          ddt += sG[pb][tr][lane * W + q];
-          dus += sU[pb][tr][lane * W + q];
+          pre += sP[pbuf][tr][lane * W + q];
+          ddt += sG[pbuf][tr][lane * W + q];
+          dus += sU[pbuf][tr][lane * W + q];
         }
         const bool ok = live && ch_ok && t < L;
         const uint32_t off = ok ? static_cast<uint32_t>((t * Dm + ch) * 4) : kOutOfRange;
@@ -429,7 +416,70 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         dbias_acc += ok ? dd : 0.0f;
       }
     }
-    if constexpr (NB == 1) __syncthreads();
+  };
+  // Items of the tile after the one being finished.
+  float m_dy[IT] = {}, m_dsilu[IT] = {}, m_dsp[IT] = {}, m_u[IT] = {}, m_dp[IT] = {};
+
+  if (nt > 0) {
+    fetch2(nt - 1);
+    stage2(nt - 1);
+  }
+  __syncthreads();
+  if constexpr (NB == 2) {
+    // One barrier per tile. Iteration k computes tile k, stages tile k-1
+    // and finishes tile k+1 (whose partials were complete at the previous
+    // barrier). Waves w and w+4, which share a SIMD, take opposite orders
+    // (finish first, or compute first), so that one's recurrence overlaps
+    // the other's per-item work; the recurrence runs at raised priority.
+    const bool late = (w >> 2) & 1;
+    for (int k = nt - 1; k >= 0; --k) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        e_dy[i] = m_dy[i], e_dsilu[i] = m_dsilu[i], e_dsp[i] = m_dsp[i], e_u[i] = m_u[i], e_dp[i] = m_dp[i];
+        m_dy[i] = n_dy[i], m_dsilu[i] = n_dsilu[i], m_dsp[i] = n_dsp[i], m_u[i] = n_u[i], m_dp[i] = n_dp[i];
+      }
+      float hh[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) hh[s] = r_ck[s];
+      if (k > 0) fetch2(k - 1);
+      if (late) {
+        epilogue(k + 1);
+        __builtin_amdgcn_s_setprio(2);
+        compute_tile(k, hh);
+        __builtin_amdgcn_s_setprio(0);
+        if (k > 0) stage2(k - 1);
+      } else {
+        __builtin_amdgcn_s_setprio(2);
+        compute_tile(k, hh);
+        __builtin_amdgcn_s_setprio(0);
+        if (k > 0) stage2(k - 1);
+        epilogue(k + 1);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      e_dy[i] = m_dy[i], e_dsilu[i] = m_dsilu[i], e_dsp[i] = m_dsp[i], e_u[i] = m_u[i], e_dp[i] = m_dp[i];
+    }
+    if (nt > 0) epilogue(0);
+  } else {
+    // Single partial buffers: compute, stage the next tile, barrier,
+    // finish this tile, barrier.
+    for (int k = nt - 1; k >= 0; --k) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        e_dy[i] = n_dy[i], e_dsilu[i] = n_dsilu[i], e_dsp[i] = n_dsp[i], e_u[i] = n_u[i], e_dp[i] = n_dp[i];
+      }
+      float hh[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) hh[s] = r_ck[s];
+      if (k > 0) fetch2(k - 1);
+      compute_tile(k, hh);
+      if (k > 0) stage2(k - 1);
+      __syncthreads();
+      epilogue(k);
+      __syncthreads();
+    }
   }
 
   // ---------------------------------------------------------------- per-block outputs
