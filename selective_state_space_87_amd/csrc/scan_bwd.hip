@@ -140,7 +140,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   // overwriting this tile's before the epilogue has read them.
   constexpr int NB = 2 * 3 * T * 64 * W * 4 + 2 * T * 64 * 16 <= 150 * 1024 ? 2 : 1;
   __shared__ float4 sQ[2][T][64];                    // (dt, dt*u, dp, u) per step, channel
-  __shared__ uint32_t sBC[2][NS][T * WPS];           // packed B/C of the tile
+  __shared__ float2 sBC[2][NS][T];                   // (B, C) of the tile, unpacked once at staging
   __shared__ float sP[NB][T][64 * W];                // readout partials (pre-gate output)
   __shared__ float sG[NB][T][64 * W];                // ddt partials
   __shared__ float sU[NB][T][64 * W];                // du partials
@@ -226,22 +226,28 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       r_bc[j] = __builtin_amdgcn_raw_buffer_load_b32(rbc_b, off, 0, 0);
     }
   };
+  // A packed word holds (B, C) as bfloat16 (B in the high half), or one of
+  // the two as float32 (B first); it is unpacked once here, not by every
+  // wave that reads it.
   auto stage_bc = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < BCW; ++j) {
       const int idx = threadIdx.x + j * W * 64;
-      if (idx < NS * T * WPS) sBC[qb][idx / (T * WPS)][idx % (T * WPS)] = r_bc[j];
+      if (idx < NS * T * WPS) {
+        const int n = idx / (T * WPS), q = idx % (T * WPS);
+        const uint32_t wd = r_bc[j];
+        if constexpr (BF16_IN) {
+          sBC[qb][n][q] = make_float2(__uint_as_float(wd & 0xffff0000u), __uint_as_float(wd << 16));
+        } else {
+          reinterpret_cast<float*>(&sBC[qb][n][0])[q] = __uint_as_float(wd);
+        }
+      }
     }
   };
   auto bc_of = [&](int qb, int n, int t, float& bval, float& cval) __attribute__((always_inline)) {
-    if constexpr (BF16_IN) {
-      const uint32_t wd = sBC[qb][n][t];
-      bval = __uint_as_float(wd & 0xffff0000u);
-      cval = __uint_as_float(wd << 16);
-    } else {
-      bval = __uint_as_float(sBC[qb][n][2 * t]);
-      cval = __uint_as_float(sBC[qb][n][2 * t + 1]);
-    }
+    const float2 v = sBC[qb][n][t];
+    bval = v.x;
+    cval = v.y;
   };
   // Step size of item i of tile k from the fetched raw delta (0 beyond L).
   auto step_size = [&](int k, int i, float& x_out) __attribute__((always_inline)) -> float {
