@@ -87,6 +87,113 @@ def counter_traffic(profile_name, src_hash):
     return float(m_b.group(1))
 
 
+# The engine clock takes tens of milliseconds of load to reach its steady
+# state; a run that times its steps right after a few warm-up calls measures
+# part of the ramp. Every timed region below is therefore preceded by this
+# much wall time of the same launches (on top of the requested warm-up).
+SETTLE_S = 0.5
+
+
+def settle(torch, fn, seconds):
+    """Launch fn back to back for `seconds` of wall time; return the count."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
+def timed_steps(torch, stream, fn, steps):
+    """Time exactly `steps` calls of fn with an event between consecutive
+    calls on `stream`: (wall ms per call, event ms per call, median event ms)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return wall_ms, ev[0].elapsed_time(ev[steps]) / steps, per[len(per) // 2]
+
+
+def _oracle_block(args):
+    """Pool worker: the float64 oracle on channels [c0, c1) of the scan inputs
+    held in shared memory (storage form), single-threaded. Returns seconds."""
+    import numpy as np
+    from multiprocessing import shared_memory
+    from threadpoolctl import threadpool_limits
+
+    import oracle   # NumPy only (the package, which imports torch, is not loaded here)
+
+    def widen(a):
+        if dtype == "bf16":
+            return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return a.astype(np.float64)
+
+    names, shapes, dtype, c0, c1, steps, small = args
+    shms = {k: shared_memory.SharedMemory(name=n) for k, n in names.items()}
+    try:
+        st = np.uint16 if dtype == "bf16" else np.float32
+        arr = {k: np.ndarray(shapes[k], dtype=st, buffer=shms[k].buf) for k in names}
+        sl = {k: widen(np.ascontiguousarray(arr[k][:, :steps, c0:c1])) for k in ("u", "delta", "z")}
+        for k in ("B", "C"):
+            sl[k] = widen(np.ascontiguousarray(arr[k][:, :steps]))
+        A, D, bias = (np.asarray(v, dtype=np.float64) for v in small)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.selective_scan(sl["u"], sl["delta"], A[c0:c1], sl["B"], sl["C"], D=D[c0:c1], z=sl["z"],
+                                  delta_bias=bias[c0:c1], delta_softplus=True)
+            return time.perf_counter() - t0
+    finally:
+        for m in shms.values():
+            m.close()
+
+
+def cpu_pool_baseline(inp, cores):
+    """The oracle over independent channel blocks on `cores` processes (all of
+    the workload's steps): (seconds of wall time, state updates)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from multiprocessing import shared_memory
+
+    import numpy as np
+
+    dt = inp["in_dtype"]
+    Bt, L, d = inp["u"].shape
+    N = inp["A"].shape[1]
+    names, shapes, shms = {}, {}, []
+    try:
+        for k in ("u", "delta", "z", "B", "C"):
+            a = np.ascontiguousarray(inp[k])
+            m = shared_memory.SharedMemory(create=True, size=a.nbytes)
+            shms.append(m)
+            np.ndarray(a.shape, dtype=a.dtype, buffer=m.buf)[...] = a
+            names[k], shapes[k] = m.name, a.shape
+        small = (inp["A"], inp["D"], inp["delta_bias"])
+        blocks = 4 * cores
+        edges = [d * i // blocks for i in range(blocks + 1)]
+        tasks = [(names, shapes, dt, edges[i], edges[i + 1], L, small) for i in range(blocks) if edges[i + 1] > edges[i]]
+        # Fresh interpreters (spawn): the workers hold no GPU state. A worker
+        # that dies raises here (BrokenProcessPool) instead of being replaced.
+        with ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn")) as pool:
+            list(pool.map(_oracle_block, [(names, shapes, dt, 0, 1, 16, small)] * cores, timeout=300))
+            t0 = time.perf_counter()
+            list(pool.map(_oracle_block, tasks, timeout=600))
+            wall = time.perf_counter() - t0
+    finally:
+        for m in shms:
+            m.close()
+            m.unlink()
+    return wall, Bt * L * d * N
+
+
 def cpu_baseline(inp, sample_steps):
     """The float64 oracle, as it stands, on the first `sample_steps` time steps
     of the same workload (all batches, channels and states)."""
@@ -116,10 +223,19 @@ def cpu_baseline(inp, sample_steps):
                 break
     except OSError:
         pass
-    return {"value": ups / t / 1e9, "unit": UNIT, "cores": 1, "kind": "oracle",
-            "sample": f"float64 NumPy oracle, first {S} of {inp['u'].shape[1]} time steps of the same "
-                      f"workload (B={Bt}, d={d}, N={N}; {ups:.3e} state updates) in {t:.1f} s on one "
-                      f"thread of {cpu}"}
+    one = {"value": ups / t / 1e9, "unit": UNIT, "cores": 1, "kind": "oracle",
+           "sample": f"float64 NumPy oracle, first {S} of {inp['u'].shape[1]} time steps of the same "
+                     f"workload (B={Bt}, d={d}, N={N}; {ups:.3e} state updates) in {t:.1f} s on one "
+                     f"thread of {cpu}"}
+    # All the cores this process may use (at most 16, the host share of one
+    # GPU): a process pool over independent channel blocks, every time step.
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    wall, ups_all = cpu_pool_baseline(inp, cores)
+    return {"value": ups_all / wall / 1e9, "unit": UNIT, "cores": cores, "kind": "oracle",
+            "sample": f"float64 NumPy oracle over all {inp['u'].shape[1]} time steps of the same workload "
+                      f"(B={Bt}, d={d}, N={N}; {ups_all:.3e} state updates), {4 * cores} channel blocks on a "
+                      f"pool of {cores} single-threaded processes, {wall:.1f} s wall on {cpu}",
+            "single_thread": one}
 
 
 def bench_scan(args, torch, binding, synth):
@@ -150,16 +266,8 @@ def bench_scan(args, torch, binding, synth):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    kern_ms = e0.elapsed_time(e1) / args.steps
+    settled = settle(torch, step, SETTLE_S)
+    wall_ms, kern_ms, kern_med_ms = timed_steps(torch, stream, step, args.steps)
 
     # Cold-cache kernel time: flush the 256 MB MALL and the L2s before each launch.
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -173,7 +281,7 @@ def bench_scan(args, torch, binding, synth):
         torch.cuda.synchronize()
         cold.append(c0.elapsed_time(c1))
     del flush
-    return w, inp, wall_ms, kern_ms, sorted(cold)[1]
+    return w, inp, wall_ms, kern_ms, sorted(cold)[1], kern_med_ms, settled
 
 
 def bench_decode(args, torch, binding, synth):
@@ -191,6 +299,7 @@ def bench_decode(args, torch, binding, synth):
     for _ in range(5):
         step()
     torch.cuda.synchronize()
+    settle(torch, step, 0.2)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.decode_steps):
@@ -230,11 +339,12 @@ def conv_alg_bytes(B, L, d, K, in_bytes, out_bytes):
     return B * L * d * (in_bytes + out_bytes) + d * K * 4 + d * 4 + 2 * B * d * (K - 1) * 4
 
 
-def _timed(torch, fn, reps, warm):
+def _timed(torch, fn, reps, warm, settle_s=0.2):
     stream = torch.cuda.current_stream()
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
+    settle(torch, fn, settle_s)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
@@ -446,6 +556,87 @@ def bench_bwd(args, torch, binding, synth, inp):
                          "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
 
 
+def alu_roofline(slots, us):
+    ach = slots / (us * 1e-6) / 1e12
+    return {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_SLOTS / 1e12, "unit": "Tslot/s",
+            "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}
+
+
+def bench_workload(args, torch, binding, synth, wid, steps):
+    """Another named scan workload (the 130M-shaped layer, the long sequence),
+    timed like the headline: HIP events on the launch stream around each call
+    (B/C pre-pass, and for a chunked plan the summary pass and carry fold too)."""
+    import numpy as np
+    w = synth.WORKLOADS[wid]
+    inp = synth.workload_inputs(wid)
+    dev = torch.device("cuda:0")
+    dt = inp["in_dtype"]
+
+    def up(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t = {k: up(inp[k], dt) for k in ("u", "delta", "B", "C", "z")}
+    for k in ("A", "D", "delta_bias"):
+        t[k] = up(inp[k], "f32")
+    del inp
+    out_dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    y = torch.empty(w.batch, w.seqlen, w.dim, dtype=out_dtype, device=dev)
+    hf = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev) if w.final_state else None
+    ws = torch.empty(max(1, binding.ssm_scan_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.ssm_selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                       delta_bias=t["delta_bias"], delta_softplus=True, y=y, h_final=hf,
+                                       out_dtype=out_dtype, workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    step()
+    torch.cuda.synchronize()
+    settle(torch, step, 0.3)
+    _, us_ms, med_ms = timed_steps(torch, stream, step, steps)
+    us = us_ms * 1e3
+    ups = w.updates
+    slots = ups * SLOTS_PER_UPDATE + w.batch * w.seqlen * w.dim * SLOTS_PER_BLD
+    return {"workload": f"{w.name} (batch={w.batch}, seqlen={w.seqlen}, d_inner={w.dim}, d_state={w.dstate}, "
+                        f"{w.in_dtype} in/out, softplus, gate)",
+            "us_per_call": us, "median_us": med_ms * 1e3,
+            "chunks": binding.ssm_scan_chunks(w.batch, w.seqlen, w.dim, w.dstate),
+            "G_updates_per_s": ups / (us * 1e-6) / 1e9, "roofline": alu_roofline(slots, us),
+            "hbm_frac": scan_alg_bytes(w.batch, w.seqlen, w.dim, w.dstate, 2, 2, w.final_state)
+                        / (us * 1e-6) / HBM_BPS}
+
+
+def valu_probe():
+    """Issue rates the VALU roofline assumes, measured on this device by
+    libssm_probe.so (include/ssm_probe.h)."""
+    import ctypes
+
+    class Rates(ctypes.Structure):
+        _fields_ = [("exp", ctypes.c_double), ("fma", ctypes.c_double), ("mix", ctypes.c_double),
+                    ("mix2", ctypes.c_double), ("copy", ctypes.c_double), ("cus", ctypes.c_int),
+                    ("clock_khz", ctypes.c_int)]
+
+    path = os.path.join(ROOT, "selective_state_space_87_amd", "lib", "libssm_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.ssm_probe_valu.restype = ctypes.c_int
+    r = Rates()
+    rc = lib.ssm_probe_valu(ctypes.byref(r))
+    if rc != 0:
+        return {"error": f"ssm_probe_valu returned {rc}"}
+    peak = r.cus * SLOTS_PER_CLK_CU * r.clock_khz * 1e3
+    return {"cus": r.cus, "clock_GHz": r.clock_khz / 1e6, "peak_Tslot_per_s": peak / 1e12,
+            "exp_T_per_s": r.exp / 1e12, "exp_frac_of_slot_peak": r.exp / peak,
+            "fma_T_per_s": r.fma / 1e12, "fma_frac_of_slot_peak": r.fma / peak,
+            "scan_mix_frac_8_waves_per_simd": r.mix / peak,
+            "scan_mix_frac_2_waves_per_simd": r.mix2 / peak,
+            "copy_GBps": r.copy / 1e9,
+            "model": "64 lane-slots per clock per CU; v_exp_f32 2 slots, FMA-pipe ops 1; a 6-slot update "
+                     "(2 mul, exp, 2 fma) reaches the peak at full occupancy"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,6 +647,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the 130M-shaped and long-sequence scans")
+    ap.add_argument("--no-probe", action="store_true", help="skip the VALU / copy rate probes")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
@@ -491,7 +684,7 @@ def main():
 
     if args.copy_calibration_mib > 0:
         copy_calibration(torch, args.copy_calibration_mib)
-    w, inp, wall_ms, kern_ms, cold_ms = bench_scan(args, torch, binding, synth)
+    w, inp, wall_ms, kern_ms, cold_ms, kern_med_ms, settled = bench_scan(args, torch, binding, synth)
     ups = w.updates
     value = ups / (wall_ms * 1e-3) / 1e9
     in_b = 2 if w.in_dtype == "bf16" else 4
@@ -520,7 +713,9 @@ def main():
                    "out_dtype": w.in_dtype, "delta_softplus": True, "gate": w.gate,
                    "final_state": w.final_state},
         "kernel_ms": kern_ms,
+        "kernel_median_ms": kern_med_ms,
         "cold_kernel_ms": cold_ms,
+        "clock_settle": {"seconds": SETTLE_S, "calls": settled},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "Tslot/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "alg_slots_per_launch": alg_slots, "alg_bytes_per_launch": alg_bytes,
@@ -528,6 +723,11 @@ def main():
                      "hbm_frac": alg_bytes / (kern_ms * 1e-3) / HBM_BPS,
                      "source_hash": src_hash},
     }
+    if not args.no_workloads:
+        result["mamba130m"] = bench_workload(args, torch, binding, synth, 1, 50)
+        result["long_sequence"] = bench_workload(args, torch, binding, synth, 3, 5)
+    if not args.no_probe:
+        result["valu_probe"] = valu_probe()
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, binding, synth)
     if not args.no_zoh:

@@ -9,6 +9,7 @@ fallback. A missing library, a CPU tensor or a non-zero status raises.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -117,6 +118,26 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _launch_context(device, stream):
+    """The device current, and the stream the kernels are enqueued on current
+    too: what the binding allocates here (outputs, workspace) is then owned by
+    that stream in torch's caching allocator, so a workspace dropped after the
+    call is not handed to work on another stream while the kernels still use it."""
+    ctx = contextlib.ExitStack()
+    ctx.enter_context(torch.cuda.device(device))
+    if stream is not None:
+        ctx.enter_context(torch.cuda.stream(stream))
+    return ctx
+
+
+def _check_workspace(workspace, dev):
+    if workspace is None:
+        return 0
+    if not isinstance(workspace, torch.Tensor) or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace.numel() * workspace.element_size()
+
+
 def ssm_abi_version() -> int:
     return int(_load().ssm_abi_version())
 
@@ -172,22 +193,17 @@ def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     out_dtype = u.dtype if out_dtype is None else out_dtype
     if out_dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported output dtype {out_dtype}")
-    if y is None:
-        y = torch.empty((Bt, L, d), dtype=out_dtype, device=dev)
-    _dev_tensor("y", y, (Bt, L, d), (out_dtype,), dev)
-    if return_final_state and h_final is None:
-        h_final = torch.empty((Bt, d, N), dtype=torch.float32, device=dev)
-    _dev_tensor("h_final", h_final, (Bt, d, N), (torch.float32,), dev)
-    ws_bytes = int(lib.ssm_scan_workspace_bytes(Bt, L, d, N))
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    if workspace is not None:
-        if workspace.device != dev or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
-        ws_size = workspace.numel() * workspace.element_size()
-    else:
-        ws_size = 0
-    with torch.cuda.device(dev):
+    with _launch_context(dev, stream):
+        if y is None:
+            y = torch.empty((Bt, L, d), dtype=out_dtype, device=dev)
+        _dev_tensor("y", y, (Bt, L, d), (out_dtype,), dev)
+        if return_final_state and h_final is None:
+            h_final = torch.empty((Bt, d, N), dtype=torch.float32, device=dev)
+        _dev_tensor("h_final", h_final, (Bt, d, N), (torch.float32,), dev)
+        ws_bytes = int(lib.ssm_scan_workspace_bytes(Bt, L, d, N))
+        if workspace is None and ws_bytes > 0:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        ws_size = _check_workspace(workspace, dev)
         st = lib.ssm_selective_scan_fwd(
             Bt, L, d, N, _DTYPE_CODE[u.dtype], _DTYPE_CODE[out_dtype], _flags(delta_softplus, zoh),
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
@@ -226,10 +242,10 @@ def ssm_selective_state_update(state, x, delta, A, B, C, D=None, z=None, delta_b
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out_dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported output dtype {out_dtype}")
-    if y is None:
-        y = torch.empty((Bt, d), dtype=out_dtype, device=dev)
-    _dev_tensor("y", y, (Bt, d), (out_dtype,), dev)
-    with torch.cuda.device(dev):
+    with _launch_context(dev, stream):
+        if y is None:
+            y = torch.empty((Bt, d), dtype=out_dtype, device=dev)
+        _dev_tensor("y", y, (Bt, d), (out_dtype,), dev)
         st = lib.ssm_selective_state_update(
             Bt, d, N, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype], _flags(delta_softplus, zoh),
             _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -262,13 +278,13 @@ def ssm_causal_conv1d_fwd(x, weight, bias=None, state_in=None, silu_activation=T
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out_dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported output dtype {out_dtype}")
-    if y is None:
-        y = torch.empty((Bt, L, d), dtype=out_dtype, device=dev)
-    _dev_tensor("y", y, (Bt, L, d), (out_dtype,), dev)
-    if return_final_state and state_out is None:
-        state_out = torch.empty((Bt, d, K - 1), dtype=torch.float32, device=dev)
-    _dev_tensor("state_out", state_out, (Bt, d, K - 1), (torch.float32,), dev)
-    with torch.cuda.device(dev):
+    with _launch_context(dev, stream):
+        if y is None:
+            y = torch.empty((Bt, L, d), dtype=out_dtype, device=dev)
+        _dev_tensor("y", y, (Bt, L, d), (out_dtype,), dev)
+        if return_final_state and state_out is None:
+            state_out = torch.empty((Bt, d, K - 1), dtype=torch.float32, device=dev)
+        _dev_tensor("state_out", state_out, (Bt, d, K - 1), (torch.float32,), dev)
         st = lib.ssm_causal_conv1d_fwd(Bt, L, d, K, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype],
                                        int(bool(silu_activation)), _ptr(x), _ptr(weight), _ptr(bias),
                                        _ptr(state_in), _ptr(y), _ptr(state_out), _stream_handle(stream, dev))
@@ -302,10 +318,10 @@ def ssm_causal_conv1d_update(state, x, weight, bias=None, silu_activation=True, 
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out_dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported output dtype {out_dtype}")
-    if y is None:
-        y = torch.empty((Bt, d), dtype=out_dtype, device=dev)
-    _dev_tensor("y", y, (Bt, d), (out_dtype,), dev)
-    with torch.cuda.device(dev):
+    with _launch_context(dev, stream):
+        if y is None:
+            y = torch.empty((Bt, d), dtype=out_dtype, device=dev)
+        _dev_tensor("y", y, (Bt, d), (out_dtype,), dev)
         st = lib.ssm_causal_conv1d_update(Bt, d, K, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype],
                                           int(bool(silu_activation)), _ptr(state), _ptr(x), _ptr(weight),
                                           _ptr(bias), _ptr(y), _stream_handle(stream, dev))
@@ -347,19 +363,19 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=Non
     _dev_tensor("dy", dy, (Bt, L, d), f32, dev)
     _dev_tensor("dh_final", dh_final, (Bt, d, N), f32, dev)
     new = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)  # noqa: E731
-    g = dict(du=new(Bt, L, d), ddelta=new(Bt, L, d), dA=new(d, N), dB=new(Bt, L, N), dC=new(Bt, L, N),
-             dh0=new(Bt, d, N))
-    if D is not None:
-        g["dD"] = new(d)
-    if z is not None:
-        g["dz"] = new(Bt, L, d)
-    if delta_bias is not None:
-        g["ddelta_bias"] = new(d)
-    ws_bytes = int(lib.ssm_scan_bwd_workspace_bytes(Bt, L, d, N))
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    with torch.cuda.device(dev):
+    with _launch_context(dev, stream):
+        g = dict(du=new(Bt, L, d), ddelta=new(Bt, L, d), dA=new(d, N), dB=new(Bt, L, N), dC=new(Bt, L, N),
+                 dh0=new(Bt, d, N))
+        if D is not None:
+            g["dD"] = new(d)
+        if z is not None:
+            g["dz"] = new(Bt, L, d)
+        if delta_bias is not None:
+            g["ddelta_bias"] = new(d)
+        ws_bytes = int(lib.ssm_scan_bwd_workspace_bytes(Bt, L, d, N))
+        if workspace is None and ws_bytes > 0:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        ws_size = _check_workspace(workspace, dev)
         st = lib.ssm_selective_scan_bwd(
             Bt, L, d, N, _DTYPE_CODE[u.dtype], _flags(delta_softplus, False),
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0),
@@ -401,13 +417,13 @@ def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False,
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out_dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported output dtype {out_dtype}")
-    if y is None:
-        y = torch.empty((Bt, L, H, P), dtype=out_dtype, device=dev)
-    _dev_tensor("y", y, (Bt, L, H, P), (out_dtype,), dev)
-    if return_final_state and h_final is None:
-        h_final = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
-    _dev_tensor("h_final", h_final, (Bt, H, P, N), (torch.float32,), dev)
-    with torch.cuda.device(dev):
+    with _launch_context(dev, stream):
+        if y is None:
+            y = torch.empty((Bt, L, H, P), dtype=out_dtype, device=dev)
+        _dev_tensor("y", y, (Bt, L, H, P), (out_dtype,), dev)
+        if return_final_state and h_final is None:
+            h_final = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
+        _dev_tensor("h_final", h_final, (Bt, H, P, N), (torch.float32,), dev)
         st = lib.ssm_ssd_fwd(Bt, L, H, P, N, _DTYPE_CODE[x.dtype], _DTYPE_CODE[out_dtype],
                              _flags(dt_softplus, False), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                              _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _stream_handle(stream, dev))

@@ -82,6 +82,13 @@ ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
   p.S = p.NS / p.W;
   p.Lp = round_up(seqlen, kPadSteps);
   p.dim_blocks = ceil_div(dim, 64);
+  // The kernel also addresses one batch row's packed B/C words (up to two per
+  // step and state, float32 inputs) and one row of the per-block dB / dC
+  // partials ([Lp][NS] floats) through 32-bit buffer offsets.
+  if (int64_t(p.NS) * p.Lp * 8 > kPlaneBytesMax || int64_t(p.NS) * p.Lp * 4 > kPlaneBytesMax) {
+    p.ok = false;
+    return p;
+  }
   const int64_t tiles = p.Lp / (p.NS == 16 ? 8 : 16);  // the forward's tile length for this NS
   size_t off = 0;
   p.off_bc = off;

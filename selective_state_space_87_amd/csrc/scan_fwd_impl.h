@@ -26,7 +26,13 @@
 //     readouts in a fixed order, + D u, * silu(z), store) and prepares later
 //     tiles (softplus step size and dt*u into an LDS ring; D u and the gate in
 //     registers). Per-(b, l, d) work is done once, not once per wave. Global
-//     loads of u, delta and z run four tiles ahead.
+//     loads of u, delta and z run two tiles ahead of the preparation.
+// At eight waves with scalar B/C (N = 16) the block synchronises once every
+// two tiles ("pair barriers"): step sizes are prepared four tiles ahead and a
+// tile is read out two tiles after its recurrence, so that everything read
+// between two barriers was written before the first of them. Elsewhere there
+// is one barrier per tile, with a preparation two tiles ahead and a readout
+// one tile behind.
 // The two waves sharing a SIMD take the two phases in opposite orders (see
 // iter). There is no MFMA: this is not a dense contraction. The kernel is
 // bound by the VALU (one v_exp_f32 per state update plus 4 FMA-pipe ops).
@@ -119,13 +125,25 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr bool BCL = bc_in_lds(NS);
   constexpr int NT = W * 64;                        // threads
   constexpr int EB = BCL ? (T * NS + NT - 1) / NT : 1;  // B/C elements per thread per tile
+  // Pair barriers (eight waves of 8-step tiles, scalar B/C): one barrier
+  // every two tiles. Step sizes are then prepared four tiles ahead (a ring of
+  // 8 tile slots), and each tile is read out two tiles after its recurrence
+  // (4 partial buffers); D*u and the gate wait in 8 register sets. Otherwise
+  // one barrier per tile, a ring of 4 slots, 2 partial buffers and 4 sets.
+  // (Measured at (4, 8192, 4096, 16) bf16: 608 -> 584 us.)
+  constexpr bool PB = W == 8 && T == 8 && !BCL;
+  constexpr int RING = PB ? 8 : 4;
+  constexpr int NPB = PB ? 4 : 2;
+  constexpr int LAG = PB ? 2 : 1;
+  constexpr int UNR = PB ? 8 : 4;
 
-  // Step sizes live in a ring of 4 tile slots (tile k in slot k & 3): tiles
-  // are prepared two at a time, every other tile. Partial readouts are
-  // double-buffered by tile parity. One barrier per tile separates every
-  // writer from every reader.
-  __shared__ float2 sDD[4][T][64];                  // (dt, dt*u), or (dt, u) with ZOH
-  __shared__ __attribute__((aligned(16))) float sP[READOUT ? 2 : 1][T][READOUT ? 64 * W : 1];
+  // Step sizes live in a ring of RING tile slots (tile k in slot k % RING):
+  // tiles are prepared two at a time, every other tile. Partial readouts
+  // rotate over NPB buffers (tile k in k % NPB). A barrier after every tile,
+  // or after every odd tile with pair barriers, separates every writer from
+  // every reader.
+  __shared__ float2 sDD[RING][T][64];               // (dt, dt*u), or (dt, u) with ZOH
+  __shared__ __attribute__((aligned(16))) float sP[READOUT ? NPB : 1][T][READOUT ? 64 * W : 1];
   // LDS-staged B/C: (B, C) per step and state, a ring of 4 tile slots like
   // the step sizes. Every lane of a wave reads the same entry (a broadcast).
   __shared__ __attribute__((aligned(16))) float2 sBC[BCL ? 4 : 1][BCL ? T : 1][BCL ? NS : 1];
@@ -227,10 +245,10 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // Cooperative items of this thread: step w + W*i of each tile, channel ch.
   // Raw inputs (storage bits) are fetched two tiles at a time into two
   // register sets (set = tile parity); D*u and the gate of a tile wait until
-  // its readout, up to three tiles later (four sets, set = tile & 3).
+  // its readout, up to RING - 1 tiles later (RING sets, set = tile % RING).
   storage_t<BF16_IN> ru[2][IT], rd[2][IT], rz[2][IT];
   storage_t<BF16_IN> rbB[BCL ? 2 : 1][EB], rbC[BCL ? 2 : 1][EB];
-  float eDu[4][IT], eG[4][IT];
+  float eDu[RING][IT], eG[RING][IT];
 
   auto load_raw = [&](int k, auto set) __attribute__((always_inline)) {
     constexpr int R = decltype(set)::value;
@@ -390,12 +408,12 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
         h[s] = fmaf(abar, h[s], bu);
         if constexpr (READOUT) acc = fmaf(cval, h[s], acc);
       }
-      if constexpr (READOUT) sP[P][t][wpos] = acc;
+      if constexpr (READOUT) sP[J % NPB][t][wpos] = acc;
       if constexpr (SUMMARY) dt_sum += dd[t].x;
     }
   };
 
-  // Tile k with J = k & 3 (P = k & 1). Its step sizes are already in
+  // Tile k with J = k % UNR (P = k & 1). Its step sizes are already in
   // registers (read during tile k-1) and its B/C in SGPR set P (fetched
   // during tile k-1). The work of a tile, in the order of the "early" waves:
   //   (1) scalar fetch of tile k+1's B/C; first half of the recurrence;
@@ -403,9 +421,10 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   //       (waited on after the second half, when the scalar fetch is long
   //       done);
   //   (3) second half of the recurrence;
-  //   (4) readout of tile k-1 (stored on odd tiles, two tiles at a time); on
-  //       even tiles, preparation of tiles k+2 and k+3 and the fetch of the
-  //       raw inputs of tiles k+4 and k+5.
+  //   (4) readout of tile k-LAG (stored on odd tiles, two tiles at a time);
+  //       on even tiles, preparation of two tiles (k+2 and k+3, or k+4 and
+  //       k+5 with pair barriers) and the fetch of the raw inputs of the two
+  //       after them.
   // "Late" waves run (2), (4), (1), (3): the readout and the preparation
   // first, then the whole recurrence. A wave raises its issue priority while
   // it runs the recurrence, so the SIMD's arbiter prefers it over the other
@@ -413,11 +432,11 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // different orders, so while one runs the recurrence the other runs the
   // cooperative work, instead of both waiting on the same phase. Every
   // dependency is on data written before the previous barrier, so both
-  // orders are valid. One barrier per tile.
+  // orders are valid.
   auto lds_reads = [&](auto jj, float2 (&dd_next)[T], float (&gp)[IT][GN][GW]) __attribute__((always_inline)) {
     constexpr int J = decltype(jj)::value;
-    constexpr int Q = 1 - (J & 1);
-    read_dd(dd_next, std::integral_constant<int, (J + 1) & 3>{});
+    constexpr int Q = (J + NPB - LAG) % NPB;        // partials of tile k - LAG
+    read_dd(dd_next, std::integral_constant<int, (J + 1) % RING>{});
     if constexpr (READOUT) {
 #pragma unroll
       for (int i = 0; i < IT; ++i) gather_load(std::integral_constant<int, Q>{}, i, gp[i]);
@@ -427,11 +446,12 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     constexpr int J = decltype(jj)::value;
     constexpr int P = J & 1;
     if constexpr (READOUT) {
-      // Readout of tile k-1 (out of range at k = 0: the stores are dropped).
+      // Readout of tile k - LAG (out of range for k < LAG: the stores are dropped).
+      constexpr int E = (J + RING - LAG) % RING;
 #pragma unroll
       for (int i = 0; i < IT; ++i) {
-        yv[P][i] = (gather_sum(gp[i]) + eDu[(J + 3) & 3][i]) * eG[(J + 3) & 3][i];
-        yo[P][i] = lane_out + step_off(k - 1, i, OUT_B);
+        yv[P][i] = (gather_sum(gp[i]) + eDu[E][i]) * eG[E][i];
+        yo[P][i] = lane_out + step_off(k - LAG, i, OUT_B);
       }
       if constexpr (P == 1) {
 #pragma unroll
@@ -441,7 +461,14 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
         }
       }
     }
-    if constexpr (P == 0) {
+    if constexpr (PB) {
+      if constexpr (P == 0) {
+        prepare(k + 4, std::integral_constant<int, (J + 4) % RING>{});
+        prepare(k + 5, std::integral_constant<int, (J + 5) % RING>{});
+        load_raw(k + 6, std::integral_constant<int, 0>{});
+        load_raw(k + 7, std::integral_constant<int, 1>{});
+      }
+    } else if constexpr (P == 0) {
       prepare(k + 2, std::integral_constant<int, (J + 2) & 3>{});
       prepare(k + 3, std::integral_constant<int, (J + 3) & 3>{});
       load_raw(k + 4, std::integral_constant<int, 0>{});
@@ -494,7 +521,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       __builtin_amdgcn_sched_barrier(0);
       coop(k, jj, gp);
     }
-    __syncthreads();
+    if constexpr (!PB || (J & 1) == 1) __syncthreads();
   };
 
   float2 ddA[T], ddB[T];
@@ -509,6 +536,13 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     load_raw(2, std::integral_constant<int, 0>{});
     load_raw(3, std::integral_constant<int, 1>{});
+    if constexpr (PB) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      prepare(2, std::integral_constant<int, 2>{});
+      prepare(3, std::integral_constant<int, 3>{});
+      load_raw(4, std::integral_constant<int, 0>{});
+      load_raw(5, std::integral_constant<int, 1>{});
+    }
     if constexpr (READOUT) {
       // Out-of-range stores (dropped by the buffer unit) in the places of an
       // odd tile's output stores: loop entry then sees the same queue of
@@ -526,15 +560,20 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   }
   auto run = [&](auto late) __attribute__((always_inline)) {
     int k = 0;
-    for (; k + 3 < nt; k += 4) {
-      iter(k, std::integral_constant<int, 0>{}, late, ddA, ddB);
-      iter(k + 1, std::integral_constant<int, 1>{}, late, ddB, ddA);
-      iter(k + 2, std::integral_constant<int, 2>{}, late, ddA, ddB);
-      iter(k + 3, std::integral_constant<int, 3>{}, late, ddB, ddA);
+    for (; k + UNR - 1 < nt; k += UNR) {
+      static_for<0, UNR>([&](auto jj) __attribute__((always_inline)) {
+        constexpr int J = decltype(jj)::value;
+        if constexpr ((J & 1) == 0) iter(k + J, jj, late, ddA, ddB);
+        else iter(k + J, jj, late, ddB, ddA);
+      });
     }
-    if (k < nt) iter(k, std::integral_constant<int, 0>{}, late, ddA, ddB);
-    if (k + 1 < nt) iter(k + 1, std::integral_constant<int, 1>{}, late, ddB, ddA);
-    if (k + 2 < nt) iter(k + 2, std::integral_constant<int, 2>{}, late, ddA, ddB);
+    static_for<0, UNR - 1>([&](auto jj) __attribute__((always_inline)) {
+      constexpr int J = decltype(jj)::value;
+      if (k + J < nt) {
+        if constexpr ((J & 1) == 0) iter(k + J, jj, late, ddA, ddB);
+        else iter(k + J, jj, late, ddB, ddA);
+      }
+    });
   };
   // Two orders only where two waves of the block share each SIMD (eight
   // waves); elsewhere the second copy of the loop would cost registers.
@@ -550,26 +589,36 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
 
   if constexpr (READOUT) {
     if (nt > 0) {
-      // Held readout of tile nt-2 (when the last tile was even), then tile nt-1.
       const int last = nt - 1;
+      // Held readout of an even last iteration (tile last - LAG), still unstored.
       if ((last & 1) == 0) {
 #pragma unroll
         for (int i = 0; i < IT; ++i) buffer_store_f32<BF16_OUT>(yv[0][i], ry_b, yo[0][i]);
       }
-      float part[IT];
-      if (last & 1) {
+      // The last LAG tiles are read out here, after a barrier over their
+      // partials (the loop ends with one only after an odd tile, or after
+      // every tile without pair barriers).
+      if (PB && (last & 1) == 0) __syncthreads();
+      auto sel = [&](const float (&e)[RING][IT], int tile, int i) __attribute__((always_inline)) -> float {
+        float v = e[0][i];
+        static_for<1, RING>([&](auto r) __attribute__((always_inline)) {
+          if ((tile % RING) == decltype(r)::value) v = e[decltype(r)::value][i];
+        });
+        return v;
+      };
+      for (int tl = max(0, nt - LAG); tl < nt; ++tl) {
+        float part[IT];
+        static_for<0, NPB>([&](auto q) __attribute__((always_inline)) {
+          if ((tl % NPB) == decltype(q)::value) {
 #pragma unroll
-        for (int i = 0; i < IT; ++i) part[i] = gather_item(std::integral_constant<int, 1>{}, i);
-      } else {
+            for (int i = 0; i < IT; ++i) part[i] = gather_item(q, i);
+          }
+        });
 #pragma unroll
-        for (int i = 0; i < IT; ++i) part[i] = gather_item(std::integral_constant<int, 0>{}, i);
-      }
-      const int sl = last & 3;
-#pragma unroll
-      for (int i = 0; i < IT; ++i) {
-        const float du = sl == 0 ? eDu[0][i] : sl == 1 ? eDu[1][i] : sl == 2 ? eDu[2][i] : eDu[3][i];
-        const float g = sl == 0 ? eG[0][i] : sl == 1 ? eG[1][i] : sl == 2 ? eG[2][i] : eG[3][i];
-        buffer_store_f32<BF16_OUT>((part[i] + du) * g, ry_b, lane_out + step_off(last, i, OUT_B));
+        for (int i = 0; i < IT; ++i) {
+          buffer_store_f32<BF16_OUT>((part[i] + sel(eDu, tl, i)) * sel(eG, tl, i), ry_b,
+                                     lane_out + step_off(tl, i, OUT_B));
+        }
       }
     }
     if (p.h_final && ch_ok && c == static_cast<int>(gridDim.y) - 1) {

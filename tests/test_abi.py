@@ -221,6 +221,18 @@ def test_scan_bwd_validation(lib):
     assert need > 0 and lib.ssm_scan_bwd_workspace_bytes(1, 8, 4, 17) == 0
 
 
+def test_scan_bwd_refuses_long_rows_of_few_channels(lib):
+    """Long sequences over few channels pass the per-row [L, d] plane limit
+    but not the 32-bit offsets of a row's packed B/C words (up to 8 bytes per
+    step and state) or of its dB / dC partial rows (4 bytes per step and
+    state): such shapes have no workspace size and the call is refused."""
+    for (B, L, d, N) in ((1, 1 << 25, 8, 16), (1, 1 << 26, 4, 16), (2, 1 << 24, 16, 16)):
+        assert lib.ssm_scan_bwd_workspace_bytes(B, L, d, N) == 0
+        assert bwd(lib, B=B, L=L, d=d, N=N) == E_UNSUPPORTED
+    # just inside: 2^23 steps x 16 states x 8 bytes = 2^30
+    assert lib.ssm_scan_bwd_workspace_bytes(1, 1 << 23, 8, 16) > 0
+
+
 def test_flag_bits(lib):
     """SSM_FLAG_SOFTPLUS and SSM_FLAG_ZOH are the only flag bits; the
     backward takes softplus only (its gradients are those of k = dt)."""
