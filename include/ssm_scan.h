@@ -146,6 +146,30 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory at the time of the call
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): ssm_selective_scan_fwd with the same arguments except the
+ * workspace, which here is a device array of SSM_NOALLOC_SCRATCH_BYTES that
+ * the library owns, one per GPU, reserved from the first use of this entry
+ * point's code on that GPU until the process ends. The call allocates nothing.
+ *   - Shapes whose ssm_scan_workspace_bytes() exceeds SSM_NOALLOC_SCRATCH_BYTES
+ *     return SSM_E_WORKSPACE (checked before any launch).
+ *   - Every call on one GPU uses that GPU's single array: calls that may
+ *     overlap in time on one GPU (other streams, other threads) race and
+ *     must be serialised by the caller. Nothing in the array needs to start
+ *     at zero; a call keeps no state in it for the next one.
+ *   - Otherwise as ssm_selective_scan_fwd (same validation, results bitwise
+ *     equal to it for the same inputs).
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ssm_selective_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                   int in_dtype, int out_dtype, int flags,
+                                   const void* u, const void* delta, const float* A,
+                                   const void* B, const void* C, const float* D, const void* z,
+                                   const float* delta_bias, const float* h0,
+                                   void* y, float* h_final, void* stream);
+
+/*
  * Decode: one token's state update in place (ybb.press section 6.3; the
  * fixed-size ssm_state of the lyirs.cc notes). The step is the scan's step
  * for L = 1 with h0 = state and h_final = state:

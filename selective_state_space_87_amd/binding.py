@@ -59,6 +59,10 @@ def _load():
         lib.ssm_selective_scan_fwd.argtypes = [i64, i64, i64, i64, i32, i32, i32,
                                                vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                vp, vp, vp, sz, vp]
+        lib.ssm_selective_scan_fwd_noalloc.restype = i32
+        lib.ssm_selective_scan_fwd_noalloc.argtypes = [i64, i64, i64, i64, i32, i32, i32,
+                                                       vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                       vp, vp, vp]
         lib.ssm_selective_state_update.restype = i32
         lib.ssm_selective_state_update.argtypes = [i64, i64, i64, i32, i32, i32,
                                                    vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -212,6 +216,46 @@ def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if return_final_state or h_final is not None:
         return y, h_final
     return y
+
+
+def ssm_selective_scan_fwd_noalloc(u, delta, A, B, C, y, D=None, z=None, delta_bias=None,
+                                   delta_softplus=False, h0=None, h_final=None, stream=None, zoh=False):
+    """Selective scan forward with the library's own scratch array as its
+    workspace; see ssm_selective_scan_fwd_noalloc in include/ssm_scan.h.
+
+    Arguments as ssm_selective_scan_fwd, except that the output y (and h_final,
+    when wanted) must be given: nothing is allocated on this path. Returns y,
+    or (y, h_final).
+    """
+    lib = _load()
+    if not isinstance(u, torch.Tensor) or u.dim() != 3 or u.dtype not in _DTYPE_CODE:
+        raise ValueError("u must be a 3-d float32 or bfloat16 tensor [B, L, d]")
+    dev = u.device
+    Bt, L, d = u.shape
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be a 2-d tensor [d, N]")
+    N = A.shape[1]
+    ind = (u.dtype,)
+    _dev_tensor("u", u, (Bt, L, d), ind, dev)
+    _dev_tensor("delta", delta, (Bt, L, d), ind, dev)
+    _dev_tensor("A", A, (d, N), (torch.float32,), dev)
+    _dev_tensor("B", B, (Bt, L, N), ind, dev)
+    _dev_tensor("C", C, (Bt, L, N), ind, dev)
+    _dev_tensor("D", D, (d,), (torch.float32,), dev)
+    _dev_tensor("z", z, (Bt, L, d), ind, dev)
+    _dev_tensor("delta_bias", delta_bias, (d,), (torch.float32,), dev)
+    _dev_tensor("h0", h0, (Bt, d, N), (torch.float32,), dev)
+    if not isinstance(y, torch.Tensor) or y.dtype not in _DTYPE_CODE:
+        raise ValueError("y must be a float32 or bfloat16 tensor [B, L, d]")
+    _dev_tensor("y", y, (Bt, L, d), (y.dtype,), dev)
+    _dev_tensor("h_final", h_final, (Bt, d, N), (torch.float32,), dev)
+    with torch.cuda.device(dev):
+        st = lib.ssm_selective_scan_fwd_noalloc(
+            Bt, L, d, N, _DTYPE_CODE[u.dtype], _DTYPE_CODE[y.dtype], _flags(delta_softplus, zoh),
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            _ptr(h0), _ptr(y), _ptr(h_final), _stream_handle(stream, dev))
+    _check("ssm_selective_scan_fwd_noalloc", st)
+    return y if h_final is None else (y, h_final)
 
 
 def ssm_selective_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,

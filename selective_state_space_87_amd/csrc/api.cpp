@@ -79,13 +79,16 @@ int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
   return p.ok ? p.chunks : 0;
 }
 
-int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                           int in_dtype, int out_dtype, int flags,
-                           const void* u, const void* delta, const float* A,
-                           const void* B, const void* C, const float* D, const void* z,
-                           const float* delta_bias, const float* h0,
-                           void* y, float* h_final,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch of the scan forward; with `noalloc` the workspace
+// is the library's scratch array (workspace and workspace_bytes unused).
+int scan_fwd_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int in_dtype, int out_dtype,
+                   int flags, const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, const float* h0, void* y,
+                   float* h_final, void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
   if (dstate > kMaxScanState) return SSM_E_UNSUPPORTED;
   if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return SSM_E_DTYPE;
@@ -112,7 +115,12 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
     if (p && !aligned(p, 4)) return SSM_E_ALIGN;
   }
   const size_t need = plan.bytes;
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SSM_E_WORKSPACE;
+  if (noalloc) {
+    if (need > ssm::scan_scratch_bytes()) return SSM_E_WORKSPACE;
+    workspace = nullptr;  // a separate device allocation: overlaps nothing of the caller's
+  } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    return SSM_E_WORKSPACE;
+  }
 
   const Range ry = span(y, seqlen > 0 ? bld : 0, osz);
   const Range rhf = span(h_final, bdn, 4);
@@ -128,7 +136,7 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
     if (overlaps(rhf, inputs[i])) return SSM_E_ALIAS;
   }
   if (overlaps(rhf, rh0) && !(rhf.lo == rh0.lo && rhf.hi == rh0.hi)) return SSM_E_ALIAS;
-  const Range rws = span(workspace, need > 0 ? static_cast<int64_t>(need) : 0, 1);
+  const Range rws = span(workspace, (need > 0 && !noalloc) ? static_cast<int64_t>(need) : 0, 1);
   for (const Range& r : inputs) {
     if (overlaps(rws, r)) return SSM_E_ALIAS;
   }
@@ -155,7 +163,32 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   a.out_bf16 = out_dtype;
   a.delta_softplus = (flags & SSM_FLAG_SOFTPLUS) != 0;
   a.zoh = (flags & SSM_FLAG_ZOH) != 0;
-  return map_hip(ssm::launch_scan(a, stream));
+  return map_hip(noalloc ? ssm::launch_scan_noalloc(a, stream) : ssm::launch_scan(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           int in_dtype, int out_dtype, int flags,
+                           const void* u, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, const float* h0,
+                           void* y, float* h_final,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_fwd_entry(batch, seqlen, dim, dstate, in_dtype, out_dtype, flags, u, delta, A, B, C, D, z,
+                        delta_bias, h0, y, h_final, workspace, workspace_bytes, stream, false);
+}
+
+int ssm_selective_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                   int in_dtype, int out_dtype, int flags,
+                                   const void* u, const void* delta, const float* A,
+                                   const void* B, const void* C, const float* D, const void* z,
+                                   const float* delta_bias, const float* h0,
+                                   void* y, float* h_final, void* stream) {
+  return scan_fwd_entry(batch, seqlen, dim, dstate, in_dtype, out_dtype, flags, u, delta, A, B, C, D, z,
+                        delta_bias, h0, y, h_final, nullptr, 0, stream, true);
 }
 
 int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,

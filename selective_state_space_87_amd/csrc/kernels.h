@@ -156,6 +156,10 @@ size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
 // Enqueue the scan / decode kernels on `stream`. Arguments are already
 // validated. Return 0 or the HIP error code of the failing launch.
 int launch_scan(const ScanArgs& a, void* stream);
+// The same, with the workspace in the library's fixed per-device scratch array
+// (a.workspace is ignored); scan_scratch_bytes() is that array's size.
+int launch_scan_noalloc(const ScanArgs& a, void* stream);
+size_t scan_scratch_bytes();
 int launch_state_update(const UpdateArgs& a, void* stream);
 int launch_scan_bwd(const ScanBwdArgs& a, void* stream);
 // Forward recurrence only (N <= 16, one pass over each batch row), storing the

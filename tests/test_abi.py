@@ -300,3 +300,35 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stdout
+
+
+def scan_noalloc(lib, B=2, L=8, d=4, N=4, ind=0, outd=0, sp=1, u=P, delta=2 * P, A=3 * P, Bm=4 * P, Cm=5 * P,
+                 D=6 * P, z=7 * P, bias=8 * P, h0=9 * P, y=10 * P, hf=11 * P):
+    return lib.ssm_selective_scan_fwd_noalloc(B, L, d, N, ind, outd, sp, vp(u), vp(delta), vp(A), vp(Bm),
+                                              vp(Cm), vp(D), vp(z), vp(bias), vp(h0), vp(y), vp(hf), None)
+
+
+def test_scan_noalloc_validation(lib):
+    """The allocation-free entry validates like the forward, and refuses
+    shapes whose workspace exceeds its fixed scratch array, before any launch."""
+    limit = header_define_expr("SSM_NOALLOC_SCRATCH_BYTES")
+    assert scan_noalloc(lib, B=-1) == E_SHAPE
+    assert scan_noalloc(lib, N=129) == E_UNSUPPORTED
+    assert scan_noalloc(lib, ind=2) == E_DTYPE
+    assert scan_noalloc(lib, sp=4) == E_UNSUPPORTED
+    assert scan_noalloc(lib, u=None) == E_NULLPTR
+    assert scan_noalloc(lib, u=P + 2) == E_ALIGN
+    assert scan_noalloc(lib, y=P) == E_ALIAS
+    assert scan_noalloc(lib, d=0) == OK
+    # a workspace just above the scratch array: packed B/C of 2 * B * 16 * L words
+    L = (limit // (2 * 16 * 4)) + 64
+    assert lib.ssm_scan_workspace_bytes(1, L, 64, 16) > limit
+    assert scan_noalloc(lib, B=1, L=L, d=64, N=16) == E_WORKSPACE
+    # the long-sequence shape fits
+    assert 0 < lib.ssm_scan_workspace_bytes(1, 262144, 2560, 16) <= limit
+
+
+def header_define_expr(name):
+    """Value of a #define whose body is a size_t shift, e.g. ((size_t)64 << 20)."""
+    m = re.search(rf"#define\s+{name}\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", open(HEADER).read())
+    return int(m.group(1)) << int(m.group(2))
