@@ -17,7 +17,9 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libssm_scan.so")
+# SSM_SCAN_LIBRARY names another build of the same ABI (the test suite's
+# sanitizer build of the host-side front end, whose launches always fail).
+LIB_PATH = os.environ.get("SSM_SCAN_LIBRARY") or os.path.join(_HERE, "lib", "libssm_scan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: SSM_F32, torch.bfloat16: SSM_BF16}
