@@ -190,6 +190,66 @@ __global__ __launch_bounds__(kBlock) void conv1d_update_kernel(const ConvUpdateA
   store_elem<BO>(a.y, i, SILU ? silu_f(acc) : acc);
 }
 
+// Decode update with four adjacent channels per thread: their K-1 state
+// words per channel are 4 (K-1) consecutive floats, and their filters 4 K
+// consecutive floats, so every access is a 16-byte vector access (the state
+// rows stream through non-temporally); x and y as in the sequence kernel.
+// Requires d % 4 == 0 and 16-byte aligned state, weight and bias.
+template <int K, bool BI, bool BO, bool SILU>
+__global__ __launch_bounds__(kBlock) void conv1d_update4_kernel(const ConvUpdateArgs a) {
+  constexpr int SW = 4 * (K - 1);                  // state floats of the thread's channels
+  constexpr int SV = SW / 4;                       // 16-byte state vectors
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t groups = a.batch * a.dim / 4;
+  if (g >= groups) return;
+  const int64_t i = 4 * g;                         // first row (b * d + ch) of the thread
+  const int64_t ch = i % a.dim;
+  f32x4 sv[SV > 0 ? SV : 1];
+  f32x4 wv[K];
+  if constexpr (SV > 0) {
+    const f32x4* sp = reinterpret_cast<const f32x4*>(a.state + i * (K - 1));
+#pragma unroll
+    for (int v = 0; v < SV; ++v) sv[v] = __builtin_nontemporal_load(sp + v);
+  }
+  const f32x4* wp = reinterpret_cast<const f32x4*>(a.weight + ch * K);
+#pragma unroll
+  for (int v = 0; v < K; ++v) wv[v] = wp[v];
+  float xin[4];
+  load_vec<4, BI>(a.x, i, xin);
+  f32x4 bias4 = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + ch) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float st[SV > 0 ? SW : 1], w[4 * K];
+#pragma unroll
+  for (int v = 0; v < SV; ++v) {
+    st[4 * v] = sv[v].x; st[4 * v + 1] = sv[v].y; st[4 * v + 2] = sv[v].z; st[4 * v + 3] = sv[v].w;
+  }
+#pragma unroll
+  for (int v = 0; v < K; ++v) {
+    w[4 * v] = wv[v].x; w[4 * v + 1] = wv[v].y; w[4 * v + 2] = wv[v].z; w[4 * v + 3] = wv[v].w;
+  }
+  const float bb[4] = {bias4.x, bias4.y, bias4.z, bias4.w};
+  float out[4], ns[SV > 0 ? SW : 1];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // window oldest first: state slots 0..K-2, then x; filter tap k meets slot k
+    float acc = bb[c];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) acc = fmaf(w[c * K + k], st[c * (K - 1) + k], acc);
+    acc = fmaf(w[c * K + K - 1], xin[c], acc);
+    out[c] = SILU ? silu_f(acc) : acc;
+#pragma unroll
+    for (int k = 0; k + 1 < K - 1; ++k) ns[c * (K - 1) + k] = st[c * (K - 1) + k + 1];
+    if constexpr (K > 1) ns[c * (K - 1) + K - 2] = xin[c];
+  }
+  if constexpr (SV > 0) {
+    f32x4* so = reinterpret_cast<f32x4*>(a.state + i * (K - 1));
+#pragma unroll
+    for (int v = 0; v < SV; ++v) {
+      __builtin_nontemporal_store(f32x4{ns[4 * v], ns[4 * v + 1], ns[4 * v + 2], ns[4 * v + 3]}, so + v);
+    }
+  }
+  store_vec<4, BO>(a.y, i, out);
+}
+
 template <int KM, int VC, bool BI, bool BO>
 int launch_fwd_k(const ConvArgs& a, hipStream_t st) {
   const int64_t groups = (a.dim + VC - 1) / VC;
@@ -225,8 +285,32 @@ int launch_upd_k(const ConvUpdateArgs& a, hipStream_t st) {
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), kargs, 0, st);
 }
 
+template <int K, bool BI, bool BO>
+int launch_upd4_k(const ConvUpdateArgs& a, hipStream_t st) {
+  const int64_t groups = a.batch * a.dim / 4;
+  const int64_t blocks = (groups + kBlock - 1) / kBlock;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  ConvUpdateArgs args = a;
+  void* kargs[] = {&args};
+  const void* fn = a.silu ? reinterpret_cast<const void*>(&conv1d_update4_kernel<K, BI, BO, true>)
+                          : reinterpret_cast<const void*>(&conv1d_update4_kernel<K, BI, BO, false>);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), kargs, 0, st);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 template <bool BI, bool BO>
 int launch_upd_io(const ConvUpdateArgs& a, hipStream_t st) {
+  const bool vec = a.dim % 4 == 0 && aligned16(a.weight) && (a.bias == nullptr || aligned16(a.bias)) &&
+                   (a.width == 1 || aligned16(a.state));
+  if (vec) {
+    switch (a.width) {
+      case 2: return launch_upd4_k<2, BI, BO>(a, st);
+      case 3: return launch_upd4_k<3, BI, BO>(a, st);
+      case 4: return launch_upd4_k<4, BI, BO>(a, st);
+      default: break;
+    }
+  }
   return a.width <= 4 ? launch_upd_k<4, BI, BO>(a, st) : launch_upd_k<8, BI, BO>(a, st);
 }
 

@@ -113,9 +113,13 @@ def test_conv_continuation_and_updates_bitwise():
     assert torch.equal(st, s20)
 
 
-@pytest.mark.parametrize("K,dt", [(4, "f32"), (2, "bf16"), (6, "f32"), (1, "f32")])
-def test_conv_update_against_oracle(K, dt):
-    B, d = 5, 130
+# d = 130 takes the one-channel-per-thread kernel; d % 4 == 0 with K <= 4 the
+# four-channels-per-thread kernel (16-byte state and filter accesses).
+@pytest.mark.parametrize("K,dt,d", [(4, "f32", 130), (2, "bf16", 130), (6, "f32", 130), (1, "f32", 130),
+                                    (4, "f32", 128), (4, "bf16", 256), (3, "f32", 132), (2, "bf16", 64),
+                                    (1, "bf16", 128), (7, "f32", 128)])
+def test_conv_update_against_oracle(K, dt, d):
+    B = 5
     inp = synth.make_conv_inputs(B, 1, d, K, dt, seed=4, stream=900 + K)
     f = synth.as_float64(inp)
     dv = dev_inputs(inp)
@@ -123,7 +127,7 @@ def test_conv_update_against_oracle(K, dt):
     y = binding.ssm_causal_conv1d_update(st, dv["x"][:, 0].contiguous(), dv["weight"], dv["bias"])
     ref, sref = oracle.causal_conv1d_update(f["state"], f["x"][:, 0], f["weight"], f["bias"])
     _, _, mag = oracle_conv(inp)
-    report(f"conv update K={K} {dt}", oracle.scaled_error(download(y), ref, mag[:, 0] + 1e-30), tol_for(dt, "f32"))
+    report(f"conv update K={K} {dt} d={d}", oracle.scaled_error(download(y), ref, mag[:, 0] + 1e-30), tol_for(dt, "f32"))
     assert np.array_equal(download(st), sref)
 
 
