@@ -30,6 +30,18 @@ same sequential dependence, run backwards in time ([HiddenCost], section on
 the optimisation problems of sequential gradients: every token's gradient
 flows back through all the states after it).
 
+Exact zero-order hold (``zoh=True``; [Breakthrough] section 二.3, the forward
+of ``input_coefficient``): the input term is k_l B_l u_l with
+k = (exp(dt A) - 1) / A (k = dt at A = 0). Its derivatives replace dt where
+it multiplies B u, and add the dependence of k on dt and A:
+
+    dk/ddt = a,   dk/dA = dt^2 phi'(dt A),  phi(x) = expm1(x) / x,
+    phi'(x) = (x e^x - e^x + 1) / x^2  (= 1/2 + x/3 + x^2/8 + ... near 0)
+
+so that dB_l = sum_d lam_l k_l u_l, du_l = dp_l D + sum_n lam_l k_l B_l,
+ddt_l = sum_n lam_l a_l (A h_{l-1} + B_l u_l) and
+dA = sum_{b,l} lam_l (dt_l a_l h_{l-1} + dt_l^2 phi'(dt_l A) B_l u_l).
+
 Magnitude companions (``want_magnitude``): the same formulas evaluated on
 absolute values (|dy|, |C|, |B|, |u|, |A|, |D|, the forward's magnitude
 companion h_mag for |h|), so every gradient entry is bounded by its companion
@@ -40,7 +52,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .ssm_oracle import silu, softplus
+from .ssm_oracle import input_coefficient, silu, softplus
 
 __all__ = ["selective_scan_bwd"]
 
@@ -59,8 +71,19 @@ def _sigmoid(x):
     return out
 
 
+def _dphi(x):
+    """phi'(x) for phi(x) = expm1(x) / x (phi(0) = 1): the closed form away
+    from 0, its Taylor series (to x^4) where the closed form cancels."""
+    x = np.asarray(x, dtype=np.float64)
+    small = np.abs(x) < 1e-3
+    xs = np.where(small, 1.0, x)
+    closed = (xs * np.exp(xs) - np.expm1(xs)) / (xs * xs)
+    series = 0.5 + x / 3.0 + x * x / 8.0 + x ** 3 / 30.0 + x ** 4 / 144.0
+    return np.where(small, series, closed)
+
+
 def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
-                       delta_softplus=False, h0=None, dh_final=None, want_magnitude=False):
+                       delta_softplus=False, h0=None, dh_final=None, want_magnitude=False, zoh=False):
     """Gradients of the selective scan. Shapes as ``selective_scan``; dy [Bt, L, d],
     dh_final [Bt, d, N] (optional).
 
@@ -83,8 +106,9 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
     hm = np.empty((Bt, L + 1, d, N))           # magnitude companion of h
     hm[:, 0] = np.abs(hs[:, 0])
     abar = np.exp(dt[..., None] * A[None, None])                   # [Bt, L, d, N]
+    kco = input_coefficient(dt[..., None], A[None, None], zoh=zoh)  # [Bt, L, d, N]
     for l in range(L):
-        bx = dt[:, l, :, None] * B[:, l, None, :] * u[:, l, :, None]
+        bx = kco[:, l] * B[:, l, None, :] * u[:, l, :, None]
         hs[:, l + 1] = abar[:, l] * hs[:, l] + bx
         hm[:, l + 1] = abar[:, l] * hm[:, l] + np.abs(bx)
     p = (hs[:, 1:] * C[:, :, None, :]).sum(-1)
@@ -133,17 +157,25 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
         lam_m = dpm[:, l, :, None] * np.abs(Cl) + lam_next_m
         dC[:, l] = (dp[:, l, :, None] * hs[:, l + 1]).sum(1)
         dCm[:, l] = (dpm[:, l, :, None] * hm[:, l + 1]).sum(1)
-        dtu = (dt[:, l] * u[:, l])[..., None]
-        dB[:, l] = (lam * dtu).sum(1)
-        dBm[:, l] = (lam_m * np.abs(dtu)).sum(1)
-        du[:, l] += (lam * dt[:, l, :, None] * Bl).sum(-1)
-        dum[:, l] += (lam_m * np.abs(dt[:, l, :, None] * Bl)).sum(-1)
+        k = kco[:, l]                                                # [Bt, d, N]
+        ku = k * u[:, l, :, None]
+        dB[:, l] = (lam * ku).sum(1)
+        dBm[:, l] = (lam_m * np.abs(ku)).sum(1)
+        du[:, l] += (lam * k * Bl).sum(-1)
+        dum[:, l] += (lam_m * np.abs(k * Bl)).sum(-1)
         ah = abar[:, l] * hs[:, l]                                   # a_l h_{l-1}
         ahm = abar[:, l] * hm[:, l]
-        ddt[:, l] = (lam * (A * ah + Bl * u[:, l, :, None])).sum(-1)
-        ddtm[:, l] = (lam_m * (np.abs(A) * ahm + np.abs(Bl * u[:, l, :, None]))).sum(-1)
-        dA += (lam * dt[:, l, :, None] * ah).sum(0)
-        dAm += (lam_m * np.abs(dt[:, l, :, None]) * ahm).sum(0)
+        bu = Bl * u[:, l, :, None]
+        dkdt = abar[:, l] if zoh else 1.0                            # dk/ddt
+        ddt[:, l] = (lam * (A * ah + dkdt * bu)).sum(-1)
+        ddtm[:, l] = (lam_m * (np.abs(A) * ahm + np.abs(dkdt * bu))).sum(-1)
+        dtl = dt[:, l, :, None]
+        dA += (lam * dtl * ah).sum(0)
+        dAm += (lam_m * np.abs(dtl) * ahm).sum(0)
+        if zoh:
+            dkdA = dtl * dtl * _dphi(dtl * A)                        # dk/dA
+            dA += (lam * dkdA * bu).sum(0)
+            dAm += (lam_m * np.abs(dkdA * bu)).sum(0)
         lam_next = abar[:, l] * lam
         lam_next_m = abar[:, l] * lam_m
     ddelta = ddt * dsp

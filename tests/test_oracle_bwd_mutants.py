@@ -16,7 +16,7 @@ MUTANTS = {
     # forget the loss on the final state
     "ignore_dh_final": ("else _f64(dh_final).copy()", "else 0.0 * _f64(dh_final)"),
     # drop the input term from d(loss)/d(dt)
-    "ddt_without_input_term": ("(lam * (A * ah + Bl * u[:, l, :, None])).sum(-1)", "(lam * (A * ah)).sum(-1)"),
+    "ddt_without_input_term": ("(lam * (A * ah + dkdt * bu)).sum(-1)", "(lam * (A * ah)).sum(-1)"),
     # silu' taken as sigmoid only
     "silu_derivative_wrong": ("dsilu = s * (1.0 + z * (1.0 - s))", "dsilu = s"),
     # state gradient read out with the previous state
