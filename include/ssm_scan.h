@@ -195,10 +195,12 @@ int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
 
 /*
  * Bytes of device workspace ssm_selective_scan_bwd needs for this shape: B and
- * C repacked per state, the states at every 8-step tile start
- * ([B][ceil(L/8)][N'][d] float32, N' = N rounded up to a power of two), and
+ * C repacked per state, the states at every tile start ([B][Lp/T][N'][d]
+ * float32, N' = N rounded up to a power of two, Lp = L rounded up to 16, and
+ * tiles of T = 16 steps for N' <= 8, 128 / N' steps from N' = 16 on), and
  * per-block / per-batch partial sums of dB, dC, dA, dD and the bias gradient.
- * Returns 0 for invalid or unsupported sizes.
+ * Returns 0 for invalid or unsupported sizes (N > 64, and rows too long for
+ * 32-bit offsets into the packed B/C or the dB/dC partials).
  */
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
@@ -215,12 +217,15 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   dD      = sum_{b,l} dp u                 dz = dy p silu'(z), p = sum_n C h + D u
  *   ddelta_bias = sum_{b,l} ddelta           dh0 = exp(dt_0 A) lam_0
  *
- *   batch, seqlen, dim, dstate : as the forward, with 1 <= N <= 16 (else
+ *   batch, seqlen, dim, dstate : as the forward, with 1 <= N <= 64 (else
  *                                SSM_E_UNSUPPORTED).
  *   in_dtype, flags, u, delta, A, B, C, D, z, delta_bias, h0 : the
  *                                forward's inputs (same layouts and rules);
- *                                SSM_FLAG_ZOH returns SSM_E_UNSUPPORTED (the
- *                                gradients are those of k = dt).
+ *                                with SSM_FLAG_ZOH the gradients of the exact
+ *                                zero-order-hold forward: k = (a - 1) / A in
+ *                                place of dt in front of B u, dk/ddt = a and
+ *                                dk/dA = dt^2 phi'(dt A), phi(x) = expm1(x)/x
+ *                                (ruibaoantu.com, section 二.3).
  *   dy        [B, L, d]  float32    gradient of the loss w.r.t. y
  *   dh_final  [B, d, N]  float32    gradient w.r.t. h_final (optional, 0)
  *   du, ddelta [B, L, d] float32    outputs (ddelta w.r.t. the raw delta)

@@ -12,8 +12,8 @@ K-1 and truncated to the first L outputs, then SiLU; [Notes] "Mamba block 的
     out[b,l,d] = bias[d] + sum_{k=0}^{K-1} weight[d,k] * x[b, l-(K-1)+k, d]
     y[b,l,d]   = silu(out[b,l,d])        (or out itself without the activation)
 
-Inputs before step 0 come from an optional carried state (else zero), the
-conv_state of [Notes] ("固定大小的 recurrent states ... conv_state"):
+Inputs before step 0 come from an optional carried state (else zero): the
+fixed-size conv_state kept between tokens ([Notes], "Mamba block 的结构"):
 
     state[b,d,j] = x[b, j-(K-1), d],  j = 0..K-2   (oldest first)
 

@@ -380,12 +380,13 @@ def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate) -> int:
 
 
 def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False,
-                           h0=None, dh_final=None, workspace=None, stream=None):
+                           h0=None, dh_final=None, workspace=None, stream=None, zoh=False):
     """Gradients of the selective scan; see ssm_selective_scan_bwd in include/ssm_scan.h.
 
     Inputs as ssm_selective_scan_fwd, plus dy [B, L, d] and dh_final [B, d, N]
     (float32). Returns a dict of float32 tensors: du, ddelta, dA, dB, dC, dh0,
-    and dD / dz / ddelta_bias when D / z / delta_bias are given.
+    and dD / dz / ddelta_bias when D / z / delta_bias are given. ``zoh``: the
+    gradients of the exact zero-order-hold forward (SSM_FLAG_ZOH).
     """
     lib = _load()
     if not isinstance(u, torch.Tensor) or u.dim() != 3 or u.dtype not in _DTYPE_CODE:
@@ -423,7 +424,7 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=Non
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         ws_size = _check_workspace(workspace, dev)
         st = lib.ssm_selective_scan_bwd(
-            Bt, L, d, N, _DTYPE_CODE[u.dtype], _flags(delta_softplus, False),
+            Bt, L, d, N, _DTYPE_CODE[u.dtype], _flags(delta_softplus, zoh),
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0),
             _ptr(dy), _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
             _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g["dh0"]),

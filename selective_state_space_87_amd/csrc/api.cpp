@@ -271,7 +271,6 @@ int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
   if (in_dtype != 0 && in_dtype != 1) return SSM_E_DTYPE;
   if ((flags & ~(SSM_FLAG_SOFTPLUS | SSM_FLAG_ZOH)) != 0) return SSM_E_UNSUPPORTED;
-  if (flags & SSM_FLAG_ZOH) return SSM_E_UNSUPPORTED;  // gradients of the simplified form only
   int64_t bl, bld, bln, bdn, dn, bldn;
   if (!safe_mul(batch, seqlen, &bl) || !safe_mul(bl, dim, &bld) || !safe_mul(bl, dstate, &bln) ||
       !safe_mul(batch, dim, &bdn) || !safe_mul(bdn, dstate, &bdn) || !safe_mul(dim, dstate, &dn) ||
@@ -342,6 +341,7 @@ int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   a.dstate = dstate;
   a.in_bf16 = in_dtype;
   a.delta_softplus = (flags & SSM_FLAG_SOFTPLUS) != 0;
+  a.zoh = (flags & SSM_FLAG_ZOH) != 0;
   return map_hip(ssm::launch_scan_bwd(a, stream));
 }
 

@@ -62,7 +62,7 @@ struct ScanBwdArgs {
   float* dh0;
   void* workspace;
   int64_t batch, seqlen, dim, dstate;
-  int in_bf16, delta_softplus;
+  int in_bf16, delta_softplus, zoh;
 };
 
 struct ConvArgs {
@@ -139,7 +139,13 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 // = packed B/C, per-tile state checkpoints [B][tiles][NS][d], per-block
 // partials of dB and dC [blocks_d][B][Lp][NS], per-batch partials of dA
 // [B][d][N], dD and the bias gradient [B][d].
-constexpr int64_t kBwdMaxState = 16;
+constexpr int64_t kBwdMaxState = 64;
+// Backward (and its checkpoint pass) per padded state count NS: states per
+// lane S, waves W and tile length T, with S * T = 16 from N = 16 on, so the
+// per-tile register arrays stay the same size (eight waves of at most 256
+// registers): NS <= 8: (1, NS, 16); 16: (2, 8, 8); 32: (4, 8, 4); 64: (8, 8, 2).
+constexpr int bwd_tile_steps(int NS) { return NS <= 8 ? 16 : 128 / NS; }
+constexpr int bwd_waves(int NS) { return NS <= 8 ? NS : 8; }
 // Largest state size of the scan (padded to a power of two: 128).
 constexpr int64_t kMaxScanStates = 128;
 struct ScanBwdPlan {

@@ -78,7 +78,7 @@ ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
          seqlen * dim * 4 <= kPlaneBytesMax;  // one pass per batch row: 32-bit buffer offsets
   if (!p.ok) return p;
   p.NS = ceil_pow2(dstate);
-  p.W = p.NS < 16 ? p.NS : 8;
+  p.W = bwd_waves(p.NS);
   p.S = p.NS / p.W;
   p.Lp = round_up(seqlen, kPadSteps);
   p.dim_blocks = ceil_div(dim, 64);
@@ -89,7 +89,7 @@ ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
     p.ok = false;
     return p;
   }
-  const int64_t tiles = p.Lp / (p.NS == 16 ? 8 : 16);  // the forward's tile length for this NS
+  const int64_t tiles = p.Lp / bwd_tile_steps(p.NS);  // checkpoint spacing
   size_t off = 0;
   p.off_bc = off;
   off += align256(size_t(2 * batch * p.NS * p.Lp) * 4);

@@ -10,11 +10,17 @@
 //   dA     = sum lam_l dt_l a_l h_{l-1}                 dh0  = a_0 lam_0
 //   dB_l   = sum_d lam_l dt_l u_l                       dC_l = sum_d dp_l h_l
 //   dz_l   = dy_l p_l silu'(z_l) with p the pre-gate output; ddelta = ddt softplus'(x)
+// With the exact zero-order hold ("Mamba新突破", ruibaoantu.com, section 二.3)
+// the input coefficient k = (a - 1) / A takes dt's place in front of B u, and
+// dk/ddt = a, dk/dA = dt^2 phi'(dt A) (phi(x) = (e^x - 1) / x):
+//   ddt_l = sum_n lam_l a_l (A h_{l-1} + B_l u_l),  du_l = dp_l D + sum_n lam_l k_l B_l,
+//   dB_l = sum_d lam_l k_l u_l,  dA += lam_l dt_l^2 phi'(dt_l A) B_l u_l.
 //
-// One block per (batch, 64 channels), the forward's mapping: lane = channel,
-// wave w = states w*S .. w*S+S-1. Two passes:
+// One block per (batch, 64 channels): lane = channel, wave w = states
+// w*S .. w*S+S-1, eight waves from N = 16 on with S * T = 16 (N = 16: 8-step
+// tiles; 32: 4 states per lane, 4 steps; 64: 8 states, 2 steps). Two passes:
 //   1. the forward kernel in its checkpoint mode stores every wave's states
-//      at each tile start (scan_fwd.hip; same mapping and tiles);
+//      at each tile start (scan_fwd_impl.h; same mapping and tiles);
 //   2. this kernel, over the tiles in reverse: recompute the tile's states and
 //      transitions from its checkpoint, read the pre-gate output out of them
 //      (partials over waves in LDS, as in the forward), then run the adjoint
@@ -125,7 +131,7 @@ __device__ __forceinline__ float lane_transpose_sum(float (&v)[G], int lane) {
   return r;
 }
 
-template <int S, int W, int T, bool BF16_IN, bool SOFTPLUS>
+template <int S, int W, int T, bool BF16_IN, bool SOFTPLUS, bool ZOH>
 __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   constexpr int NS = S * W;
   constexpr int IT = T >= W ? T / W : 1;   // cooperative items per thread per tile
@@ -158,12 +164,14 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   const int64_t bdn = (static_cast<int64_t>(b) * Dm + ch) * N;
 
   float A1[S], A2[S];
+  float iA[ZOH ? S : 1];                             // 1/A (0 where A = 0), ZOH only
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int n = w * S + s;
     const bool ok = ch_ok && n < N;
     A1[s] = ok ? p.A[static_cast<int64_t>(ch) * N + n] : 0.0f;
     A2[s] = A1[s] * kLog2e;
+    if constexpr (ZOH) iA[s] = inv_or_zero(A1[s]);
   }
   const float Dv = (ch_ok && p.D) ? p.D[ch] : 0.0f;
   const float bv = (ch_ok && p.bias) ? p.bias[ch] : 0.0f;
@@ -338,6 +346,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       uvv[t] = q.w;
     }
     float av[T][S], ahv[T][S], hs[T][S], bvs[T][S], cvs[T][S];
+    float kv[ZOH ? T : 1][ZOH ? S : 1];               // input coefficient k (ZOH)
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       float acc = 0.0f;
@@ -347,9 +356,15 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         bc_of(qb, w * S + s, t, bval, cval);   // kept for the adjoint below
         bvs[t][s] = bval;
         cvs[t][s] = cval;
-        av[t][s] = exp2_hw(dtv[t] * A2[s]);
+        const float x2 = dtv[t] * A2[s];
+        av[t][s] = exp2_hw(x2);
         ahv[t][s] = av[t][s] * hh[s];
-        hh[s] = fmaf(dtu[t], bval, ahv[t][s]);
+        if constexpr (ZOH) {
+          kv[t][s] = zoh_coef(dtv[t], x2, av[t][s], iA[s]);
+          hh[s] = fmaf(kv[t][s] * uvv[t], bval, ahv[t][s]);
+        } else {
+          hh[s] = fmaf(dtu[t], bval, ahv[t][s]);
+        }
         hs[t][s] = hh[s];
         acc = fmaf(cval, hh[s], acc);
       }
@@ -363,19 +378,32 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       // ddt = sla + u slb and du = dt slb (the factors common to all states
       // applied once per step).
       float slb = 0.0f, sla = 0.0f;
+      float slk = 0.0f, dt2 = 0.0f;                   // ZOH: sum lam k B; dt^2
+      if constexpr (ZOH) dt2 = dtv[t] * dtv[t];
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         const float lam = fmaf(dpv[t], cvs[t][s], mu[s]);
-        gv[t * S + s] = lam * dtu[t];                 // -> dB (sum over channels)
         gv[T * S + t * S + s] = dpv[t] * hs[t][s];    // -> dC (sum over channels)
-        slb = fmaf(lam, bvs[t][s], slb);
         const float la = lam * ahv[t][s];
         sla = fmaf(la, A1[s], sla);
         dA_acc[s] = fmaf(la, dtv[t], dA_acc[s]);
+        if constexpr (ZOH) {
+          // dB gets lam k u; ddt gets lam a B u (dk/ddt = a); du gets lam k B;
+          // dA also gets lam dt^2 phi'(dt A) B u.
+          const float lb = lam * bvs[t][s];
+          gv[t * S + s] = lam * (kv[t][s] * uvv[t]);
+          slb = fmaf(lb, av[t][s], slb);
+          slk = fmaf(lb, kv[t][s], slk);
+          const float dphi = zoh_dphi(dtv[t] * A1[s], av[t][s]);
+          dA_acc[s] = fmaf(lb * uvv[t], dt2 * dphi, dA_acc[s]);
+        } else {
+          gv[t * S + s] = lam * dtu[t];               // -> dB (sum over channels)
+          slb = fmaf(lam, bvs[t][s], slb);
+        }
         mu[s] = av[t][s] * lam;
       }
       sG[pb][t][pslot] = fmaf(slb, uvv[t], sla);
-      sU[pb][t][pslot] = slb * dtv[t];
+      sU[pb][t][pslot] = ZOH ? slk : slb * dtv[t];
     }
     // dB / dC partials of this block: value j = lane >> (6 - log2 G) after the
     // transposed butterfly; one lane of each group writes it.
@@ -571,24 +599,36 @@ int launch_reduce_d(const ScanBwdArgs& a, const float* dAp, const float* dDp, co
                          dim3(static_cast<unsigned>((dn + 255) / 256)), dim3(256), kargs, 0, st);
 }
 
-template <int S, int W, bool BI, bool SP>
-int launch_bwd_sw(const ScanBwdArgs& a, const ScanBwd& s, int64_t blocks, hipStream_t st) {
-  constexpr int T = S * W == 16 ? 8 : 16;  // the forward's tiles (checkpoint spacing)
+template <int S, int W, bool BI, bool SP, bool ZH>
+int launch_bwd_sw(const ScanBwd& s, int64_t blocks, hipStream_t st) {
+  constexpr int T = bwd_tile_steps(S * W);  // checkpoint spacing
+  static_assert(bwd_waves(S * W) == W, "mapping of the plan");
   ScanBwd args = s;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_bwd_kernel<S, W, T, BI, SP>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_bwd_kernel<S, W, T, BI, SP, ZH>),
                          dim3(static_cast<unsigned>(blocks)), dim3(W * 64), kargs, 0, st);
 }
 
-template <bool BI, bool SP>
-int launch_bwd_ns(const ScanBwdArgs& a, const ScanBwdPlan& pl, const ScanBwd& s, int64_t blocks, hipStream_t st) {
+template <bool BI, bool SP, bool ZH>
+int launch_bwd_ns(const ScanBwdPlan& pl, const ScanBwd& s, int64_t blocks, hipStream_t st) {
   switch (pl.NS) {
-    case 1: return launch_bwd_sw<1, 1, BI, SP>(a, s, blocks, st);
-    case 2: return launch_bwd_sw<1, 2, BI, SP>(a, s, blocks, st);
-    case 4: return launch_bwd_sw<1, 4, BI, SP>(a, s, blocks, st);
-    case 8: return launch_bwd_sw<1, 8, BI, SP>(a, s, blocks, st);
-    default: return launch_bwd_sw<2, 8, BI, SP>(a, s, blocks, st);
+    case 1: return launch_bwd_sw<1, 1, BI, SP, ZH>(s, blocks, st);
+    case 2: return launch_bwd_sw<1, 2, BI, SP, ZH>(s, blocks, st);
+    case 4: return launch_bwd_sw<1, 4, BI, SP, ZH>(s, blocks, st);
+    case 8: return launch_bwd_sw<1, 8, BI, SP, ZH>(s, blocks, st);
+    case 16: return launch_bwd_sw<2, 8, BI, SP, ZH>(s, blocks, st);
+    case 32: return launch_bwd_sw<4, 8, BI, SP, ZH>(s, blocks, st);
+    case 64: return launch_bwd_sw<8, 8, BI, SP, ZH>(s, blocks, st);
+    default: return hipErrorInvalidValue;
   }
+}
+
+template <bool BI>
+int launch_bwd_io(const ScanBwdArgs& a, const ScanBwdPlan& pl, const ScanBwd& s, int64_t blocks, hipStream_t st) {
+  if (a.zoh) return a.delta_softplus ? launch_bwd_ns<BI, true, true>(pl, s, blocks, st)
+                                     : launch_bwd_ns<BI, false, true>(pl, s, blocks, st);
+  return a.delta_softplus ? launch_bwd_ns<BI, true, false>(pl, s, blocks, st)
+                          : launch_bwd_ns<BI, false, false>(pl, s, blocks, st);
 }
 
 }  // namespace
@@ -615,8 +655,11 @@ int launch_scan_bwd(const ScanBwdArgs& a, void* stream) {
     f.seqlen = a.seqlen;
     f.dim = a.dim;
     f.dstate = a.dstate;
+    f.B = a.B;
+    f.C = a.C;
     f.in_bf16 = a.in_bf16;
     f.delta_softplus = a.delta_softplus;
+    f.zoh = a.zoh;
     if (pl.Lp > 0) {
       err = launch_scan_checkpoints(f, reinterpret_cast<const uint32_t*>(ws + pl.off_bc),
                                     reinterpret_cast<float*>(ws + pl.off_ckpt), st);
@@ -651,13 +694,7 @@ int launch_scan_bwd(const ScanBwdArgs& a, void* stream) {
   s.batch = static_cast<int>(a.batch);
   const int64_t blocks = a.batch * pl.dim_blocks;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (a.in_bf16) {
-    err = a.delta_softplus ? launch_bwd_ns<true, true>(a, pl, s, blocks, st)
-                           : launch_bwd_ns<true, false>(a, pl, s, blocks, st);
-  } else {
-    err = a.delta_softplus ? launch_bwd_ns<false, true>(a, pl, s, blocks, st)
-                           : launch_bwd_ns<false, false>(a, pl, s, blocks, st);
-  }
+  err = a.in_bf16 ? launch_bwd_io<true>(a, pl, s, blocks, st) : launch_bwd_io<false>(a, pl, s, blocks, st);
   if (err != 0) return err;
   {
     const float* dBp = s.dBp;

@@ -7,12 +7,12 @@
 
 namespace ssm {
 
-int scan_tile_steps(int NS) { return NS == 16 ? 8 : 16; }
+int scan_tile_steps(int NS) { return bwd_tile_steps(NS); }
 
 int launch_scan_checkpoints(const ScanArgs& a, const uint32_t* bc, float* ckpt, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const ScanPlan pl = plan_scan(a.batch, a.seqlen, a.dim, a.dstate);
-  if (!pl.ok || pl.NS > 16 || a.batch == 0 || a.dim == 0) return hipErrorInvalidValue;
+  if (!pl.ok || pl.NS > kBwdMaxState || a.batch == 0 || a.dim == 0) return hipErrorInvalidValue;
   // one pass over the whole sequence: each batch row's plane must fit the
   // 32-bit buffer offsets
   if (a.seqlen * a.dim * 4 > kPlaneBytesMax) return hipErrorInvalidValue;
@@ -23,6 +23,8 @@ int launch_scan_checkpoints(const ScanArgs& a, const uint32_t* bc, float* ckpt, 
   s.bias = a.delta_bias;
   s.h0 = a.h0;
   s.BC = bc;
+  s.Bm = a.B;   // read directly where B/C are staged through LDS (N = 64)
+  s.Cm = a.C;
   s.hsum = ckpt;
   s.L = static_cast<int>(a.seqlen);
   s.Lp = static_cast<int>(pl.Lp);

@@ -7,8 +7,4 @@ int launch_scan_bf(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStre
   return launch_io<true, false>(a, pl, s, st);
 }
 
-int launch_ckpt_b(const ScanArgs& a, const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_t st) {
-  return a.delta_softplus ? launch_ckpt_ns<true, true>(pl, s, blocks, st) : launch_ckpt_ns<true, false>(pl, s, blocks, st);
-}
-
 }  // namespace ssm

@@ -7,8 +7,4 @@ int launch_scan_ff(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStre
   return launch_io<false, false>(a, pl, s, st);
 }
 
-int launch_ckpt_f(const ScanArgs& a, const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_t st) {
-  return a.delta_softplus ? launch_ckpt_ns<false, true>(pl, s, blocks, st) : launch_ckpt_ns<false, false>(pl, s, blocks, st);
-}
-
 }  // namespace ssm

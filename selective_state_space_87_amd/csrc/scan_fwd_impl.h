@@ -113,8 +113,13 @@ constexpr int kFull = 0, kSummary = 1, kCheckpoint = 2;
 template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool ZOH, int MODE>
 __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int NS = S * W;        // padded state count
-  constexpr int IT = T / W;        // cooperative items per thread per tile
-  static_assert(T % W == 0, "tile must split evenly over the waves");
+  // Cooperative items per thread per tile: step w + W*i of the tile. With
+  // fewer steps than waves (the backward's checkpoint pass at N = 32, 64)
+  // waves w >= T have none.
+  constexpr int IT = T >= W ? T / W : 1;
+  static_assert(T % W == 0 || (MODE == kCheckpoint && W % T == 0),
+                "tile must split evenly over the waves (or the waves over the tile, checkpoints only)");
+  const bool has_item = T >= W || threadIdx.x < 64 * T;  // (wave-uniform: w < T)
   constexpr int LW = __builtin_ctz(W);
   constexpr int NC = W >= 4 ? W / 4 : 1;            // 16-byte chunks per partial row
   constexpr int LNC = __builtin_ctz(NC);
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // k*T + w + W*i of the chunk, times the row pitch; out of range outside it.
   auto step_off = [&](int k, int i, uint32_t elem) __attribute__((always_inline)) -> uint32_t {
     const int t = k * T + w + W * i;
-    return static_cast<unsigned>(t) < static_cast<unsigned>(len)
+    return (has_item && static_cast<unsigned>(t) < static_cast<unsigned>(len))
                ? static_cast<uint32_t>(t) * static_cast<uint32_t>(Dm) * elem
                : kStepOut;
   };
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
         eDu[SL][i] = Dv * uv;
         eG[SL][i] = has_z ? g : 1.0f;
       }
-      sDD[SL][tt][lane] = make_float2(dt, ZOH ? uv : dt * uv);
+      if (has_item) sDD[SL][tt < T ? tt : 0][lane] = make_float2(dt, ZOH ? uv : dt * uv);
     }
     if constexpr (BCL) {
 #pragma unroll
@@ -727,20 +732,37 @@ int launch_io(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
                           : launch_ns<BI, BO, false, false>(a, pl, s, st);
 }
 
-template <bool BI, bool SP>
-int launch_ckpt_ns(const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_t st) {
+// Checkpoint pass of the backward: the recurrence only, storing every wave's
+// states at each tile start. Its mapping is the backward kernel's (states per
+// lane S, waves W, tile T; tiles of scan_tile_steps(NS) steps).
+template <int S, int W, int T, bool BI, bool SP, bool ZH>
+int launch_ckpt_sw(const Scan& s, int64_t blocks, hipStream_t st) {
   Scan args = s;
   void* kargs[] = {&args};
-  const void* fn = nullptr;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, false, SP, ZH, kCheckpoint>),
+                         dim3(static_cast<unsigned>(blocks)), dim3(W * 64), kargs, 0, st);
+}
+
+template <bool BI, bool SP, bool ZH>
+int launch_ckpt_ns(const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_t st) {
   switch (pl.NS) {
-    case 1: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 1, 16, BI, false, SP, false, kCheckpoint>); break;
-    case 2: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 2, 16, BI, false, SP, false, kCheckpoint>); break;
-    case 4: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 4, 16, BI, false, SP, false, kCheckpoint>); break;
-    case 8: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<1, 8, 16, BI, false, SP, false, kCheckpoint>); break;
-    case 16: fn = reinterpret_cast<const void*>(&scan_fwd_kernel<2, 8, 8, BI, false, SP, false, kCheckpoint>); break;
+    case 1: return launch_ckpt_sw<1, 1, 16, BI, SP, ZH>(s, blocks, st);
+    case 2: return launch_ckpt_sw<1, 2, 16, BI, SP, ZH>(s, blocks, st);
+    case 4: return launch_ckpt_sw<1, 4, 16, BI, SP, ZH>(s, blocks, st);
+    case 8: return launch_ckpt_sw<1, 8, 16, BI, SP, ZH>(s, blocks, st);
+    case 16: return launch_ckpt_sw<2, 8, 8, BI, SP, ZH>(s, blocks, st);
+    case 32: return launch_ckpt_sw<4, 8, 4, BI, SP, ZH>(s, blocks, st);
+    case 64: return launch_ckpt_sw<8, 8, 2, BI, SP, ZH>(s, blocks, st);
     default: return hipErrorInvalidValue;
   }
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(pl.W * 64), kargs, 0, st);
+}
+
+template <bool BI>
+int launch_ckpt_io(const ScanArgs& a, const ScanPlan& pl, const Scan& s, int64_t blocks, hipStream_t st) {
+  if (a.zoh) return a.delta_softplus ? launch_ckpt_ns<BI, true, true>(pl, s, blocks, st)
+                                     : launch_ckpt_ns<BI, false, true>(pl, s, blocks, st);
+  return a.delta_softplus ? launch_ckpt_ns<BI, true, false>(pl, s, blocks, st)
+                          : launch_ckpt_ns<BI, false, false>(pl, s, blocks, st);
 }
 
 }  // namespace

@@ -20,7 +20,7 @@ size_t scan_scratch_bytes() { return size_t(64) << 20; }
 int launch_state_update(const UpdateArgs&, void*) { return kNoDevice; }
 int launch_scan_bwd(const ScanBwdArgs&, void*) { return kNoDevice; }
 int launch_scan_checkpoints(const ScanArgs&, const uint32_t*, float*, void*) { return kNoDevice; }
-int scan_tile_steps(int NS) { return NS == 16 ? 8 : 16; }
+int scan_tile_steps(int NS) { return bwd_tile_steps(NS); }
 int launch_conv1d_fwd(const ConvArgs&, void*) { return kNoDevice; }
 int launch_conv1d_update(const ConvUpdateArgs&, void*) { return kNoDevice; }
 int launch_ssd(const SsdArgs&, void*) { return kNoDevice; }

@@ -204,7 +204,7 @@ def bwd(lib, B=2, L=8, d=4, N=4, ind=0, sp=1, ws=40 * P, wsb=1 << 24, **kw):
 
 def test_scan_bwd_validation(lib):
     assert bwd(lib, B=-1) == E_SHAPE
-    assert bwd(lib, N=17) == E_UNSUPPORTED
+    assert bwd(lib, N=65) == E_UNSUPPORTED
     assert bwd(lib, ind=4) == E_DTYPE
     assert bwd(lib, dy=None) == E_NULLPTR
     assert bwd(lib, dA=None) == E_NULLPTR
@@ -218,7 +218,8 @@ def test_scan_bwd_validation(lib):
     assert bwd(lib, ws=20 * P) == E_ALIAS            # workspace over dh0
     assert bwd(lib, d=0) == OK
     need = lib.ssm_scan_bwd_workspace_bytes(2, 8, 4, 4)
-    assert need > 0 and lib.ssm_scan_bwd_workspace_bytes(1, 8, 4, 17) == 0
+    assert need > 0 and lib.ssm_scan_bwd_workspace_bytes(1, 8, 4, 65) == 0
+    assert lib.ssm_scan_bwd_workspace_bytes(1, 8, 4, 64) > lib.ssm_scan_bwd_workspace_bytes(1, 8, 4, 17) > 0
 
 
 def test_scan_bwd_refuses_long_rows_of_few_channels(lib):
@@ -234,16 +235,16 @@ def test_scan_bwd_refuses_long_rows_of_few_channels(lib):
 
 
 def test_flag_bits(lib):
-    """SSM_FLAG_SOFTPLUS and SSM_FLAG_ZOH are the only flag bits; the
-    backward takes softplus only (its gradients are those of k = dt)."""
+    """SSM_FLAG_SOFTPLUS and SSM_FLAG_ZOH are the only flag bits, for the
+    forward, the decode step and the backward alike."""
     soft, zoh = header_define("SSM_FLAG_SOFTPLUS"), header_define("SSM_FLAG_ZOH")
     assert (soft, zoh) == (binding.FLAG_SOFTPLUS, binding.FLAG_ZOH) == (1, 2)
     for bad in (4, 8, 1 << 30, -1):
         assert scan(lib, sp=bad) == E_UNSUPPORTED
         assert upd(lib, sp=bad) == E_UNSUPPORTED
         assert bwd(lib, sp=bad) == E_UNSUPPORTED
-    assert bwd(lib, sp=zoh) == E_UNSUPPORTED
-    assert bwd(lib, sp=soft | zoh) == E_UNSUPPORTED
+    assert bwd(lib, sp=zoh, dy=None) == E_NULLPTR            # ZOH passes the flag check
+    assert bwd(lib, sp=soft | zoh, dy=None) == E_NULLPTR
     # the valid bits pass validation (these calls then stop at a later check)
     assert scan(lib, sp=soft | zoh, u=None) == E_NULLPTR
     assert upd(lib, sp=zoh, state=None) == E_NULLPTR

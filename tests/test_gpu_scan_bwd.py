@@ -28,17 +28,19 @@ def report(name, err, tol):
     assert err <= tol, f"{name}: scaled error {err:.3e} > {tol:.1e}"
 
 
-def run_bwd(inp, dy, dhf, h0=None, use_D=True, use_z=True, use_bias=True, softplus=None):
+def run_bwd(inp, dy, dhf, h0=None, use_D=True, use_z=True, use_bias=True, softplus=None, zoh=False):
     dev = scan_inputs_to_device(inp)
     sp = inp["delta_softplus"] if softplus is None else softplus
     return binding.ssm_selective_scan_bwd(
         dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], upload(dy, "f32"),
         D=dev["D"] if use_D else None, z=dev["z"] if use_z else None,
         delta_bias=dev["delta_bias"] if use_bias else None, delta_softplus=sp,
-        h0=None if h0 is None else upload(h0, "f32"), dh_final=None if dhf is None else upload(dhf, "f32"))
+        h0=None if h0 is None else upload(h0, "f32"), dh_final=None if dhf is None else upload(dhf, "f32"),
+        zoh=zoh)
 
 
-def oracle_bwd(inp, dy, dhf, h0=None, use_D=True, use_z=True, use_bias=True, softplus=None, channels=None):
+def oracle_bwd(inp, dy, dhf, h0=None, use_D=True, use_z=True, use_bias=True, softplus=None, channels=None,
+               zoh=False):
     f = synth.as_float64(inp)
     sl = slice(None) if channels is None else np.asarray(channels)
     sp = inp["delta_softplus"] if softplus is None else softplus
@@ -47,7 +49,7 @@ def oracle_bwd(inp, dy, dhf, h0=None, use_D=True, use_z=True, use_bias=True, sof
         D=f["D"][sl] if use_D else None, z=f["z"][:, :, sl] if (use_z and f.get("z") is not None) else None,
         delta_bias=f["delta_bias"][sl] if use_bias else None, delta_softplus=sp,
         h0=None if h0 is None else np.asarray(h0, float)[:, sl],
-        dh_final=None if dhf is None else np.asarray(dhf, float)[:, sl], want_magnitude=True)
+        dh_final=None if dhf is None else np.asarray(dhf, float)[:, sl], want_magnitude=True, zoh=zoh)
 
 
 def compare(name, g, ref, mag, tol, channels=None, skip=()):
@@ -75,6 +77,9 @@ def grads_in(B, L, d, N, seed):
 SHAPES = [
     (1, 64, 64, 16, "f32"), (2, 100, 70, 16, "bf16"), (1, 129, 33, 3, "f32"), (3, 40, 64, 5, "f32"),
     (1, 200, 130, 8, "bf16"), (2, 37, 64, 1, "f32"), (1, 17, 8, 2, "bf16"), (2, 300, 100, 12, "f32"),
+    # 17..64 states: four states per lane on 4-step tiles (N <= 32), eight on 2-step tiles (N <= 64)
+    (2, 150, 96, 32, "f32"), (1, 77, 70, 24, "bf16"), (2, 120, 64, 64, "f32"), (1, 93, 130, 48, "bf16"),
+    (1, 40, 64, 17, "f32"), (1, 33, 65, 33, "f32"),
 ]
 
 
@@ -163,3 +168,35 @@ def test_bwd_empty_sequence_and_deterministic():
     g2 = run_bwd(inp, dy, dhf, h0=h0)
     for k in g1:
         assert torch.equal(g1[k], g2[k]), k
+
+
+ZOH_SHAPES = [(1, 64, 64, 16, "f32"), (2, 120, 70, 16, "bf16"), (1, 100, 64, 5, "f32"), (2, 90, 96, 32, "f32"),
+              (1, 70, 64, 64, "bf16")]
+
+
+@pytest.mark.parametrize("B,L,d,N,dt", ZOH_SHAPES)
+def test_bwd_zoh(B, L, d, N, dt):
+    """Gradients of the exact zero-order-hold forward (SSM_FLAG_ZOH), with
+    one channel's A set to 0 (its limit, k = dt) and one's very small."""
+    inp = synth.make_scan_inputs(B, L, d, N, dt, seed=41, stream=4100 + N)
+    inp = dict(inp)
+    A = inp["A"].copy()
+    A[1, :] = 0.0
+    A[2, :] = np.float32(-1e-6)
+    inp["A"] = A
+    dy, dhf, h0 = grads_in(B, L, d, N, seed=L + 1)
+    g = run_bwd(inp, dy, dhf, h0=h0, zoh=True)
+    torch.cuda.synchronize()
+    ref, mag = oracle_bwd(inp, dy, dhf, h0=h0, zoh=True)
+    compare(f"bwd zoh {(B, L, d, N)} {dt}", g, ref, mag, tol_for(dt, "f32"))
+
+
+def test_bwd_zoh_differs_from_default():
+    """The flag reaches the kernels: with large steps the ZOH gradients
+    differ from the default form's by far more than the tolerance."""
+    B, L, d, N = 1, 50, 64, 16
+    inp = synth.make_scan_inputs(B, L, d, N, "f32", seed=43, stream=4300, dt_range=(0.3, 1.0))
+    dy, dhf, h0 = grads_in(B, L, d, N, seed=44)
+    gz = run_bwd(inp, dy, dhf, h0=h0, zoh=True)
+    gd = run_bwd(inp, dy, dhf, h0=h0)
+    assert (gz["dB"] - gd["dB"]).abs().max().item() > 1e-2
