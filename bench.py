@@ -65,10 +65,22 @@ def decode_alg_bytes(B, d, N, in_bytes=4, out_bytes=4):
     return state, state + B * d * in_bytes * 3 + B * d * out_bytes + 2 * B * N * in_bytes + d * N * 4 + 2 * d * 4
 
 
-def kernel_source_hash():
+# The sources each kernel's counter summary depends on: a summary in
+# profiles/ is used only while these files hash to the value it records.
+KERNEL_SOURCES = {
+    "scan": ["scan_fwd_impl.h", "scan_fwd.hip", "scan_fwd_bb.hip", "bc_pack.h", "device_math.h", "kernels.h",
+             "plan.cpp"],
+    "decode": ["state_update.hip", "device_math.h", "kernels.h"],
+    "ssd": ["ssd.hip", "device_math.h", "kernels.h"],
+    "conv": ["conv1d.hip", "device_math.h", "kernels.h"],
+}
+
+
+def kernel_source_hash(kernel="scan"):
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_87_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "selective_state_space_87_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -96,6 +108,8 @@ SETTLE_S = 0.5
 
 def settle(torch, fn, seconds):
     """Launch fn back to back for `seconds` of wall time; return the count."""
+    if seconds <= 0:
+        return 0
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -266,7 +280,7 @@ def bench_scan(args, torch, binding, synth):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    settled = settle(torch, step, SETTLE_S)
+    settled = settle(torch, step, args.settle_s)
     wall_ms, kern_ms, kern_med_ms = timed_steps(torch, stream, step, args.steps)
 
     # Cold-cache kernel time: flush the 256 MB MALL and the L2s before each launch.
@@ -309,7 +323,7 @@ def bench_decode(args, torch, binding, synth):
     us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
     state_b, alg_b = decode_alg_bytes(w.batch, w.dim, w.dstate)
     gbs = alg_b / (us * 1e-6) / 1e9
-    traffic = counter_traffic("state_update_decode_counters.md", kernel_source_hash())
+    traffic = counter_traffic("state_update_decode_counters.md", kernel_source_hash("decode"))
     return {
         "workload": f"{w.name} (batch={w.batch}, d_inner={w.dim}, N={w.dstate}, f32, "
                     f"{args.decode_steps} chained steps, same token)",
@@ -379,7 +393,8 @@ def bench_conv(args, torch, binding, synth):
     alg = conv_alg_bytes(B, L, d, K, 2, 2)
     fwd = {"workload": f"causal conv1d + SiLU (batch={B}, seqlen={L}, d_inner={d}, width={K}, bf16 in/out, "
                        f"state in/out)", "us_per_call": us,
-           "roofline": hbm_roofline(alg, us, counter_traffic("conv1d_mamba14b_counters.md", kernel_source_hash()))}
+           "roofline": hbm_roofline(alg, us, counter_traffic("conv1d_mamba14b_counters.md",
+                                                             kernel_source_hash("conv")))}
     del x, y
     Bd = 128
     ui = synth.make_conv_inputs(Bd, 1, d, K, "f32", seed=0, stream=701)
@@ -550,7 +565,7 @@ def bench_ssd(args, torch, binding, synth):
     flops = ssd_alg_flops(B, L, H, P, N)
     alg_b = 3 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + B * H * P * N * 4 + 3 * H * 4
     tflops = flops / (us * 1e-6) / 1e12
-    traffic = counter_traffic("ssd_mamba2_counters.md", kernel_source_hash())
+    traffic = counter_traffic("ssd_mamba2_counters.md", kernel_source_hash("ssd"))
     rl = hbm_roofline(alg_b, us, traffic)
     rl.update({"alg_flops_per_launch": flops, "mfma_dtype": "bf16", "mfma_TFLOPs": tflops,
                "mfma_peak_TFLOPs": MFMA_BF16_PEAK / 1e12, "mfma_frac": tflops / (MFMA_BF16_PEAK / 1e12)})
@@ -684,6 +699,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the 130M-shaped and long-sequence scans")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of launches before the headline's timed steps (0 under a counter profiler)")
     ap.add_argument("--no-probe", action="store_true", help="skip the VALU / copy rate probes")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
@@ -729,7 +746,7 @@ def main():
     alg_slots = ups * SLOTS_PER_UPDATE + bld * SLOTS_PER_BLD
     achieved = alg_slots / (kern_ms * 1e-3) / 1e12
     peak = VALU_PEAK_SLOTS / 1e12
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash("scan")
     traffic = counter_traffic("scan_fwd_mamba14b_counters.md", src_hash)
     result = {
         "metric": METRIC,
@@ -751,7 +768,7 @@ def main():
         "kernel_ms": kern_ms,
         "kernel_median_ms": kern_med_ms,
         "cold_kernel_ms": cold_ms,
-        "clock_settle": {"seconds": SETTLE_S, "calls": settled},
+        "clock_settle": {"seconds": args.settle_s, "calls": settled},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "Tslot/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "alg_slots_per_launch": alg_slots, "alg_bytes_per_launch": alg_bytes,

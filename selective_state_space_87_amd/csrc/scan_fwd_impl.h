@@ -110,7 +110,7 @@ constexpr bool bc_in_lds(int NS) { return NS >= 64; }
 // (for the backward pass, which recomputes each tile from them).
 constexpr int kFull = 0, kSummary = 1, kCheckpoint = 2;
 
-template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool ZOH, int MODE>
+template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool ZOH, int MODE, bool PAIR = true>
 __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int NS = S * W;        // padded state count
   // Cooperative items per thread per tile: step w + W*i of the tile. With
@@ -135,8 +135,10 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // 8 tile slots), and each tile is read out two tiles after its recurrence
   // (4 partial buffers); D*u and the gate wait in 8 register sets. Otherwise
   // one barrier per tile, a ring of 4 slots, 2 partial buffers and 4 sets.
-  // (Measured at (4, 8192, 4096, 16) bf16: 608 -> 584 us.)
-  constexpr bool PB = W == 8 && T == 8 && !BCL;
+  // (Measured at (4, 8192, 4096, 16) bf16: 608 -> 584 us.) Its 96 KB of LDS
+  // leave room for one block per CU: chunked plans, whose many short blocks
+  // gain from two per CU, take PAIR = false (one barrier per tile, 48 KB).
+  constexpr bool PB = PAIR && W == 8 && T == 8 && !BCL;
   constexpr int RING = PB ? 8 : 4;
   constexpr int NPB = PB ? 4 : 2;
   constexpr int LAG = PB ? 2 : 1;
@@ -684,7 +686,7 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
   Scan args = s;
   void* kargs[] = {&args};
   if (pl.chunks > 1) {
-    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kSummary>),
+    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kSummary, false>),
                               dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks - 1)),
                               dim3(W * 64), kargs, 0, st);
     if (err != 0) return err;
@@ -700,8 +702,10 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
                           dim3(static_cast<unsigned>((bdn + 255) / 256)), dim3(256), fargs, 0, st);
     if (err != 0) return err;
   }
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull>),
-                         dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks)),
+  const void* full = pl.chunks > 1
+                         ? reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, false>)
+                         : reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, true>);
+  return hipLaunchKernel(full, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks)),
                          dim3(W * 64), kargs, 0, st);
 }
 
