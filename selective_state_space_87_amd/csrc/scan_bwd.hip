@@ -20,7 +20,7 @@
 // w*S .. w*S+S-1, eight waves from N = 16 on with S * T = 16 (N = 16: 8-step
 // tiles; 32: 4 states per lane, 4 steps; 64: 8 states, 2 steps). Two passes:
 //   1. the forward kernel in its checkpoint mode stores every wave's states
-//      at each tile start (scan_fwd_impl.h; same mapping and tiles);
+//      at each tile start (scan_fwd_impl.h; same tiles);
 //   2. this kernel, over the tiles in reverse: recompute the tile's states and
 //      transitions from its checkpoint, read the pre-gate output out of them
 //      (partials over waves in LDS, as in the forward), then run the adjoint
@@ -280,14 +280,17 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
   float e_dy[IT] = {}, e_dsilu[IT] = {}, e_dsp[IT] = {}, e_u[IT] = {}, e_dp[IT] = {};
   // Checkpoint of the next tile to process, fetched one tile ahead.
   float r_ck[S];
+  // (k = -1, past the first tile, is allowed: every load is then masked, or
+  // reads B/C words of other states that nothing uses.)
   auto fetch2 = [&](int k) __attribute__((always_inline)) {
     fetch_items(k);
-    const rsrc_t rck = raw_buffer(p.ckpt + ((static_cast<int64_t>(b) * nt + k) * NS + w * S) * Dm,
+    const int kc = k >= 0 ? k : 0;
+    const rsrc_t rck = raw_buffer(p.ckpt + ((static_cast<int64_t>(b) * nt + kc) * NS + w * S) * Dm,
                                   static_cast<uint32_t>(S * Dm * 4));
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       r_ck[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rck, ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kOutOfRange, 0, 0));
+          rck, ch_ok && k >= 0 ? static_cast<uint32_t>((s * Dm + ch) * 4) : kOutOfRange, 0, 0));
     }
   };
   const rsrc_t rdu_b = raw_buffer(p.du + plane * Dm, f_bytes);
@@ -465,31 +468,41 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
     // barrier). Waves w and w+4, which share a SIMD, take opposite orders
     // (finish first, or compute first), so that one's recurrence overlaps
     // the other's per-item work; the recurrence runs at raised priority.
-    const bool late = (w >> 2) & 1;
-    for (int k = nt - 1; k >= 0; --k) {
+    // Each order is a loop of its own with no branch inside, and the last
+    // iteration fetches and stages the masked tile -1, so that the memory
+    // waits are counted exactly: the next tile's loads are waited for, not
+    // this tile's stores.
+    auto run = [&](auto late_c) __attribute__((always_inline)) {
+      for (int k = nt - 1; k >= 0; --k) {
 #pragma unroll
-      for (int i = 0; i < IT; ++i) {
-        e_dy[i] = m_dy[i], e_dsilu[i] = m_dsilu[i], e_dsp[i] = m_dsp[i], e_u[i] = m_u[i], e_dp[i] = m_dp[i];
-        m_dy[i] = n_dy[i], m_dsilu[i] = n_dsilu[i], m_dsp[i] = n_dsp[i], m_u[i] = n_u[i], m_dp[i] = n_dp[i];
-      }
-      float hh[S];
+        for (int i = 0; i < IT; ++i) {
+          e_dy[i] = m_dy[i], e_dsilu[i] = m_dsilu[i], e_dsp[i] = m_dsp[i], e_u[i] = m_u[i], e_dp[i] = m_dp[i];
+          m_dy[i] = n_dy[i], m_dsilu[i] = n_dsilu[i], m_dsp[i] = n_dsp[i], m_u[i] = n_u[i], m_dp[i] = n_dp[i];
+        }
+        float hh[S];
 #pragma unroll
-      for (int s = 0; s < S; ++s) hh[s] = r_ck[s];
-      if (k > 0) fetch2(k - 1);
-      if (late) {
-        epilogue(k + 1);
-        __builtin_amdgcn_s_setprio(2);
-        compute_tile(k, hh);
-        __builtin_amdgcn_s_setprio(0);
-        if (k > 0) stage2(k - 1);
-      } else {
-        __builtin_amdgcn_s_setprio(2);
-        compute_tile(k, hh);
-        __builtin_amdgcn_s_setprio(0);
-        if (k > 0) stage2(k - 1);
-        epilogue(k + 1);
+        for (int s = 0; s < S; ++s) hh[s] = r_ck[s];
+        fetch2(k - 1);
+        if constexpr (decltype(late_c)::value) {
+          epilogue(k + 1);
+          __builtin_amdgcn_s_setprio(2);
+          compute_tile(k, hh);
+          __builtin_amdgcn_s_setprio(0);
+          stage2(k - 1);
+        } else {
+          __builtin_amdgcn_s_setprio(2);
+          compute_tile(k, hh);
+          __builtin_amdgcn_s_setprio(0);
+          stage2(k - 1);
+          epilogue(k + 1);
+        }
+        __syncthreads();
       }
-      __syncthreads();
+    };
+    if ((w >> 2) & 1) {
+      run(std::true_type{});
+    } else {
+      run(std::false_type{});
     }
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
