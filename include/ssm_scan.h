@@ -104,9 +104,10 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  * Number of sequence chunks the scan of this shape runs in (1: one pass over
  * the whole sequence; 0: invalid or unsupported sizes). Chunking is chosen
  * when the batch has too few 64-channel blocks to occupy the device
- * (N <= 32, B * ceil(d / 64) <= 128 and L >= 2048), or when one batch row's
- * [L, d] plane exceeds 2^30 bytes at 4 bytes per element. Results of a chunked and a
- * single-pass scan agree to rounding; each is deterministic.
+ * (L >= 2048 and B * ceil(d / 64) <= 128 for N <= 32, <= 64 for N >= 33), or
+ * when one batch row's [L, d] plane exceeds 2^30 bytes at 4 bytes per element.
+ * Results of a chunked and a single-pass scan agree to rounding; each is
+ * deterministic.
  */
 int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 

@@ -132,6 +132,14 @@ constexpr int64_t kChunkMinSteps = 1024;
 // 3072 -> 4.75 ms, 4096 -> 4.78 ms.
 constexpr int64_t kBlockSlots = 3072;
 constexpr int64_t kChunkWhenBlocksAtMost = 128;
+// From 64 padded states on (a block holds 8x the work of the N = 16 shape,
+// and the summary pass adds about 0.8 of a pass over the split steps), a
+// scan is split only when at most a quarter of the CUs would have a block,
+// into about one block per CU. Measured (bf16, gate): (1, 8192, 4096, 128)
+// 3317 -> 1752 us, (1, 8192, 2048, 64) 1719 -> 480 us; at 128 blocks,
+// (2, 8192, 4096, 128), splitting lost (3356 -> 3500 us at 512 slots).
+constexpr int64_t kBlockSlotsLarge = 256;
+constexpr int64_t kChunkLargeWhenBlocksAtMost = 64;
 
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 

@@ -36,11 +36,13 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   if (batch > 0 && dim > 0 && p.Lp > 0) {
     const int64_t blocks = batch * p.dim_blocks;
     int64_t k = 1;
-    // (From 64 padded states on, a block already holds 8x the work of the
-    // N = 16 shape and its summary pass spills registers: such scans are
-    // chunked only when the plane size below requires it.)
-    if (p.NS < 64 && blocks <= kChunkWhenBlocksAtMost && p.Lp >= 2 * kChunkMinSteps) {
-      k = kBlockSlots / blocks;
+    // From 64 padded states on a block holds 8x the work of the N = 16
+    // shape: such scans are split only when most of the device would
+    // otherwise idle, and into fewer chunks.
+    const bool large = p.NS >= 64;
+    if (blocks <= (large ? kChunkLargeWhenBlocksAtMost : kChunkWhenBlocksAtMost) &&
+        p.Lp >= 2 * kChunkMinSteps) {
+      k = (large ? kBlockSlotsLarge : kBlockSlots) / blocks;
       if (p.Lp / kChunkMinSteps < k) k = p.Lp / kChunkMinSteps;
       if (k < 1) k = 1;
     }

@@ -114,11 +114,11 @@ template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool 
 __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int NS = S * W;        // padded state count
   // Cooperative items per thread per tile: step w + W*i of the tile. With
-  // fewer steps than waves (the backward's checkpoint pass at N = 32, 64)
-  // waves w >= T have none.
+  // fewer steps than waves (the backward's checkpoint pass at N = 32, 64, the
+  // summary pass from N = 64 on) waves w >= T have none.
   constexpr int IT = T >= W ? T / W : 1;
-  static_assert(T % W == 0 || (MODE == kCheckpoint && W % T == 0),
-                "tile must split evenly over the waves (or the waves over the tile, checkpoints only)");
+  static_assert(T % W == 0 || (MODE != kFull && W % T == 0),
+                "tile must split evenly over the waves (or the waves over the tile, without readout)");
   const bool has_item = T >= W || threadIdx.x < 64 * T;  // (wave-uniform: w < T)
   constexpr int LW = __builtin_ctz(W);
   constexpr int NC = W >= 4 ? W / 4 : 1;            // 16-byte chunks per partial row
@@ -143,6 +143,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int NPB = PB ? 4 : 2;
   constexpr int LAG = PB ? 2 : 1;
   constexpr int UNR = PB ? 8 : 4;
+  static_assert(UNR % RING == 0 && RING % NPB == 0, "tile slots must repeat with the unrolled loop");
 
   // Step sizes live in a ring of RING tile slots (tile k in slot k % RING):
   // tiles are prepared two at a time, every other tile. Partial readouts
@@ -606,27 +607,29 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       // partials (the loop ends with one only after an odd tile, or after
       // every tile without pair barriers).
       if (PB && (last & 1) == 0) __syncthreads();
-      auto sel = [&](const float (&e)[RING][IT], int tile, int i) __attribute__((always_inline)) -> float {
-        float v = e[0][i];
-        static_for<1, RING>([&](auto r) __attribute__((always_inline)) {
-          if ((tile % RING) == decltype(r)::value) v = e[decltype(r)::value][i];
-        });
-        return v;
-      };
-      for (int tl = max(0, nt - LAG); tl < nt; ++tl) {
-        float part[IT];
-        static_for<0, NPB>([&](auto q) __attribute__((always_inline)) {
-          if ((tl % NPB) == decltype(q)::value) {
+      // Tile tl = nt - LAG + D sits in ring slot tl % RING and partial buffer
+      // tl % NPB. The loop runs tiles in groups of UNR (a multiple of RING)
+      // from tile 0, so both follow at compile time from (nt - 1) % UNR: one
+      // branch per value, with constant register-set indexes (an index
+      // computed at run time would put the ring in scratch memory).
+      static_for<0, UNR>([&](auto jl) __attribute__((always_inline)) {
+        constexpr int JL = decltype(jl)::value;
+        if ((nt - 1) % UNR == JL) {
+          static_for<0, LAG>([&](auto dl) __attribute__((always_inline)) {
+            constexpr int D = decltype(dl)::value;
+            constexpr int R = ((JL - (LAG - 1) + D) % RING + RING) % RING;
+            const int tl = nt - LAG + D;
+            if (tl >= 0) {
 #pragma unroll
-            for (int i = 0; i < IT; ++i) part[i] = gather_item(q, i);
-          }
-        });
-#pragma unroll
-        for (int i = 0; i < IT; ++i) {
-          buffer_store_f32<BF16_OUT>((part[i] + sel(eDu, tl, i)) * sel(eG, tl, i), ry_b,
-                                     lane_out + step_off(tl, i, OUT_B));
+              for (int i = 0; i < IT; ++i) {
+                const float part = gather_item(std::integral_constant<int, R % NPB>{}, i);
+                buffer_store_f32<BF16_OUT>((part + eDu[R][i]) * eG[R][i], ry_b,
+                                           lane_out + step_off(tl, i, OUT_B));
+              }
+            }
+          });
         }
-      }
+      });
     }
     if (p.h_final && ch_ok && c == static_cast<int>(gridDim.y) - 1) {
 #pragma unroll
@@ -686,7 +689,12 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
   Scan args = s;
   void* kargs[] = {&args};
   if (pl.chunks > 1) {
-    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kSummary, false>),
+    // The summary's result (a chunk's final state and step-size sum) does
+    // not depend on its tiling. With B/C staged through LDS it takes shorter
+    // tiles (4 steps at 8 states per lane, 2 at 16): with no readout between
+    // steps, 8-step tiles ran out of registers (spilled to scratch).
+    constexpr int TS = bc_in_lds(S * W) ? 32 / S : T;
+    int err = hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, TS, BI, BO, SP, ZH, kSummary, false>),
                               dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks - 1)),
                               dim3(W * 64), kargs, 0, st);
     if (err != 0) return err;

@@ -138,14 +138,22 @@ def test_chunk_plan(lib):
     assert ch(1, 262144, 2560, 16) > 1           # 40 blocks: split in time
     assert ch(1, 4096, 64, 16) > 1
     assert ch(2, 5000, 100, 16) > 1
+    # from 33 states on: split only at 64 blocks or fewer
+    assert ch(1, 8192, 4096, 128) > 1            # 64 blocks
+    assert ch(1, 8192, 2048, 64) > 1
+    assert ch(2, 8192, 4096, 128) == 1           # 128 blocks
+    assert ch(4, 2048, 4096, 128) == 1
+    assert ch(1, 8192, 4096, 33) > 1
     # plane limit alone: many blocks, but L * d * 4 bytes above 2^30
     assert ch(200, (1 << 20) + 16, 256, 16) > 1
     assert ch(200, 1 << 20, 256, 16) == 1
-    for B, L, d, N in [(1, 262144, 2560, 16), (1, 4096, 64, 16), (2, 5000, 100, 16), (1, 3000, 64, 3)]:
+    for B, L, d, N in [(1, 262144, 2560, 16), (1, 4096, 64, 16), (2, 5000, 100, 16), (1, 3000, 64, 3),
+                       (1, 8192, 4096, 128)]:
         k = ch(B, L, d, N)
         ws = lib.ssm_scan_workspace_bytes(B, L, d, N)
         summaries = (k - 1) * B * d * (N + 1) * 4
-        assert ws >= summaries + 2 * B * N * L * 4 * (1 if N != 3 else 0), (B, L, d, N, k, ws)
+        packed_bc = 2 * B * N * L * 4 if N == 16 else 0  # (none from 64 padded states on)
+        assert ws >= summaries + packed_bc, (B, L, d, N, k, ws)
         # the chunks' padded lengths cover the sequence, each at least 1024 steps when split
         assert k == 1 or L // k >= 1000
 

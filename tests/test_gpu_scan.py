@@ -114,10 +114,11 @@ def test_large_state(B, L, d, N, dt):
 
 
 def test_large_state_chunked_by_plane_size():
-    """N = 128 is chunked only when a batch row's plane passes 2^30 bytes
-    (here 65,600 x 4,096 x 4 bytes): the summary pass and the carry fold."""
+    """N = 128 with a batch row's plane above 2^30 bytes (here 65,600 x 4,096
+    x 4 bytes) at 64 channel blocks: the summary pass (its own short tiles)
+    and the carry fold over sampled channels."""
     B, L, d, N = 1, 65600, 4096, 128
-    assert binding.ssm_scan_chunks(1, 4100, 64, N) == 1
+    assert binding.ssm_scan_chunks(2, 8192, 4096, N) == 1   # 128 blocks: one pass
     k = binding.ssm_scan_chunks(B, L, d, N)
     assert k > 1
     inp = synth.make_scan_inputs(B, L, d, N, "bf16", seed=5, stream=4500)
@@ -260,6 +261,8 @@ def test_guard_bands_and_full_coverage():
 CHUNKED = [
     (1, 4096, 64, 16, "f32"), (2, 5000, 100, 16, "bf16"), (1, 3000, 64, 3, "f32"),
     (1, 2100, 130, 32, "bf16"), (1, 2048, 1, 1, "f32"), (3, 6000, 40, 8, "bf16"),
+    # from 33 states on: B/C through LDS, the summary pass in 2- or 4-step tiles
+    (1, 2100, 64, 128, "bf16"), (1, 2050, 40, 64, "f32"), (2, 2064, 33, 100, "f32"), (1, 3000, 70, 33, "bf16"),
 ]
 
 

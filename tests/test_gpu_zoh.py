@@ -93,7 +93,8 @@ def _oracle_args(inp):
                 delta_bias=f["delta_bias"], delta_softplus=True)
 
 
-@pytest.mark.parametrize("B,L,d,N,dt", [(1, 4100, 64, 16, "bf16"), (2, 3000, 40, 8, "f32")])
+@pytest.mark.parametrize("B,L,d,N,dt", [(1, 4100, 64, 16, "bf16"), (2, 3000, 40, 8, "f32"), (1, 2100, 64, 128, "bf16"),
+                                       (1, 2050, 40, 64, "f32")])
 def test_zoh_chunked(B, L, d, N, dt):
     k = binding.ssm_scan_chunks(B, L, d, N)
     assert k > 1
