@@ -261,6 +261,8 @@ def test_guard_bands_and_full_coverage():
 CHUNKED = [
     (1, 4096, 64, 16, "f32"), (2, 5000, 100, 16, "bf16"), (1, 3000, 64, 3, "f32"),
     (1, 2100, 130, 32, "bf16"), (1, 2048, 1, 1, "f32"), (3, 6000, 40, 8, "bf16"),
+    # two states per lane with padding states (N padded to 16 and 32)
+    (1, 2100, 64, 15, "bf16"), (1, 2050, 64, 24, "f32"),
     # from 33 states on: B/C through LDS, the summary pass in 2- or 4-step tiles
     (1, 2100, 64, 128, "bf16"), (1, 2050, 40, 64, "f32"), (2, 2064, 33, 100, "f32"), (1, 3000, 70, 33, "bf16"),
 ]
