@@ -73,6 +73,8 @@ KERNEL_SOURCES = {
     "decode": ["state_update.hip", "device_math.h", "kernels.h"],
     "ssd": ["ssd.hip", "device_math.h", "kernels.h"],
     "conv": ["conv1d.hip", "device_math.h", "kernels.h"],
+    "bwd": ["scan_bwd.hip", "scan_fwd_impl.h", "scan_ckpt_b.hip", "bc_pack.h", "device_math.h", "kernels.h",
+            "plan.cpp"],
 }
 
 
@@ -97,6 +99,23 @@ def counter_traffic(profile_name, src_hash):
     if not (m_hash and m_b) or m_hash.group(1) != src_hash:
         return None
     return float(m_b.group(1))
+
+
+def valu_counters(profile_name, src_hash):
+    """Issued / algorithmic VALU lane-slots and VALU busy of a kernel, from its
+    committed rocprofv3 counter summary, if that was taken on the current
+    kernel sources (same source hash); else None."""
+    p = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", txt)
+    m_ratio = re.search(r"issued / algorithmic:\s*\**([0-9.]+)", txt)
+    m_busy = re.search(r"VALU busy[^:]*:\s*([0-9.]+)", txt)
+    if not (m_hash and m_ratio and m_busy) or m_hash.group(1) != src_hash:
+        return None
+    return {"issued_per_algorithmic_slot": float(m_ratio.group(1)), "valu_busy": float(m_busy.group(1)),
+            "profile": profile_name}
 
 
 # The engine clock takes tens of milliseconds of load to reach its steady
@@ -604,7 +623,8 @@ def bench_bwd(args, torch, binding, synth, inp):
     return {"workload": f"{w.name} backward (dy float32, all gradients float32)", "us_per_call": us,
             "G_updates_per_s": ups / (us * 1e-6) / 1e9,
             "roofline": {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_SLOTS / 1e12, "unit": "Tslot/s",
-                         "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
+                         "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots,
+                         "valu_counters": valu_counters("scan_bwd_mamba14b_valu.md", kernel_source_hash("bwd"))}}
 
 
 def alu_roofline(slots, us):
@@ -774,7 +794,8 @@ def main():
                      "alg_slots_per_launch": alg_slots, "alg_bytes_per_launch": alg_bytes,
                      "hbm_GBps": alg_bytes / (kern_ms * 1e-3) / 1e9,
                      "hbm_frac": alg_bytes / (kern_ms * 1e-3) / HBM_BPS,
-                     "source_hash": src_hash},
+                     "source_hash": src_hash,
+                     "valu_counters": valu_counters("scan_fwd_mamba14b_valu.md", src_hash)},
     }
     if not args.no_workloads:
         result["mamba130m"] = bench_workload(args, torch, binding, synth, 1, 50)
