@@ -400,7 +400,10 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
 //   state    (B o w)^T X = B^T (w x)       w x = hi + lo          2 x
 // Operands are read as 16-byte runs of 8 consecutive k: every LDS array is
 // laid out with the contraction index contiguous (x, w x and B are also
-// stored transposed), rows padded by 8 elements (16 bytes).
+// stored transposed). x^T's rows are padded by 8 elements (16 bytes), which
+// keeps its transposing 2-byte stores on distinct banks; the other arrays
+// permute their 16-byte chunks per row (swz), which keeps the operand reads
+// on distinct banks.
 // With N >= 64 the block has sixteen waves (four per SIMD, at most 128
 // registers each), so that one wave's LDS and transcendental latencies hide
 // behind three others' work; the LDS arrays (up to 157 KiB at N = 128) allow
@@ -423,6 +426,20 @@ __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *reinterpret_
 // consecutive rows, one run each) keeps its conflict-free pattern.
 __device__ __forceinline__ int xt_at(int pp, int s) { return pp * (kQ + 8) + (s ^ (8 * ((pp >> 4) & 3))); }
 
+// Element (r, e) of a bfloat16 array of RE elements per row whose 16-byte
+// chunks (8 elements) are permuted per row: chunk c of row r is stored at
+// c ^ 2 ((r / (32 / C)) mod (C / 2)), C = RE / 8 chunks per row. gfx950 serves
+// a 16-byte LDS read 32 lanes at a time over 128 four-byte banks; an MFMA
+// operand read (lane l: row l mod 16, chunk 4 j + l / 16) then touches every
+// bank once per 32 lanes, where rows padded by 16 bytes hit each bank twice
+// (measured with a probe: 116 against 178 bytes per clock per CU).
+template <int RE>
+__device__ __forceinline__ int swz(int r, int e) {
+  constexpr int C = RE / 8, PER = C >= 16 ? 1 : 16 / C;
+  static_assert(RE % 8 == 0 && C >= 2 && C <= 16 && (C & (C - 1)) == 0, "rows of 2 to 16 chunks");
+  return r * RE + ((((e >> 3) ^ ((r / PER) & (C - 1))) << 3) | (e & 7));
+}
+
 __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
   hi = f32_to_bf16_bits(v);
   lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
@@ -431,8 +448,11 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
 template <int NP, int WV, bool BF16_OUT, bool SOFTPLUS>
 __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
   constexpr int NTH = 64 * WV;   // threads of the block (WV waves: 8, or 16 for NP >= 64)
-  constexpr int CS = NP + 8;     // row stride of C, B [Q][NP] and H^T [P][NP] (elements)
-  constexpr int QS = kQ + 8;     // row stride of x^T [P][Q], S [Q][Q], (B o w)^T [NP][Q]
+  constexpr int QS = kQ + 8;     // row stride of x^T [P][Q] (elements)
+  // C, B [Q][NP] and H^T [P][NP] in rows of NP; S [Q][Q], B^T [NP][Q] and
+  // (w x)^T [P][Q] in rows of Q; both with permuted 16-byte chunks (swz).
+  auto cix = [](int r, int e) __attribute__((always_inline)) { return swz<NP>(r, e); };
+  auto qix = [](int r, int e) __attribute__((always_inline)) { return swz<kQ>(r, e); };
   // Y (and its readout) is 4 x 4 tiles of 16 x 16 (t by p); a wave takes YW
   // tiles of one column p: t-tiles {w/4, 3 - w/4} with 8 waves (equal
   // shares of the triangular S X), t-tile w/4 with 16.
@@ -453,13 +473,13 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef std::conditional_t<XE == 8, u32x4, u32x2> xw_t;       // a thread's run of x
   typedef std::conditional_t<CPL == 8, u32x4, u32x2> zw_t;      // a lane's gate values
-  __shared__ __attribute__((aligned(16))) uint16_t sC[kQ * CS];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * CS];
-  __shared__ __attribute__((aligned(16))) uint16_t sBt[NP * QS];     // B^T (exact)
-  __shared__ __attribute__((aligned(16))) uint16_t sXw[2][kP * QS];  // (w x)^T, hi and lo
+  __shared__ __attribute__((aligned(16))) uint16_t sC[kQ * NP];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * NP];
+  __shared__ __attribute__((aligned(16))) uint16_t sBt[NP * kQ];     // B^T (exact)
+  __shared__ __attribute__((aligned(16))) uint16_t sXw[2][kP * kQ];  // (w x)^T, hi and lo
   __shared__ __attribute__((aligned(16))) uint16_t sXt[2][kP * QS];  // x^T, by chunk parity
-  __shared__ __attribute__((aligned(16))) uint16_t sS[2][kQ * QS];   // S, hi and lo
-  __shared__ __attribute__((aligned(16))) uint16_t sHt[2][kP * CS];  // H^T, hi and lo
+  __shared__ __attribute__((aligned(16))) uint16_t sS[2][kQ * kQ];   // S, hi and lo
+  __shared__ __attribute__((aligned(16))) uint16_t sHt[2][kP * NP];  // H^T, hi and lo
   __shared__ __attribute__((aligned(16))) float sCs[kQ];
   __shared__ __attribute__((aligned(16))) float sDt[kQ];
   __shared__ float sW[kQ];
@@ -496,7 +516,7 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
 
   // S above the diagonal blocks is read (k-steps of 32 cover it) but never
   // written: zero it once.
-  for (int i = tid; i < 2 * kQ * QS; i += NTH) (&sS[0][0])[i] = 0;
+  for (int i = tid; i < 2 * kQ * kQ; i += NTH) (&sS[0][0])[i] = 0;
   f32x4 hacc[SN * SPC];  // tile (jn, jp) at jn * SPC + jp
 #pragma unroll
   for (int j = 0; j < SN * SPC; ++j) {
@@ -506,7 +526,7 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       const int n = 16 * (nb + j / SPC) + 4 * lk + v;
       const float h = p.h0 ? p.h0[hsb + static_cast<int64_t>(pc) * N + n] : 0.0f;
       hacc[j][v] = h;
-      split_bf16(h, sHt[0][pc * CS + n], sHt[1][pc * CS + n]);
+      split_bf16(h, sHt[0][cix(pc, n)], sHt[1][cix(pc, n)]);
     }
   }
 
@@ -583,8 +603,8 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       const int e = (i * NTH + tid) * 8;
       if (e >= kQ * NP) break;
       const int t = e / NP, n = e % NP;
-      *reinterpret_cast<u32x4*>(&sB[t * CS + n]) = br[i];
-      *reinterpret_cast<u32x4*>(&sC[t * CS + n]) = cr[i];
+      *reinterpret_cast<u32x4*>(&sB[cix(t, n)]) = br[i];
+      *reinterpret_cast<u32x4*>(&sC[cix(t, n)]) = cr[i];
     }
     zq = zr;
     if (w == 0) {
@@ -625,10 +645,10 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       u32x4 v;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[j] = static_cast<uint32_t>(sB[(s0 + 2 * j) * CS + n]) |
-               (static_cast<uint32_t>(sB[(s0 + 2 * j + 1) * CS + n]) << 16);
+        v[j] = static_cast<uint32_t>(sB[cix(s0 + 2 * j, n)]) |
+               (static_cast<uint32_t>(sB[cix(s0 + 2 * j + 1, n)]) << 16);
       }
-      *reinterpret_cast<u32x4*>(&sBt[n * QS + s0]) = v;
+      *reinterpret_cast<u32x4*>(&sBt[qix(n, s0)]) = v;
     }
     if (tid >= XW0) {
       const int item = tid - XW0;
@@ -646,8 +666,8 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
         vh[j] = static_cast<uint32_t>(hi[2 * j]) | (static_cast<uint32_t>(hi[2 * j + 1]) << 16);
         vl[j] = static_cast<uint32_t>(lo[2 * j]) | (static_cast<uint32_t>(lo[2 * j + 1]) << 16);
       }
-      *reinterpret_cast<u32x4*>(&sXw[0][xt_at(pp, s0)]) = vh;
-      *reinterpret_cast<u32x4*>(&sXw[1][xt_at(pp, s0)]) = vl;
+      *reinterpret_cast<u32x4*>(&sXw[0][qix(pp, s0)]) = vh;
+      *reinterpret_cast<u32x4*>(&sXw[1][qix(pp, s0)]) = vl;
     }
     // (2b) Scores: lower tiles q = w, w + WV; S = G decayed and scaled, split.
     // Computed transposed, G^T = B C^T, so that a lane holds 4 consecutive s
@@ -667,7 +687,7 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       for (int k0 = 0; k0 < NP; k0 += 32) {
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
-          g[j] = mfma32(lds8(&sB[(16 * si[j] + lr) * CS + k0 + 8 * lk]), lds8(&sC[(16 * ti[j] + lr) * CS + k0 + 8 * lk]),
+          g[j] = mfma32(lds8(&sB[cix(16 * si[j] + lr, k0 + 8 * lk)]), lds8(&sC[cix(16 * ti[j] + lr, k0 + 8 * lk)]),
                         g[j]);
         }
       }
@@ -685,10 +705,10 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
           // D x enters S X as D on the diagonal of S
           split_bf16(t > s0 + v ? val : (t == s0 + v ? val + Dh : 0.0f), hi[v], lo[v]);
         }
-        *reinterpret_cast<u32x2*>(&sS[0][t * QS + s0]) =
+        *reinterpret_cast<u32x2*>(&sS[0][qix(t, s0)]) =
             u32x2{static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
                   static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
-        *reinterpret_cast<u32x2*>(&sS[1][t * QS + s0]) =
+        *reinterpret_cast<u32x2*>(&sS[1][qix(t, s0)]) =
             u32x2{static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16),
                   static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
       }
@@ -708,11 +728,11 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
     for (int j = 0; j < YW; ++j) yacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k0 = 0; k0 < NP; k0 += 32) {
-      const bf16x8 hh = lds8(&sHt[0][pcol * CS + k0 + 8 * lk]);
-      const bf16x8 hl = lds8(&sHt[1][pcol * CS + k0 + 8 * lk]);
+      const bf16x8 hh = lds8(&sHt[0][cix(pcol, k0 + 8 * lk)]);
+      const bf16x8 hl = lds8(&sHt[1][cix(pcol, k0 + 8 * lk)]);
 #pragma unroll
       for (int j = 0; j < YW; ++j) {
-        const bf16x8 cv = lds8(&sC[(16 * yt[j] + lr) * CS + k0 + 8 * lk]);
+        const bf16x8 cv = lds8(&sC[cix(16 * yt[j] + lr, k0 + 8 * lk)]);
         yacc[j] = mfma32(cv, hh, yacc[j]);
         yacc[j] = mfma32(cv, hl, yacc[j]);
       }
@@ -729,11 +749,11 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       for (int k0 = 0; k0 < 16 * (TB + 1); k0 += 32) {
         const bf16x8 xv = lds8(&xt[xt_at(pcol, k0 + 8 * lk)]);
         if (k0 < 16 * (TA + 1)) {
-          yacc[0] = mfma32(lds8(&sS[0][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
-          yacc[0] = mfma32(lds8(&sS[1][(16 * TA + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
+          yacc[0] = mfma32(lds8(&sS[0][qix(16 * TA + lr, k0 + 8 * lk)]), xv, yacc[0]);
+          yacc[0] = mfma32(lds8(&sS[1][qix(16 * TA + lr, k0 + 8 * lk)]), xv, yacc[0]);
         }
-        yacc[YW - 1] = mfma32(lds8(&sS[0][(16 * TB + lr) * QS + k0 + 8 * lk]), xv, yacc[YW - 1]);
-        yacc[YW - 1] = mfma32(lds8(&sS[1][(16 * TB + lr) * QS + k0 + 8 * lk]), xv, yacc[YW - 1]);
+        yacc[YW - 1] = mfma32(lds8(&sS[0][qix(16 * TB + lr, k0 + 8 * lk)]), xv, yacc[YW - 1]);
+        yacc[YW - 1] = mfma32(lds8(&sS[1][qix(16 * TB + lr, k0 + 8 * lk)]), xv, yacc[YW - 1]);
       }
     };
     if constexpr (YW == 2) {
@@ -746,14 +766,14 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       // one tile: TA = TB (the first product pair is the only one)
       if (yt[0] < 2) {
         const bf16x8 xv = lds8(&xt[xt_at(pcol, 8 * lk)]);
-        yacc[0] = mfma32(lds8(&sS[0][(16 * yt[0] + lr) * QS + 8 * lk]), xv, yacc[0]);
-        yacc[0] = mfma32(lds8(&sS[1][(16 * yt[0] + lr) * QS + 8 * lk]), xv, yacc[0]);
+        yacc[0] = mfma32(lds8(&sS[0][qix(16 * yt[0] + lr, 8 * lk)]), xv, yacc[0]);
+        yacc[0] = mfma32(lds8(&sS[1][qix(16 * yt[0] + lr, 8 * lk)]), xv, yacc[0]);
       } else {
 #pragma unroll
         for (int k0 = 0; k0 < kQ; k0 += 32) {
           const bf16x8 xv = lds8(&xt[xt_at(pcol, k0 + 8 * lk)]);
-          yacc[0] = mfma32(lds8(&sS[0][(16 * yt[0] + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
-          yacc[0] = mfma32(lds8(&sS[1][(16 * yt[0] + lr) * QS + k0 + 8 * lk]), xv, yacc[0]);
+          yacc[0] = mfma32(lds8(&sS[0][qix(16 * yt[0] + lr, k0 + 8 * lk)]), xv, yacc[0]);
+          yacc[0] = mfma32(lds8(&sS[1][qix(16 * yt[0] + lr, k0 + 8 * lk)]), xv, yacc[0]);
         }
       }
     }
@@ -766,12 +786,12 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       bf16x8 xh[SPC], xl[SPC];
 #pragma unroll
       for (int jp = 0; jp < SPC; ++jp) {
-        xh[jp] = lds8(&sXw[0][xt_at(16 * (pb + jp) + lr, k0 + 8 * lk)]);
-        xl[jp] = lds8(&sXw[1][xt_at(16 * (pb + jp) + lr, k0 + 8 * lk)]);
+        xh[jp] = lds8(&sXw[0][qix(16 * (pb + jp) + lr, k0 + 8 * lk)]);
+        xl[jp] = lds8(&sXw[1][qix(16 * (pb + jp) + lr, k0 + 8 * lk)]);
       }
 #pragma unroll
       for (int jn = 0; jn < SN; ++jn) {
-        const bf16x8 bv = lds8(&sBt[(16 * (nb + jn) + lr) * QS + k0 + 8 * lk]);
+        const bf16x8 bv = lds8(&sBt[qix(16 * (nb + jn) + lr, k0 + 8 * lk)]);
 #pragma unroll
         for (int jp = 0; jp < SPC; ++jp) {
           hacc[jn * SPC + jp] = mfma32(bv, xh[jp], hacc[jn * SPC + jp]);
@@ -842,10 +862,10 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
       uint16_t hi[4], lo[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) split_bf16(hacc[j][v], hi[v], lo[v]);
-      *reinterpret_cast<u32x2*>(&sHt[0][pc * CS + n]) =
+      *reinterpret_cast<u32x2*>(&sHt[0][cix(pc, n)]) =
           u32x2{static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
                 static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
-      *reinterpret_cast<u32x2*>(&sHt[1][pc * CS + n]) =
+      *reinterpret_cast<u32x2*>(&sHt[1][cix(pc, n)]) =
           u32x2{static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16),
                 static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
     }
