@@ -513,11 +513,15 @@ def bench_zoh(args, torch, binding, synth, inp):
                          "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
 
 
-def bench_large_state(args, torch, binding, synth):
+def bench_large_state(args, torch, binding, synth, B=4, L=2048):
     """The scan at N = 128 (B and C staged through LDS), on the 1.4B layer's
-    width with a shorter sequence: (4, 2048, 4096, 128), bf16 in and out."""
+    width: (4, 2048, 4096, 128), bf16 in and out, 256 channel blocks; or
+    (2, 8192, 4096, 128), 128 blocks, where each channel's states run in two
+    blocks (partial readouts through the workspace and a combine pass). For
+    the latter, the allocation-free entry point, which keeps one block per
+    channel at this size, is timed beside it."""
     import numpy as np
-    B, L, d, N = 4, 2048, 4096, 128
+    d, N = 4096, 128
     inp = synth.make_scan_inputs(B, L, d, N, "bf16", seed=0, stream=4200)
     dev = torch.device("cuda:0")
 
@@ -538,10 +542,19 @@ def bench_large_state(args, torch, binding, synth):
     ups = B * L * d * N
     slots = ups * SLOTS_PER_UPDATE + B * L * d * SLOTS_PER_BLD
     ach = slots / (us * 1e-6) / 1e12
-    return {"workload": f"scan, N=128 (batch={B}, seqlen={L}, d_inner={d}, bf16 in/out, h_final)",
-            "us_per_call": us, "G_updates_per_s": ups / (us * 1e-6) / 1e9,
-            "roofline": {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_SLOTS / 1e12, "unit": "Tslot/s",
-                         "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
+    split = binding.ssm_scan_workspace_bytes(B, L, d, N) >= 2 * B * L * d * 4
+    out = {"workload": f"scan, N=128 (batch={B}, seqlen={L}, d_inner={d}, bf16 in/out, h_final)"
+                       + (", states split over two blocks per channel" if split else ""),
+           "us_per_call": us, "G_updates_per_s": ups / (us * 1e-6) / 1e9,
+           "roofline": {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_SLOTS / 1e12, "unit": "Tslot/s",
+                        "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots}}
+    if split and binding.ssm_scan_workspace_bytes(B, L, d, N) > (64 << 20):
+        fn1 = lambda: binding.ssm_selective_scan_fwd_noalloc(t["u"], t["delta"], t["A"], t["B"], t["C"],  # noqa
+                                                             y, D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                                                             delta_softplus=True, h_final=hf)
+        us1 = _timed(torch, fn1, max(3, args.large_state_steps // 2), 3)
+        out["one_block_per_channel_us_per_call"] = us1
+    return out
 
 
 # Mamba-2 SSD layer, chunked matrix form with chunks of Q = 64 steps. Its
@@ -810,6 +823,7 @@ def main():
         result["ssd"] = bench_ssd(args, torch, binding, synth)
     if not args.no_large_state:
         result["scan_n128"] = bench_large_state(args, torch, binding, synth)
+        result["scan_n128_split"] = bench_large_state(args, torch, binding, synth, B=2, L=8192)
     if not args.no_bwd:
         result["scan_bwd"] = bench_bwd(args, torch, binding, synth, inp)
     if not args.no_conv:

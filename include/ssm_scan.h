@@ -95,8 +95,13 @@ const char* ssm_status_string(int status);
  * operator (A_i, b_i) (+) (A_j, b_j) = (A_j A_i, A_j b_i + b_j) of
  * "Mamba的隐藏代价" (kongchang.com), section on sequential gradients, and the
  * chunked processing with a carried state of intelliparadigm.com section 6.2.
- * It depends only on the four sizes. Returns 0 for invalid or unsupported
- * sizes, and for batch, dim or seqlen 0.
+ * With 65 to 128 padded states (N > 64) and 65 to 128 blocks of 64 channels
+ * (B * ceil(d / 64)) in a single pass, each channel's states are split over
+ * two blocks of 64 so that the device fills; the workspace then also holds
+ * the two float32 partial readouts sum_n C h over each half of the states,
+ * [2][B, L, d] (rounded up), which a combine pass adds in that order before
+ * the skip and the gate. It depends only on the four sizes. Returns 0 for
+ * invalid or unsupported sizes, and for batch, dim or seqlen 0.
  */
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
@@ -130,8 +135,8 @@ int64_t ssm_scan_chunks(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
  *   y         [B, L, d]  out_dtype  output; must not overlap any input
  *   h_final   [B, d, N]  float32    final state (optional); may equal h0
  *   workspace, workspace_bytes      device scratch of at least
- *                                   ssm_scan_workspace_bytes() bytes (may be
- *                                   NULL when that is 0)
+ *                                   ssm_scan_workspace_bytes() bytes, 16-byte
+ *                                   aligned (may be NULL when that is 0)
  *   stream                          hipStream_t
  *
  * L = 0 writes h_final = h0 (or zeros) and nothing else. Results are
@@ -159,6 +164,10 @@ int ssm_selective_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
  *     overlap in time on one GPU (other streams, other threads) race and
  *     must be serialised by the caller. Nothing in the array needs to start
  *     at zero; a call keeps no state in it for the next one.
+ *   - A shape whose states ssm_selective_scan_fwd splits over two blocks
+ *     (see ssm_scan_workspace_bytes), with partial readouts too large for the
+ *     array, runs here with one block per channel instead: its results then
+ *     agree with ssm_selective_scan_fwd to rounding, not bitwise.
  *   - Otherwise as ssm_selective_scan_fwd (same validation, results bitwise
  *     equal to it for the same inputs).
  */

@@ -98,8 +98,15 @@ int scan_fwd_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
       !safe_mul(batch, dim, &bdn) || !safe_mul(bdn, dstate, &bdn) || !safe_mul(dim, dstate, &dn)) {
     return SSM_E_SHAPE;
   }
-  const ssm::ScanPlan plan = ssm::plan_scan(batch, seqlen, dim, dstate);
+  ssm::ScanPlan plan = ssm::plan_scan(batch, seqlen, dim, dstate);
   if (!plan.ok) return SSM_E_UNSUPPORTED;
+  // The allocation-free entry runs a plan that splits states over blocks only
+  // when its partial-readout planes fit the library's scratch array.
+  bool allow_split = true;
+  if (noalloc && plan.splits > 1 && plan.bytes > ssm::scan_scratch_bytes()) {
+    allow_split = false;
+    plan = ssm::plan_scan(batch, seqlen, dim, dstate, false);
+  }
   if (batch == 0 || dim == 0) return SSM_OK;  // no channel: nothing to compute or write
   const int64_t isz = in_dtype == 1 ? 2 : 4, osz = out_dtype == 1 ? 2 : 4;
   if (A == nullptr) return SSM_E_NULLPTR;
@@ -115,6 +122,7 @@ int scan_fwd_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
     if (p && !aligned(p, 4)) return SSM_E_ALIGN;
   }
   const size_t need = plan.bytes;
+  if (!noalloc && need > 0 && workspace != nullptr && !aligned(workspace, 16)) return SSM_E_ALIGN;
   if (noalloc) {
     if (need > ssm::scan_scratch_bytes()) return SSM_E_WORKSPACE;
     workspace = nullptr;  // a separate device allocation: overlaps nothing of the caller's
@@ -163,6 +171,7 @@ int scan_fwd_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
   a.out_bf16 = out_dtype;
   a.delta_softplus = (flags & SSM_FLAG_SOFTPLUS) != 0;
   a.zoh = (flags & SSM_FLAG_ZOH) != 0;
+  a.allow_split = allow_split ? 1 : 0;
   return map_hip(noalloc ? ssm::launch_scan_noalloc(a, stream) : ssm::launch_scan(a, stream));
 }
 

@@ -22,6 +22,7 @@ struct ScanArgs {
   void* workspace;
   int64_t batch, seqlen, dim, dstate;
   int in_bf16, out_bf16, delta_softplus, zoh;
+  int allow_split;  // the plan may split a channel's states over blocks (see ScanPlan)
 };
 
 struct UpdateArgs {
@@ -112,6 +113,12 @@ constexpr int64_t kSsdMaxState = 128;
 // the B/C pre-pass: per-chunk summaries (local final state from zero, and the
 // sum of the step sizes), an in-order fold of the summaries into each chunk's
 // incoming state, and the full scan of every chunk from that state.
+// With 128 padded states and too few channel blocks for the device but too
+// many for time chunks to pay, a single-pass scan instead splits every
+// channel's states over `splits` = 2 blocks of 64 states each: each writes
+// the float32 partial readout of its states, sum_n C h, to a plane of the
+// workspace (`part_plane` elements apart), and a combine pass forms
+// y = (part_0 + part_1 + D u) silu(z) in that fixed order.
 // Pure function of the sizes (not of the device or the dtypes).
 struct ScanPlan {
   bool ok;                 // false: sizes beyond what the kernels address
@@ -119,7 +126,9 @@ struct ScanPlan {
   int64_t Lp;              // sequence length padded to a multiple of kPadSteps
   int64_t chunk, chunks;   // steps per chunk (multiple of kPadSteps), chunk count
   int64_t dim_blocks;      // blocks of 64 channels per batch row
-  size_t off_bc, off_hsum, off_ssum, bytes;  // workspace layout
+  int splits;              // blocks per channel (state groups of NS / splits)
+  int64_t part_plane;      // elements per partial-readout plane (multiple of 64)
+  size_t off_bc, off_hsum, off_ssum, off_part, bytes;  // workspace layout
 };
 
 constexpr int64_t kPadSteps = 16;        // tiles never straddle this boundary
@@ -140,8 +149,12 @@ constexpr int64_t kChunkWhenBlocksAtMost = 128;
 // (2, 8192, 4096, 128), splitting lost (3356 -> 3500 us at 512 slots).
 constexpr int64_t kBlockSlotsLarge = 256;
 constexpr int64_t kChunkLargeWhenBlocksAtMost = 64;
+// 128 padded states at 65 to 128 channel blocks: two blocks per channel.
+constexpr int64_t kSplitWhenBlocksAtMost = 128;
 
-ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+// allow_split = false keeps every channel in one block (no partial planes in
+// the workspace).
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool allow_split = true);
 
 // Backward: same state mapping (N <= 16), the forward's tiles; workspace
 // = packed B/C, per-tile state checkpoints [B][tiles][NS][d], per-block

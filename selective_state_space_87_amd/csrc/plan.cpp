@@ -18,7 +18,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, bool allow_split) {
   ScanPlan p{};
   p.ok = batch >= 0 && seqlen >= 0 && dim >= 0 && dstate >= 1 && dstate <= kMaxScanStates &&
          seqlen < (int64_t(1) << 30) && dim < (int64_t(1) << 24);
@@ -33,6 +33,8 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   p.dim_blocks = ceil_div(dim, 64);
   p.chunks = 1;
   p.chunk = p.Lp;
+  p.splits = 1;
+  p.part_plane = 0;
   if (batch > 0 && dim > 0 && p.Lp > 0) {
     const int64_t blocks = batch * p.dim_blocks;
     int64_t k = 1;
@@ -58,10 +60,20 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
     p.chunk = round_up(ceil_div(p.Lp, k), kPadSteps);
     if (p.chunk > steps_max) p.chunk = steps_max;
     p.chunks = ceil_div(p.Lp, p.chunk);
+    // Two blocks of 64 states per channel where one block per channel would
+    // leave at least half of the device idle and the sequence is not split
+    // in time. The partial readouts cross HBM once in float32 (written, then
+    // read by the combine pass), small beside 128 state updates per element.
+    if (allow_split && p.NS == 128 && p.chunks == 1 && blocks > kChunkLargeWhenBlocksAtMost &&
+        blocks <= kSplitWhenBlocksAtMost) {
+      p.splits = 2;
+      p.part_plane = round_up(batch * seqlen * dim, 64);
+    }
   }
   // Workspace: packed B/C (one word per (b, n, step) for bfloat16 inputs,
   // two for float32; sized for float32; none from 64 padded states on, where
-  // the kernel reads B and C as given), then the chunk summaries.
+  // the kernel reads B and C as given), then the chunk summaries, then the
+  // partial-readout planes of a split plan ([splits][B, L, d] float32).
   size_t off = 0;
   p.off_bc = off;
   if (batch > 0 && dim > 0 && p.Lp > 0 && p.NS < 64) off += align256(size_t(2 * batch * p.NS * p.Lp) * 4);
@@ -69,6 +81,8 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   if (p.chunks > 1) off += align256(size_t(p.chunks * batch * dim * dstate) * 4);
   p.off_ssum = off;
   if (p.chunks > 1) off += align256(size_t((p.chunks - 1) * batch * dim) * 4);
+  p.off_part = off;
+  if (p.splits > 1) off += align256(size_t(p.splits * p.part_plane) * 4);
   p.bytes = off;
   return p;
 }

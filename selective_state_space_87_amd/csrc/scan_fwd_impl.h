@@ -58,12 +58,13 @@ struct Scan {
   const uint32_t* BC;  // packed B/C (see bc_pack_kernel); null when staged through LDS
   const void* Bm;      // B and C as given, [B, L, N] (read directly when staged through LDS)
   const void* Cm;
-  void* y;
+  void* y;             // output; with states split over blocks, the partial-readout planes
   float* h_final;
   float* hsum;         // summary pass: chunk c's final state from zero into slot c + 1;
                        // checkpoint pass: states at every tile start, [B][tiles][NS][d]
   float* ssum;         // summary pass: chunk c's sum of step sizes, [chunks-1][B][d]
   int L, Lp, dim, N, chunk, batch;
+  int64_t y_split;     // states split over blocks: elements between partial planes (else 0)
 };
 
 // Per (input, output) dtype: launch the scan (and, for float32 output, the
@@ -164,6 +165,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   const int ch = static_cast<int>(blockIdx.x % tiles_d) * 64 + lane;
   const bool ch_ok = ch < Dm;
   const int c = blockIdx.y;                         // sequence chunk
+  // States split over blocks: block z runs states n0 .. n0 + NS - 1 of its
+  // channels and writes the partial readout of those states to plane z.
+  const int n0 = static_cast<int>(blockIdx.z) * NS;
   const int t0 = c * p.chunk;
   const int len = min(p.L - t0, p.chunk);           // valid steps of this chunk
   const int nt = min(p.Lp - t0, p.chunk) / T;       // tiles (padded steps / T)
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   float iA[ZOH ? S : 1];                            // 1/A (0 where A = 0), ZOH only
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const int n = w * S + s;
+    const int n = n0 + w * S + s;
     const bool ok = ch_ok && n < N;
     const float av = ok ? p.A[static_cast<int64_t>(ch) * N + n] : 0.0f;
     A2[s] = av * kLog2e;
@@ -201,10 +205,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   const bool has_z = READOUT && p.z != nullptr;
   float dt_sum = 0.0f;
 
-  // LDS-staged B/C: thread element j of a tile is e = tid + j*NT of the
-  // tile's T*N contiguous entries of B (and of C), i.e. step e / N, state
-  // e % N. States N..NS-1 are never written: zero them once (no other
-  // writer touches them, so no ordering is needed beyond the first barrier).
+  // LDS-staged B/C: thread element j of a tile is entry e = tid + j*NT of
+  // the tile's T x NS (B, C) pairs, step e / NS, state n0 + e % NS, read
+  // from row e / NS of the [L, N] input (states at or beyond N read as 0).
   int bc_dst[EB];
   uint32_t bc_src[EB];
   if constexpr (BCL) {
@@ -212,14 +215,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
 #pragma unroll
     for (int j = 0; j < EB; ++j) {
       const int e = tid + j * NT;
-      const bool ok = e < T * N;
-      bc_dst[j] = ok ? (e / N) * NS + (e % N) : -1;
-      bc_src[j] = ok ? static_cast<uint32_t>(e) * IN_B : kLaneOut;
-    }
-    if (N < NS) {
-      for (int e = tid; e < 4 * T * NS; e += NT) {
-        if (e % NS >= N) (&sBC[0][0][0])[e] = make_float2(0.0f, 0.0f);
-      }
+      const int n = n0 + e % NS;
+      bc_dst[j] = e < T * NS ? e : -1;
+      bc_src[j] = (e < T * NS && n < N) ? static_cast<uint32_t>((e / NS) * N + n) * IN_B : kLaneOut;
     }
   }
 
@@ -231,7 +229,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   const rsrc_t rd_b = raw_buffer(static_cast<const char*>(p.delta) + pb * IN_B, elems * IN_B);
   const rsrc_t rz_b = raw_buffer(has_z ? static_cast<const char*>(p.z) + pb * IN_B : nullptr,
                                  has_z ? elems * IN_B : 0u);
-  const rsrc_t ry_b = raw_buffer(READOUT ? static_cast<char*>(p.y) + pb * OUT_B : nullptr,
+  const rsrc_t ry_b = raw_buffer(READOUT ? static_cast<char*>(p.y) + (pb + blockIdx.z * p.y_split) * OUT_B : nullptr,
                                  READOUT ? elems * OUT_B : 0u);
   const uint32_t lane_in = ch_ok ? static_cast<uint32_t>(ch) * IN_B : kLaneOut;
   const uint32_t lane_out = ch_ok ? static_cast<uint32_t>(ch) * OUT_B : kLaneOut;
@@ -634,7 +632,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     if (p.h_final && ch_ok && c == static_cast<int>(gridDim.y) - 1) {
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = w * S + s;
+        const int n = n0 + w * S + s;
         if (n < N) p.h_final[bdn + n] = h[s];
       }
     }
@@ -644,7 +642,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       const int64_t cb1 = cb + p.batch;              // slot c + 1
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = w * S + s;
+        const int n = n0 + w * S + s;
         if (n < N) p.hsum[(cb1 * Dm + ch) * N + n] = h[s];
       }
       if (w == 0) p.ssum[cb * Dm + ch] = dt_sum;
@@ -713,7 +711,8 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
   const void* full = pl.chunks > 1
                          ? reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, false>)
                          : reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, true>);
-  return hipLaunchKernel(full, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks)),
+  return hipLaunchKernel(full, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks),
+                                    static_cast<unsigned>(pl.splits)),
                          dim3(W * 64), kargs, 0, st);
 }
 

@@ -119,6 +119,34 @@ def test_workspace_query(lib):
         assert scan(lib, B=1, L=262144, d=2560, N=16, ws=1 << 40, wsb=need - 1) == E_WORKSPACE
 
 
+def test_workspace_alignment(lib):
+    assert scan(lib, ws=20 * P + 8) == E_ALIGN       # workspace must be 16-byte aligned
+    assert scan(lib, ws=20 * P + 16) != E_ALIGN
+
+
+def test_state_split_plan(lib):
+    """Single-pass scans with 65 to 128 padded states (N > 64) and 65 to 128
+    channel blocks split each channel's states over two blocks: the workspace
+    then holds two float32 partial-readout planes of [B, L, d]."""
+    ws = lib.ssm_scan_workspace_bytes
+    ch = lib.ssm_scan_chunks
+
+    def planes(B, L, d):
+        return 2 * (-(-B * L * d // 64) * 64) * 4
+
+    for B, L, d, N in [(2, 8192, 4096, 128), (1, 64, 4160, 128), (2, 40, 4096, 100), (1, 8192, 8192, 65)]:
+        assert ch(B, L, d, N) == 1
+        assert ws(B, L, d, N) >= planes(B, L, d), (B, L, d, N)
+    # no split: full device (256 blocks), 64 or fewer blocks (chunked in time,
+    # or too short to chunk), or at most 64 padded states
+    assert ws(4, 2048, 4096, 128) < planes(4, 2048, 4096)
+    assert ws(3, 2048, 4096, 128) < planes(3, 2048, 4096)                 # 192 blocks
+    assert ch(1, 8192, 4096, 128) > 1 and ws(1, 8192, 4096, 128) < planes(1, 8192, 4096)
+    assert ws(1, 64, 4096, 128) == 0
+    assert ws(2, 8192, 4096, 64) == 0
+    assert ws(2, 8192, 4096, 33) == 0
+
+
 def test_size_limits(lib):
     assert scan(lib, B=1, L=1 << 30, d=4) == E_UNSUPPORTED
     assert scan(lib, B=1, L=8, d=1 << 24) == E_UNSUPPORTED

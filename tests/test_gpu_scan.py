@@ -127,6 +127,66 @@ def test_large_state_chunked_by_plane_size():
     check_scan(f"large N chunked x{k} {(B, L, d, N)} bf16 sampled", inp, "f32", h0=h0, channels=ch)
 
 
+# 65 to 128 padded states at 65 to 128 channel blocks, single pass: each
+# channel's states run in two blocks of 64, whose float32 partial readouts a
+# combine pass adds (then the skip and the gate).
+STATE_SPLIT = [(1, 64, 4160, 128, "bf16"), (2, 40, 4096, 100, "f32"), (1, 33, 4100, 65, "bf16")]
+
+
+@pytest.mark.parametrize("B,L,d,N,dt", STATE_SPLIT)
+def test_state_split(B, L, d, N, dt):
+    assert binding.ssm_scan_chunks(B, L, d, N) == 1
+    assert binding.ssm_scan_workspace_bytes(B, L, d, N) >= 2 * B * L * d * 4
+    inp = synth.make_scan_inputs(B, L, d, N, dt, seed=6, stream=4700 + N)
+    h0 = np.random.default_rng(N + 7).standard_normal((B, d, N)).astype(np.float32) * 0.5
+    check_scan(f"state split {(B, L, d, N)} {dt}", inp, "f32", h0=h0)
+    check_scan(f"state split {(B, L, d, N)} {dt}", inp, "bf16")
+
+
+@pytest.mark.parametrize("opts", [dict(use_D=False), dict(use_z=False), dict(use_bias=False, softplus=False)])
+def test_state_split_optional_parts(opts):
+    inp = synth.make_scan_inputs(1, 48, 4160, 128, "f32", seed=7, stream=4800)
+    if opts.get("softplus") is False:
+        inp = dict(inp)
+        inp["delta"] = np.abs(inp["delta"]) * np.float32(0.05)   # positive raw steps
+    check_scan(f"state split options {opts}", inp, "f32", gpu_kwargs=opts)
+
+
+def test_state_split_in_place_deterministic_and_covering():
+    """h_final over h0 in place, bitwise repeatable, every output written
+    and nothing else (NaN guards around y), on a split plan."""
+    B, L, d, N = 1, 40, 4150, 128
+    assert binding.ssm_scan_workspace_bytes(B, L, d, N) >= 2 * B * L * d * 4
+    inp = synth.make_scan_inputs(B, L, d, N, "bf16", seed=8, stream=4900)
+    dev = scan_inputs_to_device(inp)
+    h0 = np.random.default_rng(49).standard_normal((B, d, N)).astype(np.float32) * 0.5
+    kw = dict(D=dev["D"], z=dev["z"], delta_bias=dev["delta_bias"], delta_softplus=True)
+    y1, h1 = binding.ssm_selective_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"],
+                                            h0=upload(h0, "f32"), return_final_state=True,
+                                            out_dtype=torch.float32, **kw)
+    guard = torch.full((B * L * d + 2048,), float("nan"), dtype=torch.float32, device="cuda")
+    y2 = guard[1024:1024 + B * L * d].view(B, L, d)
+    hs = upload(h0, "f32")
+    binding.ssm_selective_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], h0=hs, y=y2,
+                                   h_final=hs, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    print("[parity] state split: in place, repeat, guards", flush=True)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    assert torch.equal(h1.view(torch.int32), hs.view(torch.int32))
+    assert torch.isnan(guard[:1024]).all() and torch.isnan(guard[1024 + B * L * d:]).all()
+    assert not torch.isnan(y2).any()
+
+
+def test_state_split_full_size_sampled():
+    """(2, 8192, 4096, 128) bf16: 128 channel blocks, two blocks per channel."""
+    B, L, d, N = 2, 8192, 4096, 128
+    assert binding.ssm_scan_workspace_bytes(B, L, d, N) >= 2 * B * L * d * 4
+    inp = synth.make_scan_inputs(B, L, d, N, "bf16", seed=9, stream=5000)
+    ch = np.r_[0, 1, 63, 64, 2047, 4094, 4095]
+    h0 = np.random.default_rng(50).standard_normal((B, d, N)).astype(np.float32) * 0.5
+    check_scan(f"state split full size {(B, L, d, N)} bf16 sampled", inp, "bf16", h0=h0, channels=ch)
+
+
 @pytest.mark.parametrize("opts", [
     dict(use_D=False), dict(use_z=False), dict(use_bias=False), dict(softplus=False, use_bias=False),
     dict(use_D=False, use_z=False, use_bias=False),

@@ -54,6 +54,37 @@ def test_noalloc_two_calls_second_smaller():
     run_both(small, "second call (smaller, single pass)", False)
 
 
+def test_noalloc_state_split_plans():
+    """A scan whose states the plan splits over two blocks: bitwise equal to
+    the forward with a workspace where the partial planes fit the scratch
+    array; with one block per channel (equal to rounding) where they do not."""
+    small = synth.make_scan_inputs(1, 64, 4160, 128, "bf16", seed=3, stream=932)
+    assert binding.ssm_scan_workspace_bytes(1, 64, 4160, 128) <= 64 << 20
+    run_both(small, "state split within the scratch array", False)
+    B, L, d, N = 2, 8192, 4096, 128
+    assert binding.ssm_scan_workspace_bytes(B, L, d, N) > 64 << 20
+    inp = synth.make_scan_inputs(B, L, d, N, "bf16", seed=4, stream=933)
+    dev = scan_inputs_to_device(inp)
+    kw = dict(D=dev["D"], z=dev["z"], delta_bias=dev["delta_bias"], delta_softplus=True)
+    y_ref, h_ref = binding.ssm_selective_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"],
+                                                  out_dtype=torch.float32, return_final_state=True, **kw)
+    y = torch.empty_like(y_ref)
+    h = torch.empty_like(h_ref)
+    binding.ssm_selective_scan_fwd_noalloc(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], y, h_final=h,
+                                           **kw)
+    torch.cuda.synchronize()
+    ch = np.r_[0, 63, 64, 4095]
+    ref, href, ymag, hmag = oracle_scan(inp, channels=ch)
+    tol = tol_for("bf16", "f32")
+    ey = oracle.scaled_error(download(y)[:, :, ch], ref, ymag)
+    eh = oracle.scaled_error(download(h)[:, ch], href, hmag)
+    ea = oracle.scaled_error(download(y), download(y_ref), np.abs(download(y_ref)) + 1.0)
+    print(f"[noalloc] state split too large for the scratch: y err {ey:.2e}, h err {eh:.2e}, "
+          f"vs workspace entry {ea:.2e}", flush=True)
+    assert ey <= tol and eh <= tol and ea <= tol
+    assert torch.equal(h.view(torch.int32), h_ref.view(torch.int32))
+
+
 def test_noalloc_refuses_oversized_workspace():
     limit = 64 << 20
     L = (limit // (2 * 16 * 4)) + 64
