@@ -95,9 +95,10 @@ const char* ssm_status_string(int status);
  * operator (A_i, b_i) (+) (A_j, b_j) = (A_j A_i, A_j b_i + b_j) of
  * "Mamba的隐藏代价" (kongchang.com), section on sequential gradients, and the
  * chunked processing with a carried state of intelliparadigm.com section 6.2.
- * With 65 to 128 padded states (N > 64) and 65 to 128 blocks of 64 channels
- * (B * ceil(d / 64)) in a single pass, each channel's states are split over
- * two blocks of 64 so that the device fills; the workspace then also holds
+ * With N > 32 (padded to 64 or 128 states) and 65 to 128 blocks of 64
+ * channels (B * ceil(d / 64)) in a single pass, each channel's states are
+ * split over two blocks of half the padded states, so that the device fills;
+ * the workspace then also holds
  * the two float32 partial readouts sum_n C h over each half of the states,
  * [2][B, L, d] (rounded up), which a combine pass adds in that order before
  * the skip and the gate. It depends only on the four sizes. Returns 0 for

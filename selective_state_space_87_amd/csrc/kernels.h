@@ -113,9 +113,9 @@ constexpr int64_t kSsdMaxState = 128;
 // the B/C pre-pass: per-chunk summaries (local final state from zero, and the
 // sum of the step sizes), an in-order fold of the summaries into each chunk's
 // incoming state, and the full scan of every chunk from that state.
-// With 128 padded states and too few channel blocks for the device but too
-// many for time chunks to pay, a single-pass scan instead splits every
-// channel's states over `splits` = 2 blocks of 64 states each: each writes
+// With 64 or 128 padded states and too few channel blocks for the device but
+// too many for time chunks to pay, a single-pass scan instead splits every
+// channel's states over `splits` = 2 blocks of half the states each: each writes
 // the float32 partial readout of its states, sum_n C h, to a plane of the
 // workspace (`part_plane` elements apart), and a combine pass forms
 // y = (part_0 + part_1 + D u) silu(z) in that fixed order.
@@ -149,7 +149,7 @@ constexpr int64_t kChunkWhenBlocksAtMost = 128;
 // (2, 8192, 4096, 128), splitting lost (3356 -> 3500 us at 512 slots).
 constexpr int64_t kBlockSlotsLarge = 256;
 constexpr int64_t kChunkLargeWhenBlocksAtMost = 64;
-// 128 padded states at 65 to 128 channel blocks: two blocks per channel.
+// 64 or 128 padded states at 65 to 128 channel blocks: two blocks per channel.
 constexpr int64_t kSplitWhenBlocksAtMost = 128;
 
 // allow_split = false keeps every channel in one block (no partial planes in

@@ -60,11 +60,12 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, b
     p.chunk = round_up(ceil_div(p.Lp, k), kPadSteps);
     if (p.chunk > steps_max) p.chunk = steps_max;
     p.chunks = ceil_div(p.Lp, p.chunk);
-    // Two blocks of 64 states per channel where one block per channel would
-    // leave at least half of the device idle and the sequence is not split
-    // in time. The partial readouts cross HBM once in float32 (written, then
-    // read by the combine pass), small beside 128 state updates per element.
-    if (allow_split && p.NS == 128 && p.chunks == 1 && blocks > kChunkLargeWhenBlocksAtMost &&
+    // Two blocks of half the padded states per channel where one block per
+    // channel would leave at least half of the device idle and the sequence
+    // is not split in time. The partial readouts cross HBM once in float32
+    // (written, then read by the combine pass), small beside 64 or 128 state
+    // updates per element.
+    if (allow_split && p.NS >= 64 && p.chunks == 1 && blocks > kChunkLargeWhenBlocksAtMost &&
         blocks <= kSplitWhenBlocksAtMost) {
       p.splits = 2;
       p.part_plane = round_up(batch * seqlen * dim, 64);

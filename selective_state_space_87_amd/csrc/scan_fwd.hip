@@ -157,9 +157,9 @@ int launch_scan(const ScanArgs& a, void* stream) {
   s.batch = static_cast<int>(a.batch);
   s.y_split = 0;
   if (pl.splits > 1) {
-    // Each block runs 64 of the 128 padded states of its channels and writes
-    // their partial readout (float32, no skip, no gate) to its plane; the
-    // combine pass then forms y.
+    // Each block runs half of the padded states of its channels (64 of 128,
+    // or 32 of 64) and writes their partial readout (float32, no skip, no
+    // gate) to its plane; the combine pass then forms y.
     float* part = reinterpret_cast<float*>(ws + pl.off_part);
     Scan sh = s;
     sh.y = part;

@@ -12,7 +12,10 @@
 // is channel d0+l, and wave w owns states n = w*S .. w*S+S-1, kept in VGPRs
 // for the whole chunk; every state chain is walked once, in order. Padded N
 // up to 8 runs one state per wave; 16 two states per lane on eight waves; 32
-// two on sixteen; 64 and 128 run N/8 per lane on eight waves.
+// two on sixteen; 64 and 128 run N/8 per lane on eight waves. Where a plan
+// splits a channel's states over two blocks (blockIdx.z), each runs half of
+// them (32 states: four per lane, B/C through LDS) and writes its partial
+// readout, without skip and gate, to a plane of its own.
 //
 // Time is processed in tiles of T steps (8 at N = 16). Per tile:
 //   * recurrence: each wave advances its states through the tile. B[t, n] and
@@ -111,7 +114,8 @@ constexpr bool bc_in_lds(int NS) { return NS >= 64; }
 // (for the backward pass, which recomputes each tile from them).
 constexpr int kFull = 0, kSummary = 1, kCheckpoint = 2;
 
-template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool ZOH, int MODE, bool PAIR = true>
+template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool ZOH, int MODE, bool PAIR = true,
+          bool FORCE_BCL = false>
 __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int NS = S * W;        // padded state count
   // Cooperative items per thread per tile: step w + W*i of the tile. With
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr uint32_t IN_B = BF16_IN ? 2 : 4, OUT_B = BF16_OUT ? 2 : 4;
   constexpr bool READOUT = MODE == kFull;
   constexpr bool SUMMARY = MODE == kSummary;
-  constexpr bool BCL = bc_in_lds(NS);
+  constexpr bool BCL = FORCE_BCL || bc_in_lds(NS);  // forced for the 32-state halves of a split 64
   constexpr int NT = W * 64;                        // threads
   constexpr int EB = BCL ? (T * NS + NT - 1) / NT : 1;  // B/C elements per thread per tile
   // Pair barriers (eight waves of 8-step tiles, scalar B/C): one barrier
@@ -679,7 +683,7 @@ __global__ __launch_bounds__(256) void carry_fold_kernel(const float* __restrict
   }
 }
 
-template <int S, int W, int T, bool BI, bool BO, bool SP, bool ZH>
+template <int S, int W, int T, bool BI, bool BO, bool SP, bool ZH, bool FBCL = false>
 int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t st) {
   static_assert(kPadSteps % T == 0, "tile must divide the padding");
   const int64_t blocks = a.batch * pl.dim_blocks;
@@ -709,8 +713,8 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
     if (err != 0) return err;
   }
   const void* full = pl.chunks > 1
-                         ? reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, false>)
-                         : reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, true>);
+                         ? reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, false, FBCL>)
+                         : reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, true, FBCL>);
   return hipLaunchKernel(full, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks),
                                     static_cast<unsigned>(pl.splits)),
                          dim3(W * 64), kargs, 0, st);
@@ -728,7 +732,14 @@ int launch_ns(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
     case 4: return launch_sw<1, 4, 16, BI, BO, SP, ZH>(a, pl, s, st);
     case 8: return launch_sw<1, 8, 16, BI, BO, SP, ZH>(a, pl, s, st);
     case 16: return launch_sw<2, 8, 8, BI, BO, SP, ZH>(a, pl, s, st);
-    case 32: return launch_sw<2, 16, 16, BI, BO, SP, ZH>(a, pl, s, st);
+    case 32:
+      // the 32-state halves of a split 64-state plan (float32 partials): four
+      // states per lane on eight waves, B/C through LDS like the whole
+      if constexpr (!BO) {
+        if (pl.splits > 1) return launch_sw<4, 8, 8, BI, BO, SP, ZH, true>(a, pl, s, st);
+      }
+      if (pl.splits > 1) return hipErrorInvalidValue;
+      return launch_sw<2, 16, 16, BI, BO, SP, ZH>(a, pl, s, st);
     case 64: return launch_sw<8, 8, 8, BI, BO, SP, ZH>(a, pl, s, st);   // B/C through LDS
     case 128: return launch_sw<16, 8, 8, BI, BO, SP, ZH>(a, pl, s, st);  // B/C through LDS
     default: return hipErrorInvalidValue;

@@ -125,7 +125,7 @@ def test_workspace_alignment(lib):
 
 
 def test_state_split_plan(lib):
-    """Single-pass scans with 65 to 128 padded states (N > 64) and 65 to 128
+    """Single-pass scans with N > 32 (64 or 128 padded states) and 65 to 128
     channel blocks split each channel's states over two blocks: the workspace
     then holds two float32 partial-readout planes of [B, L, d]."""
     ws = lib.ssm_scan_workspace_bytes
@@ -134,17 +134,18 @@ def test_state_split_plan(lib):
     def planes(B, L, d):
         return 2 * (-(-B * L * d // 64) * 64) * 4
 
-    for B, L, d, N in [(2, 8192, 4096, 128), (1, 64, 4160, 128), (2, 40, 4096, 100), (1, 8192, 8192, 65)]:
+    for B, L, d, N in [(2, 8192, 4096, 128), (1, 64, 4160, 128), (2, 40, 4096, 100), (1, 8192, 8192, 65),
+                       (2, 8192, 4096, 64), (2, 8192, 4096, 33)]:
         assert ch(B, L, d, N) == 1
         assert ws(B, L, d, N) >= planes(B, L, d), (B, L, d, N)
     # no split: full device (256 blocks), 64 or fewer blocks (chunked in time,
-    # or too short to chunk), or at most 64 padded states
+    # or too short to chunk), or at most 32 states
     assert ws(4, 2048, 4096, 128) < planes(4, 2048, 4096)
     assert ws(3, 2048, 4096, 128) < planes(3, 2048, 4096)                 # 192 blocks
     assert ch(1, 8192, 4096, 128) > 1 and ws(1, 8192, 4096, 128) < planes(1, 8192, 4096)
     assert ws(1, 64, 4096, 128) == 0
-    assert ws(2, 8192, 4096, 64) == 0
-    assert ws(2, 8192, 4096, 33) == 0
+    assert ws(4, 8192, 4096, 64) == 0
+    assert ws(2, 8192, 4096, 32) < planes(2, 8192, 4096)
 
 
 def test_size_limits(lib):

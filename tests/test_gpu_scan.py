@@ -127,10 +127,11 @@ def test_large_state_chunked_by_plane_size():
     check_scan(f"large N chunked x{k} {(B, L, d, N)} bf16 sampled", inp, "f32", h0=h0, channels=ch)
 
 
-# 65 to 128 padded states at 65 to 128 channel blocks, single pass: each
-# channel's states run in two blocks of 64, whose float32 partial readouts a
-# combine pass adds (then the skip and the gate).
-STATE_SPLIT = [(1, 64, 4160, 128, "bf16"), (2, 40, 4096, 100, "f32"), (1, 33, 4100, 65, "bf16")]
+# N > 32 (64 or 128 padded states) at 65 to 128 channel blocks, single pass:
+# each channel's states run in two blocks of half of them, whose float32
+# partial readouts a combine pass adds (then the skip and the gate).
+STATE_SPLIT = [(1, 64, 4160, 128, "bf16"), (2, 40, 4096, 100, "f32"), (1, 33, 4100, 65, "bf16"),
+               (1, 70, 4160, 64, "f32"), (2, 35, 4000, 40, "bf16")]
 
 
 @pytest.mark.parametrize("B,L,d,N,dt", STATE_SPLIT)

@@ -50,6 +50,8 @@ SHAPES = [
     (1, 1, 1, 1, "f32"), (2, 67, 70, 16, "f32"), (1, 129, 130, 3, "bf16"), (3, 40, 64, 5, "f32"),
     (2, 100, 33, 64, "bf16"), (1, 64, 256, 8, "f32"), (2, 130, 300, 12, "f32"), (1, 150, 70, 32, "f32"),
     (1, 70, 96, 128, "f32"), (2, 50, 64, 100, "bf16"),
+    # states split over two blocks per channel (65 to 128 channel blocks)
+    (1, 40, 4160, 128, "bf16"), (2, 30, 4096, 64, "f32"),
 ]
 
 
