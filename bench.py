@@ -415,6 +415,8 @@ def bench_conv(args, torch, binding, synth):
            "roofline": hbm_roofline(alg, us, counter_traffic("conv1d_mamba14b_counters.md",
                                                              kernel_source_hash("conv")))}
     del x, y
+    if args.no_conv_update:
+        return fwd, None
     Bd = 128
     ui = synth.make_conv_inputs(Bd, 1, d, K, "f32", seed=0, stream=701)
     xs = torch.from_numpy(ui["x"][:, 0]).to(dev)
@@ -745,6 +747,7 @@ def main():
     ap.add_argument("--large-state-steps", type=int, default=20)
     ap.add_argument("--zoh-steps", type=int, default=50)
     ap.add_argument("--conv-steps", type=int, default=50)
+    ap.add_argument("--no-conv-update", action="store_true", help="time the conv1d but not its decode update")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=8192)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

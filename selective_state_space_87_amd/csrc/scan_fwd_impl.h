@@ -207,6 +207,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   const float Dv = __builtin_fmaf((ch_ok && p.D) ? p.D[ch] : 0.0f, 1.0f, 0.0f);
   const float bv = __builtin_fmaf((ch_ok && p.bias) ? p.bias[ch] : 0.0f, 1.0f, 0.0f);
   const bool has_z = READOUT && p.z != nullptr;
+  // Without z the gate is 1: the gate is formed as fma(z, sigmoid(z), g_off)
+  // with g_off = 1 and z read as 0 (its descriptor is empty), else g_off = 0.
+  const float g_off = has_z ? 0.0f : 1.0f;
   float dt_sum = 0.0f;
 
   // LDS-staged B/C: thread element j of a tile is entry e = tid + j*NT of
@@ -302,9 +305,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       float dt = SOFTPLUS ? softplus_f(x) : x;
       dt = t_ok ? dt : 0.0f;
       if constexpr (READOUT) {
-        const float g = silu_f(bits_to_f32<BF16_IN>(rz[R][i]));
+        const float zv = bits_to_f32<BF16_IN>(rz[R][i]);
         eDu[SL][i] = Dv * uv;
-        eG[SL][i] = has_z ? g : 1.0f;
+        eG[SL][i] = fmaf(zv, rcp_hw(1.0f + exp2_hw(-zv * kLog2e)), g_off);  // silu(z), or 1
       }
       if (has_item) sDD[SL][tt < T ? tt : 0][lane] = make_float2(dt, ZOH ? uv : dt * uv);
     }
