@@ -99,9 +99,9 @@ const char* ssm_status_string(int status);
  * channels (B * ceil(d / 64)) in a single pass, each channel's states are
  * split over two blocks of half the padded states, so that the device fills;
  * the workspace then also holds
- * the two float32 partial readouts sum_n C h over each half of the states,
- * [2][B, L, d] (rounded up), which a combine pass adds in that order before
- * the skip and the gate. It depends only on the four sizes. Returns 0 for
+ * the two float32 partial readouts sum_n C h over each half of the states
+ * (the first with the skip D u), [2][B, L, d] (rounded up), which a combine
+ * pass adds before the gate. It depends only on the four sizes. Returns 0 for
  * invalid or unsupported sizes, and for batch, dim or seqlen 0.
  */
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);

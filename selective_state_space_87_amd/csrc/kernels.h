@@ -116,9 +116,9 @@ constexpr int64_t kSsdMaxState = 128;
 // With 64 or 128 padded states and too few channel blocks for the device but
 // too many for time chunks to pay, a single-pass scan instead splits every
 // channel's states over `splits` = 2 blocks of half the states each: each writes
-// the float32 partial readout of its states, sum_n C h, to a plane of the
-// workspace (`part_plane` elements apart), and a combine pass forms
-// y = (part_0 + part_1 + D u) silu(z) in that fixed order.
+// the float32 partial readout of its states, sum_n C h (the first block's
+// plus D u), to a plane of the workspace (`part_plane` elements apart), and
+// a combine pass forms y = (part_0 + part_1) silu(z).
 // Pure function of the sizes (not of the device or the dtypes).
 struct ScanPlan {
   bool ok;                 // false: sizes beyond what the kernels address

@@ -12,67 +12,51 @@ int scan_tile_steps(int NS) { return bwd_tile_steps(NS); }
 namespace {
 
 // Combine pass of a scan whose channels' states are split over two blocks:
-// y = (part_0 + part_1 + D u) * silu(z), in that order, over the flattened
-// [B, L, d] elements, four consecutive elements per thread (16-byte partial
-// loads; u, z and y move as 8- or 16-byte runs). HBM-bound.
+// y = (part_0 + part_1) * silu(z) (part_0 holds the skip D u), over the
+// flattened [B, L, d] elements, four consecutive elements per thread
+// (16-byte partial loads; z and y move as 8- or 16-byte runs). HBM-bound.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
 template <bool BI, bool BO>
 __global__ __launch_bounds__(256) void scan_split_combine_kernel(const float* __restrict__ part, int64_t plane,
-                                                                 const void* __restrict__ u,
-                                                                 const void* __restrict__ z,
-                                                                 const float* __restrict__ D, void* __restrict__ y,
-                                                                 int64_t total, int dim) {
+                                                                 const void* __restrict__ z, void* __restrict__ y,
+                                                                 int64_t total) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256 * 4;
   for (int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4; i0 < total; i0 += stride) {
-    int ch = static_cast<int>(i0 % dim);
-    float v[4];
     if (i0 + 4 <= total) {
-      const float4 p0 = *reinterpret_cast<const float4*>(part + i0);
-      const float4 p1 = *reinterpret_cast<const float4*>(part + plane + i0);
-      float uv[4], zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (BI) {
-        const uint2 ub = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(u) + i0);
-        uv[0] = __uint_as_float(ub.x << 16);
-        uv[1] = __uint_as_float(ub.x & 0xffff0000u);
-        uv[2] = __uint_as_float(ub.y << 16);
-        uv[3] = __uint_as_float(ub.y & 0xffff0000u);
-        if (z) {
-          const uint2 zb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(z) + i0);
+      const f32x4v p0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(part + i0));
+      const f32x4v p1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(part + plane + i0));
+      float v[4] = {p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w};
+      if (z) {
+        float zv[4];
+        if constexpr (BI) {
+          const u32x2v zb = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(static_cast<const uint16_t*>(z) + i0));
           zv[0] = __uint_as_float(zb.x << 16);
           zv[1] = __uint_as_float(zb.x & 0xffff0000u);
           zv[2] = __uint_as_float(zb.y << 16);
           zv[3] = __uint_as_float(zb.y & 0xffff0000u);
-        }
-      } else {
-        const float4 uf = *reinterpret_cast<const float4*>(static_cast<const float*>(u) + i0);
-        uv[0] = uf.x, uv[1] = uf.y, uv[2] = uf.z, uv[3] = uf.w;
-        if (z) {
-          const float4 zf = *reinterpret_cast<const float4*>(static_cast<const float*>(z) + i0);
+        } else {
+          const f32x4v zf = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(static_cast<const float*>(z) + i0));
           zv[0] = zf.x, zv[1] = zf.y, zv[2] = zf.z, zv[3] = zf.w;
         }
-      }
-      const float pa[4] = {p0.x, p0.y, p0.z, p0.w}, pc[4] = {p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float dv = D ? D[ch] : 0.0f;
-        v[j] = ((pa[j] + pc[j]) + dv * uv[j]) * (z ? silu_f(zv[j]) : 1.0f);
-        ch = ch + 1 == dim ? 0 : ch + 1;
+        for (int j = 0; j < 4; ++j) v[j] *= silu_f(zv[j]);
       }
       if constexpr (BO) {
-        const uint2 o = {static_cast<uint32_t>(f32_to_bf16_bits(v[0])) |
-                             (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16),
-                         static_cast<uint32_t>(f32_to_bf16_bits(v[2])) |
-                             (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16)};
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + i0) = o;
+        const u32x2v o = {static_cast<uint32_t>(f32_to_bf16_bits(v[0])) |
+                              (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16),
+                          static_cast<uint32_t>(f32_to_bf16_bits(v[2])) |
+                              (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16)};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2v*>(static_cast<uint16_t*>(y) + i0));
       } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(y) + i0) = make_float4(v[0], v[1], v[2], v[3]);
+        const f32x4v o = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4v*>(static_cast<float*>(y) + i0));
       }
     } else {
       for (int64_t i = i0; i < total; ++i) {
-        const float uv = load_elem<BI>(u, i);
-        const float dv = D ? D[ch] : 0.0f;
-        const float out = ((part[i] + part[plane + i]) + dv * uv) * (z ? silu_f(load_elem<BI>(z, i)) : 1.0f);
+        const float out = (part[i] + part[plane + i]) * (z ? silu_f(load_elem<BI>(z, i)) : 1.0f);
         store_elem<BO>(y, i, out);
-        ch = ch + 1 == dim ? 0 : ch + 1;
       }
     }
   }
@@ -85,13 +69,9 @@ int launch_split_combine(const ScanArgs& a, const ScanPlan& pl, const float* par
   const int64_t groups = (total + 3) / 4;
   const int64_t grid = groups < 256 * 2048 ? (groups + 255) / 256 : 2048;
   const int64_t plane = pl.part_plane;
-  const void* u = a.u;
   const void* z = a.z;
-  const float* D = a.D;
   void* y = a.y;
-  int dim = static_cast<int>(a.dim);
-  void* kargs[] = {const_cast<float**>(&part), const_cast<int64_t*>(&plane), &u, &z, &D, &y,
-                   const_cast<int64_t*>(&total), &dim};
+  void* kargs[] = {const_cast<float**>(&part), const_cast<int64_t*>(&plane), &z, &y, const_cast<int64_t*>(&total)};
   return hipLaunchKernel(reinterpret_cast<const void*>(&scan_split_combine_kernel<BI, BO>),
                          dim3(static_cast<unsigned>(grid)), dim3(256), kargs, 0, st);
 }
@@ -158,13 +138,13 @@ int launch_scan(const ScanArgs& a, void* stream) {
   s.y_split = 0;
   if (pl.splits > 1) {
     // Each block runs half of the padded states of its channels (64 of 128,
-    // or 32 of 64) and writes their partial readout (float32, no skip, no
-    // gate) to its plane; the combine pass then forms y.
+    // or 32 of 64) and writes their partial readout (float32, without the
+    // gate; the first block's with the skip D u) to its plane; the combine
+    // pass then forms y.
     float* part = reinterpret_cast<float*>(ws + pl.off_part);
     Scan sh = s;
     sh.y = part;
     sh.y_split = pl.part_plane;
-    sh.D = nullptr;
     sh.z = nullptr;
     ScanPlan ph = pl;
     ph.NS = pl.NS / pl.splits;

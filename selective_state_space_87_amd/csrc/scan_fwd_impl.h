@@ -15,7 +15,8 @@
 // two on sixteen; 64 and 128 run N/8 per lane on eight waves. Where a plan
 // splits a channel's states over two blocks (blockIdx.z), each runs half of
 // them (32 states: four per lane, B/C through LDS) and writes its partial
-// readout, without skip and gate, to a plane of its own.
+// readout, without the gate (the first block's with the skip D u), to a
+// plane of its own.
 //
 // Time is processed in tiles of T steps (8 at N = 16). Per tile:
 //   * recurrence: each wave advances its states through the tile. B[t, n] and
@@ -204,7 +205,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     h[s] = __builtin_fmaf((ok && hinit) ? hinit[bdn + n] : 0.0f, 1.0f, 0.0f);
   }
   // Same ALU pass-through for the per-channel constants.
-  const float Dv = __builtin_fmaf((ch_ok && p.D) ? p.D[ch] : 0.0f, 1.0f, 0.0f);
+  // (with states split over blocks, the skip D u enters the first block's
+  // partial readout only)
+  const float Dv = __builtin_fmaf((ch_ok && p.D && blockIdx.z == 0) ? p.D[ch] : 0.0f, 1.0f, 0.0f);
   const float bv = __builtin_fmaf((ch_ok && p.bias) ? p.bias[ch] : 0.0f, 1.0f, 0.0f);
   const bool has_z = READOUT && p.z != nullptr;
   // Without z the gate is 1: the gate is formed as fma(z, sigmoid(z), g_off)
