@@ -635,11 +635,37 @@ def bench_bwd(args, torch, binding, synth, inp):
     ups = w.updates
     slots = ups * BWD_SLOTS_PER_UPDATE + w.batch * w.seqlen * w.dim * BWD_SLOTS_PER_BLD
     ach = slots / (us * 1e-6) / 1e12
-    return {"workload": f"{w.name} backward (dy float32, all gradients float32)", "us_per_call": us,
-            "G_updates_per_s": ups / (us * 1e-6) / 1e9,
-            "roofline": {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_SLOTS / 1e12, "unit": "Tslot/s",
-                         "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots,
-                         "valu_counters": valu_counters("scan_bwd_mamba14b_valu.md", kernel_source_hash("bwd"))}}
+    out = {"workload": f"{w.name} backward (dy float32, all gradients float32)", "us_per_call": us,
+           "G_updates_per_s": ups / (us * 1e-6) / 1e9,
+           "roofline": {"bound": "alu", "achieved": ach, "peak": VALU_PEAK_SLOTS / 1e12, "unit": "Tslot/s",
+                        "frac": ach / (VALU_PEAK_SLOTS / 1e12), "traffic": None, "alg_slots_per_launch": slots,
+                        "valu_counters": valu_counters("scan_bwd_mamba14b_valu.md", kernel_source_hash("bwd"))}}
+    # A training step that keeps the forward's states: the forward writes the
+    # backward's checkpoints, the backward takes them (no recurrence pass of
+    # its own). Timed beside the plain forward (bf16 y, as the headline).
+    ck = torch.empty(binding.ssm_scan_checkpoint_bytes(w.batch, w.seqlen, w.dim, w.dstate) // 4,
+                     dtype=torch.float32, device=dev)
+    y = torch.empty(w.batch, w.seqlen, w.dim, dtype=t["u"].dtype, device=dev)
+    hf = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
+    fws = torch.empty(max(binding.ssm_scan_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate), 1),
+                      dtype=torch.uint8, device=dev)
+    fkw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True, y=y, h_final=hf,
+               workspace=fws)
+    f_plain = lambda: binding.ssm_selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], **fkw)  # noqa
+    f_ckpt = lambda: binding.ssm_selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"],  # noqa
+                                                    checkpoints=ck, **fkw)
+    b_ckpt = lambda: binding.ssm_selective_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy,  # noqa
+                                                    D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                                                    delta_softplus=True, workspace=ws, checkpoints=ck)
+    us_fp = _timed(torch, f_plain, args.bwd_steps, 2)
+    us_fc = _timed(torch, f_ckpt, args.bwd_steps, 2)
+    us_bc = _timed(torch, b_ckpt, args.bwd_steps, 2)
+    out["with_forward_checkpoints"] = {
+        "forward_us": us_fp, "forward_writing_checkpoints_us": us_fc, "backward_from_checkpoints_us": us_bc,
+        "checkpoint_bytes": ck.numel() * 4,
+        "training_step_us": {"recomputing": us_fp + us, "keeping_checkpoints": us_fc + us_bc},
+        "backward_roofline": alu_roofline(slots, us_bc)}
+    return out
 
 
 def alu_roofline(slots, us):

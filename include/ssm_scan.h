@@ -261,6 +261,51 @@ int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * A training step that keeps the forward's states instead of recomputing
+ * them ("Mamba的隐藏代价" (kongchang.com), section on the optimisation
+ * problems of sequential gradients, names storing or recomputing each step's
+ * local terms as the two options). For 1 <= N <= 16 only.
+ *
+ * ssm_scan_checkpoint_bytes: bytes of the checkpoints, the states at every
+ * tile start of the backward, [B][Lp/T][N'][d] float32 (N' = N rounded up to
+ * a power of two, Lp = L rounded up to 16, T = 16 steps for N' <= 8 and 8
+ * for N' = 16). Returns 0 for sizes the backward does not run or N > 16.
+ *
+ * ssm_selective_scan_fwd_ckpt: ssm_selective_scan_fwd (same arguments, rules
+ * and results, bitwise) that also writes the checkpoints (caller-owned,
+ * ssm_scan_checkpoint_bytes() bytes, 4-byte aligned, overlapping no input,
+ * output or the workspace; may be NULL only for L = 0). A single-pass scan
+ * writes them from its own recurrence; where the sequence runs in chunks
+ * (ssm_scan_chunks() > 1) they are computed by a recurrence pass before the
+ * scan. N > 16, or sizes ssm_selective_scan_bwd does not run, give
+ * SSM_E_UNSUPPORTED.
+ *
+ * ssm_selective_scan_bwd_ckpt: ssm_selective_scan_bwd (same arguments, rules
+ * and results, bitwise, and the same workspace) with the states taken from
+ * the checkpoints that ssm_selective_scan_fwd_ckpt wrote for the same inputs
+ * and h0, instead of a recurrence pass of its own. The checkpoints are an
+ * input: no output may overlap them.
+ */
+size_t ssm_scan_checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+int ssm_selective_scan_fwd_ckpt(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                int in_dtype, int out_dtype, int flags,
+                                const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, const float* h0,
+                                void* y, float* h_final, float* checkpoints,
+                                void* workspace, size_t workspace_bytes, void* stream);
+int ssm_selective_scan_bwd_ckpt(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                int in_dtype, int flags,
+                                const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, const float* h0,
+                                const float* dy, const float* dh_final,
+                                float* du, float* ddelta, float* dA, float* dB, float* dC,
+                                float* dD, float* dz, float* ddelta_bias, float* dh0,
+                                const float* checkpoints,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Causal depthwise conv1d (+ SiLU) over a sequence: the short local
  * convolution that precedes the selective scan in the block ("从 Transformer
  * 到 Mamba", ybb.press, section 5: depthwise Conv1d of width d_conv padded by

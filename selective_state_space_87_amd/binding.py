@@ -73,6 +73,12 @@ def _load():
         lib.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
         lib.ssm_selective_scan_bwd.restype = i32
         lib.ssm_selective_scan_bwd.argtypes = [i64, i64, i64, i64, i32, i32] + [vp] * 21 + [sz, vp]
+        lib.ssm_scan_checkpoint_bytes.restype = sz
+        lib.ssm_scan_checkpoint_bytes.argtypes = [i64, i64, i64, i64]
+        lib.ssm_selective_scan_fwd_ckpt.restype = i32
+        lib.ssm_selective_scan_fwd_ckpt.argtypes = [i64, i64, i64, i64, i32, i32, i32] + [vp] * 13 + [sz, vp]
+        lib.ssm_selective_scan_bwd_ckpt.restype = i32
+        lib.ssm_selective_scan_bwd_ckpt.argtypes = [i64, i64, i64, i64, i32, i32] + [vp] * 22 + [sz, vp]
         lib.ssm_causal_conv1d_fwd.restype = i32
         lib.ssm_causal_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32, i32, i32,
                                               vp, vp, vp, vp, vp, vp, vp]
@@ -168,13 +174,17 @@ def ssm_scan_chunks(batch, seqlen, dim, dstate) -> int:
 def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                            delta_softplus=False, h0=None, out_dtype=None,
                            return_final_state=False, y=None, h_final=None,
-                           workspace=None, stream=None, zoh=False):
+                           workspace=None, stream=None, zoh=False, checkpoints=None):
     """Selective scan forward; see ssm_selective_scan_fwd in include/ssm_scan.h.
 
     u, delta, z: [B, L, d]; B, C: [B, L, N] (all float32 or all bfloat16);
     A: [d, N], D, delta_bias: [d], h0: [B, d, N] (float32).
     ``zoh`` selects the exact zero-order-hold input coefficient (SSM_FLAG_ZOH).
-    Returns y ([B, L, d], ``out_dtype`` or the input dtype) or (y, h_final).
+    ``checkpoints``: a float32 tensor of ssm_scan_checkpoint_bytes() bytes, or
+    True to allocate one: calls ssm_selective_scan_fwd_ckpt, which also writes
+    the backward's state checkpoints there (N <= 16).
+    Returns y ([B, L, d], ``out_dtype`` or the input dtype) or (y, h_final);
+    with checkpoints, (y, h_final, checkpoints).
     """
     lib = _load()
     if not isinstance(u, torch.Tensor) or u.dim() != 3:
@@ -210,11 +220,24 @@ def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         if workspace is None and ws_bytes > 0:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         ws_size = _check_workspace(workspace, dev)
-        st = lib.ssm_selective_scan_fwd(
-            Bt, L, d, N, _DTYPE_CODE[u.dtype], _DTYPE_CODE[out_dtype], _flags(delta_softplus, zoh),
-            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-            _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), ws_size, _stream_handle(stream, dev))
-    _check("ssm_selective_scan_fwd", st)
+        if checkpoints is None:
+            st = lib.ssm_selective_scan_fwd(
+                Bt, L, d, N, _DTYPE_CODE[u.dtype], _DTYPE_CODE[out_dtype], _flags(delta_softplus, zoh),
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), ws_size, _stream_handle(stream, dev))
+        else:
+            ck_bytes = int(lib.ssm_scan_checkpoint_bytes(Bt, L, d, N))
+            if checkpoints is True:
+                checkpoints = torch.empty(max(ck_bytes // 4, 1), dtype=torch.float32, device=dev)
+            _check_checkpoints(checkpoints, ck_bytes, dev)
+            st = lib.ssm_selective_scan_fwd_ckpt(
+                Bt, L, d, N, _DTYPE_CODE[u.dtype], _DTYPE_CODE[out_dtype], _flags(delta_softplus, zoh),
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                _ptr(h0), _ptr(y), _ptr(h_final), _ptr(checkpoints), _ptr(workspace), ws_size,
+                _stream_handle(stream, dev))
+    _check("ssm_selective_scan_fwd" + ("" if checkpoints is None else "_ckpt"), st)
+    if checkpoints is not None:
+        return y, h_final, checkpoints
     if return_final_state or h_final is not None:
         return y, h_final
     return y
@@ -375,18 +398,31 @@ def ssm_causal_conv1d_update(state, x, weight, bias=None, silu_activation=True, 
     return y
 
 
+def ssm_scan_checkpoint_bytes(batch, seqlen, dim, dstate) -> int:
+    return int(_load().ssm_scan_checkpoint_bytes(batch, seqlen, dim, dstate))
+
+
+def _check_checkpoints(ck, need, dev):
+    if not isinstance(ck, torch.Tensor) or ck.dtype != torch.float32 or ck.device != dev or not ck.is_contiguous():
+        raise ValueError("checkpoints must be a contiguous float32 tensor on the inputs' device")
+    if ck.numel() * 4 < need:
+        raise ValueError(f"checkpoints hold {ck.numel() * 4} bytes, {need} needed")
+
+
 def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate) -> int:
     return int(_load().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate))
 
 
 def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False,
-                           h0=None, dh_final=None, workspace=None, stream=None, zoh=False):
+                           h0=None, dh_final=None, workspace=None, stream=None, zoh=False, checkpoints=None):
     """Gradients of the selective scan; see ssm_selective_scan_bwd in include/ssm_scan.h.
 
     Inputs as ssm_selective_scan_fwd, plus dy [B, L, d] and dh_final [B, d, N]
     (float32). Returns a dict of float32 tensors: du, ddelta, dA, dB, dC, dh0,
     and dD / dz / ddelta_bias when D / z / delta_bias are given. ``zoh``: the
     gradients of the exact zero-order-hold forward (SSM_FLAG_ZOH).
+    ``checkpoints``: the tensor ssm_selective_scan_fwd(..., checkpoints=...)
+    filled for the same inputs and h0: calls ssm_selective_scan_bwd_ckpt.
     """
     lib = _load()
     if not isinstance(u, torch.Tensor) or u.dim() != 3 or u.dtype not in _DTYPE_CODE:
@@ -423,13 +459,17 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=Non
         if workspace is None and ws_bytes > 0:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         ws_size = _check_workspace(workspace, dev)
-        st = lib.ssm_selective_scan_bwd(
-            Bt, L, d, N, _DTYPE_CODE[u.dtype], _flags(delta_softplus, zoh),
-            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0),
-            _ptr(dy), _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
-            _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g["dh0"]),
-            _ptr(workspace), ws_size, _stream_handle(stream, dev))
-    _check("ssm_selective_scan_bwd", st)
+        args = [Bt, L, d, N, _DTYPE_CODE[u.dtype], _flags(delta_softplus, zoh),
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0),
+                _ptr(dy), _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g["dh0"])]
+        if checkpoints is None:
+            st = lib.ssm_selective_scan_bwd(*args, _ptr(workspace), ws_size, _stream_handle(stream, dev))
+        else:
+            _check_checkpoints(checkpoints, int(lib.ssm_scan_checkpoint_bytes(Bt, L, d, N)), dev)
+            st = lib.ssm_selective_scan_bwd_ckpt(*args, _ptr(checkpoints), _ptr(workspace), ws_size,
+                                                 _stream_handle(stream, dev))
+    _check("ssm_selective_scan_bwd" + ("" if checkpoints is None else "_ckpt"), st)
     return g
 
 

@@ -11,6 +11,7 @@ namespace {
 
 constexpr int64_t kMaxScanState = ssm::kMaxScanStates;
 constexpr int64_t kMaxDecodeState = 256;
+constexpr int64_t kMaxCkptState = 16;  // forward checkpoints: the backward's tiles match the scan's
 constexpr int64_t kMaxElems = int64_t(1) << 52;
 constexpr int64_t kMaxConvWidth = 8;
 constexpr int64_t kMaxConvSeq = int64_t(65535) * 64;  // 65535 segments of 64 steps
@@ -88,9 +89,14 @@ namespace {
 int scan_fwd_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int in_dtype, int out_dtype,
                    int flags, const void* u, const void* delta, const float* A, const void* B, const void* C,
                    const float* D, const void* z, const float* delta_bias, const float* h0, void* y,
-                   float* h_final, void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
+                   float* h_final, void* workspace, size_t workspace_bytes, void* stream, bool noalloc,
+                   bool want_ckpt = false, float* ckpt = nullptr) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
   if (dstate > kMaxScanState) return SSM_E_UNSUPPORTED;
+  // checkpoints for the backward: its sizes and N <= 16
+  if (want_ckpt && (dstate > kMaxCkptState || !ssm::plan_scan_bwd(batch, seqlen, dim, dstate).ok)) {
+    return SSM_E_UNSUPPORTED;
+  }
   if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return SSM_E_DTYPE;
   if ((flags & ~(SSM_FLAG_SOFTPLUS | SSM_FLAG_ZOH)) != 0) return SSM_E_UNSUPPORTED;
   int64_t bl, bld, bln, bdn, dn;
@@ -149,6 +155,15 @@ int scan_fwd_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
     if (overlaps(rws, r)) return SSM_E_ALIAS;
   }
   if (overlaps(rws, ry) || overlaps(rws, rhf)) return SSM_E_ALIAS;
+  if (want_ckpt && seqlen > 0) {
+    if (ckpt == nullptr) return SSM_E_NULLPTR;
+    if (!aligned(ckpt, 4)) return SSM_E_ALIGN;
+    const Range rck = span(ckpt, static_cast<int64_t>(ssm::scan_checkpoint_bytes(batch, seqlen, dim, dstate)), 1);
+    for (const Range& r : inputs) {
+      if (overlaps(rck, r)) return SSM_E_ALIAS;
+    }
+    if (overlaps(rck, ry) || overlaps(rck, rhf) || overlaps(rck, rws)) return SSM_E_ALIAS;
+  }
 
   ssm::ScanArgs a;
   a.u = u;
@@ -172,6 +187,7 @@ int scan_fwd_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
   a.delta_softplus = (flags & SSM_FLAG_SOFTPLUS) != 0;
   a.zoh = (flags & SSM_FLAG_ZOH) != 0;
   a.allow_split = allow_split ? 1 : 0;
+  a.ckpt = (want_ckpt && seqlen > 0) ? ckpt : nullptr;
   return map_hip(noalloc ? ssm::launch_scan_noalloc(a, stream) : ssm::launch_scan(a, stream));
 }
 
@@ -198,6 +214,24 @@ int ssm_selective_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, i
                                    void* y, float* h_final, void* stream) {
   return scan_fwd_entry(batch, seqlen, dim, dstate, in_dtype, out_dtype, flags, u, delta, A, B, C, D, z,
                         delta_bias, h0, y, h_final, nullptr, 0, stream, true);
+}
+
+size_t ssm_scan_checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > kMaxCkptState) return 0;
+  int64_t t;
+  if (!safe_mul(batch, seqlen, &t) || !safe_mul(t, dim, &t) || !safe_mul(t, dstate, &t)) return 0;
+  return ssm::scan_checkpoint_bytes(batch, seqlen, dim, dstate);
+}
+
+int ssm_selective_scan_fwd_ckpt(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                int in_dtype, int out_dtype, int flags,
+                                const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, const float* h0,
+                                void* y, float* h_final, float* checkpoints,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_fwd_entry(batch, seqlen, dim, dstate, in_dtype, out_dtype, flags, u, delta, A, B, C, D, z,
+                        delta_bias, h0, y, h_final, workspace, workspace_bytes, stream, false, true, checkpoints);
 }
 
 int ssm_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
@@ -268,16 +302,21 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
   return p.ok ? p.bytes : 0;
 }
 
-int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                           int in_dtype, int flags,
-                           const void* u, const void* delta, const float* A,
-                           const void* B, const void* C, const float* D, const void* z,
-                           const float* delta_bias, const float* h0,
-                           const float* dy, const float* dh_final,
-                           float* du, float* ddelta, float* dA, float* dB, float* dC,
-                           float* dD, float* dz, float* ddelta_bias, float* dh0,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch of the scan backward; with `want_ckpt` the states
+// at the tile starts come from `ckpt` (written by the forward with
+// checkpoints) instead of the checkpoint pass.
+int scan_bwd_entry(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int in_dtype, int flags,
+                   const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                   const void* z, const float* delta_bias, const float* h0, const float* dy,
+                   const float* dh_final, float* du, float* ddelta, float* dA, float* dB, float* dC, float* dD,
+                   float* dz, float* ddelta_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                   void* stream, bool want_ckpt, const float* ckpt) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return SSM_E_SHAPE;
+  if (want_ckpt && dstate > kMaxCkptState) return SSM_E_UNSUPPORTED;
   if (in_dtype != 0 && in_dtype != 1) return SSM_E_DTYPE;
   if ((flags & ~(SSM_FLAG_SOFTPLUS | SSM_FLAG_ZOH)) != 0) return SSM_E_UNSUPPORTED;
   int64_t bl, bld, bln, bdn, dn, bldn;
@@ -304,10 +343,15 @@ int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   }
   const size_t need = plan.bytes;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SSM_E_WORKSPACE;
+  const bool use_ckpt = want_ckpt && bl > 0;
+  if (use_ckpt && ckpt == nullptr) return SSM_E_NULLPTR;
+  if (use_ckpt && !aligned(ckpt, 4)) return SSM_E_ALIGN;
+  const int64_t ck_bytes = use_ckpt ? static_cast<int64_t>(ssm::scan_checkpoint_bytes(batch, seqlen, dim, dstate)) : 0;
   const int64_t isz = in_dtype == 1 ? 2 : 4;
   const Range inputs[] = {span(u, bld, isz), span(delta, bld, isz), span(z, bld, isz), span(B, bln, isz),
                           span(C, bln, isz), span(A, dn, 4), span(D, dim, 4), span(delta_bias, dim, 4),
-                          span(h0, bdn, 4), span(dy, bld, 4), span(dh_final, bdn, 4)};
+                          span(h0, bdn, 4), span(dy, bld, 4), span(dh_final, bdn, 4),
+                          span(use_ckpt ? ckpt : nullptr, ck_bytes, 1)};
   const Range outputs[] = {span(du, bld, 4), span(ddelta, bld, 4), span(dA, dn, 4), span(dB, bln, 4),
                            span(dC, bln, 4), span(D ? dD : nullptr, dim, 4), span(z ? dz : nullptr, bld, 4),
                            span(delta_bias ? ddelta_bias : nullptr, dim, 4), span(dh0, bdn, 4),
@@ -351,7 +395,41 @@ int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   a.in_bf16 = in_dtype;
   a.delta_softplus = (flags & SSM_FLAG_SOFTPLUS) != 0;
   a.zoh = (flags & SSM_FLAG_ZOH) != 0;
+  a.ckpt_in = use_ckpt ? ckpt : nullptr;
   return map_hip(ssm::launch_scan_bwd(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_selective_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                           int in_dtype, int flags,
+                           const void* u, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, const float* h0,
+                           const float* dy, const float* dh_final,
+                           float* du, float* ddelta, float* dA, float* dB, float* dC,
+                           float* dD, float* dz, float* ddelta_bias, float* dh0,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_bwd_entry(batch, seqlen, dim, dstate, in_dtype, flags, u, delta, A, B, C, D, z, delta_bias, h0, dy,
+                        dh_final, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, workspace, workspace_bytes,
+                        stream, false, nullptr);
+}
+
+int ssm_selective_scan_bwd_ckpt(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                int in_dtype, int flags,
+                                const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, const float* h0,
+                                const float* dy, const float* dh_final,
+                                float* du, float* ddelta, float* dA, float* dB, float* dC,
+                                float* dD, float* dz, float* ddelta_bias, float* dh0,
+                                const float* checkpoints,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_bwd_entry(batch, seqlen, dim, dstate, in_dtype, flags, u, delta, A, B, C, D, z, delta_bias, h0, dy,
+                        dh_final, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, workspace, workspace_bytes,
+                        stream, true, checkpoints);
 }
 
 int ssm_causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,

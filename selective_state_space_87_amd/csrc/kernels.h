@@ -23,6 +23,7 @@ struct ScanArgs {
   int64_t batch, seqlen, dim, dstate;
   int in_bf16, out_bf16, delta_softplus, zoh;
   int allow_split;  // the plan may split a channel's states over blocks (see ScanPlan)
+  float* ckpt;      // or null: also write the backward's state checkpoints (N <= 16)
 };
 
 struct UpdateArgs {
@@ -64,6 +65,7 @@ struct ScanBwdArgs {
   void* workspace;
   int64_t batch, seqlen, dim, dstate;
   int in_bf16, delta_softplus, zoh;
+  const float* ckpt_in;  // or null: state checkpoints written by the forward (else recomputed)
 };
 
 struct ConvArgs {
@@ -176,6 +178,10 @@ struct ScanBwdPlan {
   size_t off_bc, off_ckpt, off_dbp, off_dcp, off_dap, off_ddp, off_dbiasp, bytes;
 };
 ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+// Bytes of the backward's state checkpoints [B][Lp / T][NS][d] float32 (T =
+// bwd_tile_steps(NS)), as the forward with checkpoints writes them; 0 where
+// the backward does not run (its plan) or N > 16.
+size_t scan_checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
 // Workspace bytes the scan needs for this shape.
 size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);

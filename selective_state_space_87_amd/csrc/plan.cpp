@@ -126,6 +126,12 @@ ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
   return p;
 }
 
+size_t scan_checkpoint_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  const ScanBwdPlan p = plan_scan_bwd(batch, seqlen, dim, dstate);
+  if (!p.ok || p.NS > 16) return 0;
+  return size_t(batch) * size_t(p.Lp / bwd_tile_steps(p.NS)) * size_t(p.NS) * size_t(dim) * 4;
+}
+
 size_t scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   const ScanPlan p = plan_scan(batch, seqlen, dim, dstate);
   return p.ok ? p.bytes : 0;

@@ -691,7 +691,7 @@ int launch_scan_bwd(const ScanBwdArgs& a, void* stream) {
     f.in_bf16 = a.in_bf16;
     f.delta_softplus = a.delta_softplus;
     f.zoh = a.zoh;
-    if (pl.Lp > 0) {
+    if (pl.Lp > 0 && a.ckpt_in == nullptr) {
       err = launch_scan_checkpoints(f, reinterpret_cast<const uint32_t*>(ws + pl.off_bc),
                                     reinterpret_cast<float*>(ws + pl.off_ckpt), st);
       if (err != 0) return err;
@@ -712,7 +712,7 @@ int launch_scan_bwd(const ScanBwdArgs& a, void* stream) {
   s.ddelta = a.ddelta;
   s.dz = a.dz;
   s.dh0 = a.dh0;
-  s.ckpt = reinterpret_cast<float*>(ws + pl.off_ckpt);
+  s.ckpt = a.ckpt_in ? const_cast<float*>(a.ckpt_in) : reinterpret_cast<float*>(ws + pl.off_ckpt);
   s.dBp = reinterpret_cast<float*>(ws + pl.off_dbp);
   s.dCp = reinterpret_cast<float*>(ws + pl.off_dcp);
   s.dAp = reinterpret_cast<float*>(ws + pl.off_dap);

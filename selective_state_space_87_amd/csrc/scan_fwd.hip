@@ -136,6 +136,16 @@ int launch_scan(const ScanArgs& a, void* stream) {
   s.chunk = static_cast<int>(pl.chunk);
   s.batch = static_cast<int>(a.batch);
   s.y_split = 0;
+  s.ckpt = nullptr;
+  s.ckpt_tiles = 0;
+  // Checkpoints for the backward (N <= 16): a single-pass scan writes them
+  // itself; a chunked one is followed by the checkpoint pass.
+  const bool ckpt_in_scan = a.ckpt != nullptr && pl.chunks == 1;
+  if (ckpt_in_scan) {
+    s.ckpt = a.ckpt;
+    s.ckpt_tiles = static_cast<int>(pl.Lp / bwd_tile_steps(pl.NS));
+  }
+  if (a.ckpt != nullptr && (pl.NS > 16 || pl.splits > 1)) return hipErrorInvalidValue;
   if (pl.splits > 1) {
     // Each block runs half of the padded states of its channels (64 of 128,
     // or 32 of 64) and writes their partial readout (float32, without the
@@ -159,6 +169,11 @@ int launch_scan(const ScanArgs& a, void* stream) {
   if (!bcl) {
     const int err = launch_bc_pack(a.B, a.C, reinterpret_cast<uint32_t*>(ws + pl.off_bc), a.batch, a.seqlen,
                                    pl.Lp, static_cast<int>(a.dstate), pl.NS, a.in_bf16 != 0, st);
+    if (err != 0) return err;
+  }
+  if (a.ckpt != nullptr && !ckpt_in_scan && pl.Lp > 0) {
+    // before the scan, which may overwrite h0 with h_final
+    const int err = launch_scan_checkpoints(a, reinterpret_cast<const uint32_t*>(ws + pl.off_bc), a.ckpt, st);
     if (err != 0) return err;
   }
   if (a.in_bf16) return a.out_bf16 ? launch_scan_bb(a, pl, s, st) : launch_scan_bf(a, pl, s, st);

@@ -69,6 +69,8 @@ struct Scan {
   float* ssum;         // summary pass: chunk c's sum of step sizes, [chunks-1][B][d]
   int L, Lp, dim, N, chunk, batch;
   int64_t y_split;     // states split over blocks: elements between partial planes (else 0)
+  float* ckpt;         // full scan with checkpoints: states at every tile start, [B][ckpt_tiles][NS][d]
+  int ckpt_tiles;
 };
 
 // Per (input, output) dtype: launch the scan (and, for float32 output, the
@@ -113,7 +115,9 @@ constexpr bool bc_in_lds(int NS) { return NS >= 64; }
 // exporting its final state and the sum of its step sizes. kCheckpoint: the
 // recurrence from h0 only, storing every wave's states at each tile start
 // (for the backward pass, which recomputes each tile from them).
-constexpr int kFull = 0, kSummary = 1, kCheckpoint = 2;
+// kFullCkpt: kFull that also stores those checkpoints (single pass, N <= 16),
+// so that a training step's backward need not recompute them.
+constexpr int kFull = 0, kSummary = 1, kCheckpoint = 2, kFullCkpt = 3;
 
 template <int S, int W, int T, bool BF16_IN, bool BF16_OUT, bool SOFTPLUS, bool ZOH, int MODE, bool PAIR = true,
           bool FORCE_BCL = false>
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   // fewer steps than waves (the backward's checkpoint pass at N = 32, 64, the
   // summary pass from N = 64 on) waves w >= T have none.
   constexpr int IT = T >= W ? T / W : 1;
-  static_assert(T % W == 0 || (MODE != kFull && W % T == 0),
+  static_assert(T % W == 0 || (MODE != kFull && MODE != kFullCkpt && W % T == 0),
                 "tile must split evenly over the waves (or the waves over the tile, without readout)");
   const bool has_item = T >= W || threadIdx.x < 64 * T;  // (wave-uniform: w < T)
   constexpr int LW = __builtin_ctz(W);
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
   constexpr int LNC = __builtin_ctz(NC);
   constexpr int WPS = BF16_IN ? 1 : 2;              // packed B/C words per step
   constexpr uint32_t IN_B = BF16_IN ? 2 : 4, OUT_B = BF16_OUT ? 2 : 4;
-  constexpr bool READOUT = MODE == kFull;
+  constexpr bool READOUT = MODE == kFull || MODE == kFullCkpt;
   constexpr bool SUMMARY = MODE == kSummary;
   constexpr bool BCL = FORCE_BCL || bc_in_lds(NS);  // forced for the 32-state halves of a split 64
   constexpr int NT = W * 64;                        // threads
@@ -496,6 +500,15 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     constexpr int P = J & 1;
     constexpr int Q = 1 - P;
     float gp[IT][GN][GW];
+    if constexpr (MODE == kFullCkpt) {
+      // as the checkpoint pass below, into the caller's checkpoint array
+      const rsrc_t rck = raw_buffer(p.ckpt + ((static_cast<int64_t>(b) * p.ckpt_tiles + k) * NS + w * S) * Dm,
+                                    static_cast<uint32_t>(S * Dm * 4));
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        buffer_store_f32<false>(h[s], rck, ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kLaneOut);
+      }
+    }
     if constexpr (MODE == kCheckpoint) {
       // Branch-free through a descriptor over this wave's rows of tile k
       // (lanes beyond d are dropped by the buffer unit): a branch here would
@@ -721,6 +734,15 @@ int launch_sw(const ScanArgs& a, const ScanPlan& pl, const Scan& s, hipStream_t 
   const void* full = pl.chunks > 1
                          ? reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, false, FBCL>)
                          : reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFull, true, FBCL>);
+  if (s.ckpt != nullptr) {
+    // checkpoints from the scan itself: single pass, N <= 16 (the backward's tiles)
+    if constexpr (S * W <= 16 && !FBCL) {
+      if (pl.chunks != 1 || pl.splits != 1) return hipErrorInvalidValue;
+      full = reinterpret_cast<const void*>(&scan_fwd_kernel<S, W, T, BI, BO, SP, ZH, kFullCkpt, true>);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   return hipLaunchKernel(full, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(pl.chunks),
                                     static_cast<unsigned>(pl.splits)),
                          dim3(W * 64), kargs, 0, st);

@@ -259,6 +259,47 @@ def test_scan_bwd_validation(lib):
     assert lib.ssm_scan_bwd_workspace_bytes(1, 8, 4, 64) > lib.ssm_scan_bwd_workspace_bytes(1, 8, 4, 17) > 0
 
 
+def test_checkpoint_entries_validation(lib):
+    """ssm_scan_checkpoint_bytes, ssm_selective_scan_fwd_ckpt and
+    ssm_selective_scan_bwd_ckpt: sizes, N <= 16, pointers and overlaps."""
+    ck = lib.ssm_scan_checkpoint_bytes
+    assert ck(4, 8192, 4096, 16) == 4 * (8192 // 8) * 16 * 4096 * 4
+    assert ck(2, 100, 64, 5) == 2 * (112 // 16) * 8 * 64 * 4
+    assert ck(1, 8, 4, 17) == 0 and ck(1, 8, 4, 0) == 0 and ck(-1, 8, 4, 4) == 0
+    assert ck(1, 1 << 23, 64, 16) == 0            # rows too long for the backward
+
+    def fwdck(B=2, L=8, d=4, N=4, ckp=30 * P, **kw):
+        a = dict(u=P, delta=2 * P, A=3 * P, Bm=4 * P, Cm=5 * P, D=6 * P, z=7 * P, bias=8 * P, h0=9 * P, y=10 * P,
+                 hf=11 * P)
+        a.update(kw)
+        order = ("u", "delta", "A", "Bm", "Cm", "D", "z", "bias", "h0", "y", "hf")
+        return lib.ssm_selective_scan_fwd_ckpt(B, L, d, N, 0, 0, 1, *[vp(a[k]) for k in order], vp(ckp), vp(20 * P),
+                                               1 << 20, None)
+
+    assert fwdck(ckp=None) == E_NULLPTR
+    assert fwdck(N=17) == E_UNSUPPORTED
+    assert fwdck(ckp=30 * P + 2) == E_ALIGN
+    assert fwdck(ckp=P) == E_ALIAS                  # over u
+    assert fwdck(ckp=10 * P) == E_ALIAS             # over y
+    assert fwdck(ckp=20 * P) == E_ALIAS             # over the workspace
+    assert fwdck(B=0) == OK
+
+    def bwdck(ckp=30 * P, N=4, **kw):
+        ptrs = dict(u=P, delta=2 * P, A=3 * P, Bm=4 * P, Cm=5 * P, D=6 * P, z=7 * P, bias=8 * P, h0=9 * P,
+                    dy=10 * P, dhf=11 * P, du=12 * P, ddelta=13 * P, dA=14 * P, dB=15 * P, dC=16 * P, dD=17 * P,
+                    dz=18 * P, dbias=19 * P, dh0=20 * P)
+        ptrs.update(kw)
+        order = ("u", "delta", "A", "Bm", "Cm", "D", "z", "bias", "h0", "dy", "dhf", "du", "ddelta", "dA", "dB",
+                 "dC", "dD", "dz", "dbias", "dh0")
+        return lib.ssm_selective_scan_bwd_ckpt(2, 8, 4, N, 0, 1, *[vp(ptrs[k]) for k in order], vp(ckp),
+                                               vp(40 * P), 1 << 24, None)
+
+    assert bwdck(ckp=None) == E_NULLPTR
+    assert bwdck(N=32) == E_UNSUPPORTED
+    assert bwdck(ckp=30 * P + 1) == E_ALIGN
+    assert bwdck(du=30 * P) == E_ALIAS              # an output over the checkpoints
+
+
 def test_scan_bwd_refuses_long_rows_of_few_channels(lib):
     """Long sequences over few channels pass the per-row [L, d] plane limit
     but not the 32-bit offsets of a row's packed B/C words (up to 8 bytes per

@@ -200,3 +200,54 @@ def test_bwd_zoh_differs_from_default():
     gz = run_bwd(inp, dy, dhf, h0=h0, zoh=True)
     gd = run_bwd(inp, dy, dhf, h0=h0)
     assert (gz["dB"] - gd["dB"]).abs().max().item() > 1e-2
+
+
+# A training step that keeps the forward's states: ssm_selective_scan_fwd_ckpt
+# writes the backward's checkpoints (from the scan itself in a single pass, or
+# by a recurrence pass before a chunked scan), ssm_selective_scan_bwd_ckpt
+# takes them instead of recomputing them. Both are bitwise equal to the plain
+# entry points, whose parity with the oracle the tests above establish.
+CKPT_SHAPES = [(2, 300, 96, 16, "bf16", False), (1, 257, 70, 5, "f32", True), (2, 130, 64, 1, "f32", False),
+               (1, 4100, 64, 16, "bf16", False), (3, 64, 200, 12, "bf16", True)]
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+@pytest.mark.parametrize("B,L,d,N,dt,zoh", CKPT_SHAPES)
+def test_checkpoints_from_forward(B, L, d, N, dt, zoh):
+    inp = synth.make_scan_inputs(B, L, d, N, dt, seed=12, stream=6000 + N)
+    dy, dhf, _ = grads_in(B, L, d, N, 13)
+    h0 = np.random.default_rng(N + 3).standard_normal((B, d, N)).astype(np.float32) * 0.5
+    dev = scan_inputs_to_device(inp)
+    kw = dict(D=dev["D"], z=dev["z"], delta_bias=dev["delta_bias"], delta_softplus=True, zoh=zoh)
+    chunked = binding.ssm_scan_chunks(B, L, d, N) > 1
+    y0, hf0 = binding.ssm_selective_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"],
+                                             h0=upload(h0, "f32"), return_final_state=True, **kw)
+    # in place (h_final over h0): the checkpoints still start from the given h0
+    hs = upload(h0, "f32")
+    y1, hf1, ck = binding.ssm_selective_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], h0=hs,
+                                                 h_final=hs, checkpoints=True, **kw)
+    gk = dict(D=dev["D"], z=dev["z"], delta_bias=dev["delta_bias"], delta_softplus=True, zoh=zoh,
+              h0=upload(h0, "f32"), dh_final=upload(dhf, "f32"))
+    g0 = binding.ssm_selective_scan_bwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], upload(dy, "f32"),
+                                        **gk)
+    g1 = binding.ssm_selective_scan_bwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], upload(dy, "f32"),
+                                        checkpoints=ck, **gk)
+    torch.cuda.synchronize()
+    print(f"[ckpt] {(B, L, d, N)} {dt} zoh={zoh} chunked forward={chunked}: "
+          f"{ck.numel() * 4} checkpoint bytes", flush=True)
+    assert ck.numel() * 4 >= binding.ssm_scan_checkpoint_bytes(B, L, d, N) > 0
+    assert torch.equal(_bits(y0), _bits(y1)) and torch.equal(_bits(hf0), _bits(hf1))
+    for k in g0:
+        assert torch.equal(_bits(g0[k]), _bits(g1[k])), k
+
+
+def test_checkpoints_refused_beyond_16_states():
+    inp = synth.make_scan_inputs(1, 40, 64, 32, "f32", seed=14, stream=6100)
+    dev = scan_inputs_to_device(inp)
+    assert binding.ssm_scan_checkpoint_bytes(1, 40, 64, 32) == 0
+    with pytest.raises(binding.SSMError) as e:
+        binding.ssm_selective_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], checkpoints=True)
+    assert e.value.status == 7  # SSM_E_UNSUPPORTED
