@@ -60,7 +60,9 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+/* 2: the workspace must be 16-byte aligned; the forward with checkpoints and
+ * the backward from them were added. */
+#define SSM_ABI_VERSION 2
 
 /* Status codes. */
 #define SSM_OK 0

@@ -139,7 +139,7 @@ int launch_scan(const ScanArgs& a, void* stream) {
   s.ckpt = nullptr;
   s.ckpt_tiles = 0;
   // Checkpoints for the backward (N <= 16): a single-pass scan writes them
-  // itself; a chunked one is followed by the checkpoint pass.
+  // itself; a chunked one is preceded by the checkpoint pass.
   const bool ckpt_in_scan = a.ckpt != nullptr && pl.chunks == 1;
   if (ckpt_in_scan) {
     s.ckpt = a.ckpt;
