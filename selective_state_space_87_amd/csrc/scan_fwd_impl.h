@@ -501,12 +501,14 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
     constexpr int Q = 1 - P;
     float gp[IT][GN][GW];
     if constexpr (MODE == kFullCkpt) {
-      // as the checkpoint pass below, into the caller's checkpoint array
+      // as the checkpoint pass below, into the caller's checkpoint array,
+      // non-temporal (the backward reads them back long after)
       const rsrc_t rck = raw_buffer(p.ckpt + ((static_cast<int64_t>(b) * p.ckpt_tiles + k) * NS + w * S) * Dm,
                                     static_cast<uint32_t>(S * Dm * 4));
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        buffer_store_f32<false>(h[s], rck, ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kLaneOut);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h[s]), rck,
+                                              ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kLaneOut, 0, 2);
       }
     }
     if constexpr (MODE == kCheckpoint) {
