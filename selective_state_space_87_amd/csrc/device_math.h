@@ -134,21 +134,25 @@ __device__ __forceinline__ rsrc_t raw_buffer(const void* base, uint32_t bytes) {
 template <bool BF16>
 using storage_t = std::conditional_t<BF16, uint16_t, uint32_t>;
 
-template <bool BF16>
+// Cache policy of a buffer access: 0, or kNonTemporal for streams read or
+// written once (the nt bit).
+constexpr int kNonTemporal = 2;
+
+template <bool BF16, int AUX = 0>
 __device__ __forceinline__ storage_t<BF16> buffer_load_bits(rsrc_t r, uint32_t off) {
   if constexpr (BF16) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
   } else {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
   }
 }
 
-template <bool BF16>
+template <bool BF16, int AUX = 0>
 __device__ __forceinline__ void buffer_store_f32(float v, rsrc_t r, uint32_t off) {
   if constexpr (BF16) {
-    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r, off, 0, AUX);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, AUX);
   }
 }
 

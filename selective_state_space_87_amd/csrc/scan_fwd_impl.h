@@ -275,9 +275,9 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const uint32_t off = lane_in + step_off(k, i, IN_B);
-      ru[R][i] = buffer_load_bits<BF16_IN>(ru_b, off);
-      rd[R][i] = buffer_load_bits<BF16_IN>(rd_b, off);
-      if constexpr (READOUT) rz[R][i] = buffer_load_bits<BF16_IN>(rz_b, off);
+      ru[R][i] = buffer_load_bits<BF16_IN, kNonTemporal>(ru_b, off);
+      rd[R][i] = buffer_load_bits<BF16_IN, kNonTemporal>(rd_b, off);
+      if constexpr (READOUT) rz[R][i] = buffer_load_bits<BF16_IN, kNonTemporal>(rz_b, off);
     }
     if constexpr (BCL) {
       // Tile k's rows of B and C: T*N contiguous elements from step t0 + k*T,
@@ -476,8 +476,8 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
       if constexpr (P == 1) {
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
-          buffer_store_f32<BF16_OUT>(yv[0][i], ry_b, yo[0][i]);
-          buffer_store_f32<BF16_OUT>(yv[1][i], ry_b, yo[1][i]);
+          buffer_store_f32<BF16_OUT, kNonTemporal>(yv[0][i], ry_b, yo[0][i]);
+          buffer_store_f32<BF16_OUT, kNonTemporal>(yv[1][i], ry_b, yo[1][i]);
         }
       }
     }
