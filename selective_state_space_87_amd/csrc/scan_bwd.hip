@@ -221,10 +221,10 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
       const bool live = T >= W || item_step(i) < T;
       const int t = live ? k * T + item_step(i) : -1;
       const uint32_t off = item_off(t, EB);
-      r_u[i] = buffer_load_bits<BF16_IN>(ru_b, off);
-      r_d[i] = buffer_load_bits<BF16_IN>(rd_b, off);
-      r_z[i] = buffer_load_bits<BF16_IN>(rz_b, off);
-      r_dy[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdy_b, item_off(t, 4), 0, 0));
+      r_u[i] = buffer_load_bits<BF16_IN, kNonTemporal>(ru_b, off);
+      r_d[i] = buffer_load_bits<BF16_IN, kNonTemporal>(rd_b, off);
+      r_z[i] = buffer_load_bits<BF16_IN, kNonTemporal>(rz_b, off);
+      r_dy[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdy_b, item_off(t, 4), 0, kNonTemporal));
     }
 #pragma unroll
     for (int j = 0; j < BCW; ++j) {
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       r_ck[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rck, ch_ok && k >= 0 ? static_cast<uint32_t>((s * Dm + ch) * 4) : kOutOfRange, 0, 0));
+          rck, ch_ok && k >= 0 ? static_cast<uint32_t>((s * Dm + ch) * 4) : kOutOfRange, 0, kNonTemporal));
     }
   };
   const rsrc_t rdu_b = raw_buffer(p.du + plane * Dm, f_bytes);
@@ -463,10 +463,10 @@ __global__ __launch_bounds__(W * 64) void scan_bwd_kernel(const ScanBwd p) {
         const bool ok = live && ch_ok && t < L;
         const uint32_t off = ok ? static_cast<uint32_t>((t * Dm + ch) * 4) : kOutOfRange;
         pre = fmaf(Dv, e_u[i], pre);
-        buffer_store_f32<false>(e_dy[i] * pre * e_dsilu[i], rdz_b, off);
+        buffer_store_f32<false, kNonTemporal>(e_dy[i] * pre * e_dsilu[i], rdz_b, off);
         const float dd = ddt * e_dsp[i];
-        buffer_store_f32<false>(dd, rdd_b, off);
-        buffer_store_f32<false>(fmaf(e_dp[i], Dv, dus), rdu_b, off);
+        buffer_store_f32<false, kNonTemporal>(dd, rdd_b, off);
+        buffer_store_f32<false, kNonTemporal>(fmaf(e_dp[i], Dv, dus), rdu_b, off);
         dD_acc = fmaf(ok ? e_dp[i] : 0.0f, e_u[i], dD_acc);
         dbias_acc += ok ? dd : 0.0f;
       }

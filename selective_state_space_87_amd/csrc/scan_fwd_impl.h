@@ -507,8 +507,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
                                     static_cast<uint32_t>(S * Dm * 4));
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h[s]), rck,
-                                              ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kLaneOut, 0, 2);
+        buffer_store_f32<false, kNonTemporal>(h[s], rck, ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kLaneOut);
       }
     }
     if constexpr (MODE == kCheckpoint) {
@@ -519,7 +518,7 @@ __global__ __launch_bounds__(W * 64) void scan_fwd_kernel(const Scan p) {
                                     static_cast<uint32_t>(S * Dm * 4));
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        buffer_store_f32<false>(h[s], rck, ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kLaneOut);
+        buffer_store_f32<false, kNonTemporal>(h[s], rck, ch_ok ? static_cast<uint32_t>((s * Dm + ch) * 4) : kLaneOut);
       }
     }
     if constexpr (decltype(late)::value) {
