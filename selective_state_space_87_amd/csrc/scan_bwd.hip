@@ -584,11 +584,28 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   const int64_t bt = i / N;
   const int t = static_cast<int>(bt % L);
   const int b = static_cast<int>(bt / L);
+  // Sums in block order; eight blocks' partials are loaded (non-temporal:
+  // each is read once) before they are added, so the loads overlap.
   float sb = 0.0f, sc = 0.0f;
-  for (int k = 0; k < blocks_d; ++k) {
-    const int64_t o = ((static_cast<int64_t>(k) * batch + b) * Lp + t) * NS + n;
-    sb += dBp[o];
-    sc += dCp[o];
+  const int64_t stride = static_cast<int64_t>(batch) * Lp * NS;  // one block's partials
+  const int64_t base = (static_cast<int64_t>(b) * Lp + t) * NS + n;
+  int k = 0;
+  for (; k + 8 <= blocks_d; k += 8) {
+    float xb[8], xc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xb[j] = __builtin_nontemporal_load(dBp + (k + j) * stride + base);
+      xc[j] = __builtin_nontemporal_load(dCp + (k + j) * stride + base);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sb += xb[j];
+      sc += xc[j];
+    }
+  }
+  for (; k < blocks_d; ++k) {
+    sb += dBp[k * stride + base];
+    sc += dCp[k * stride + base];
   }
   dB[i] = sb;
   dC[i] = sc;
