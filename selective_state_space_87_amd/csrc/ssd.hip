@@ -97,6 +97,16 @@ struct SsdStage {
   storage_t<BF16_IN> dtr;
 };
 
+// (batch row, head) item of this block. Consecutive block indices go to
+// the eight XCDs in turn, each with its own L2; when the grid is a multiple
+// of eight, block i takes item (i mod 8) * (grid / 8) + i / 8 (a bijection),
+// so every XCD holds a contiguous run of items, the heads of one or two batch
+// rows, and B and C of a batch row are fetched into few L2s.
+__device__ __forceinline__ int block_item() {
+  const unsigned g = gridDim.x, i = blockIdx.x;
+  return static_cast<int>((g & 7u) ? i : (i & 7u) * (g >> 3) + (i >> 3));
+}
+
 template <bool BF16>
 __device__ __forceinline__ void unpack_store(float* dst, u32x4 v) {
   if constexpr (BF16) {
@@ -131,8 +141,9 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(const SsdArgs p) {
   const int w = tid >> 6;
   const int lr = lane & 15, lk = lane >> 4;
   const int H = static_cast<int>(p.nheads), P = static_cast<int>(p.headdim), N = static_cast<int>(p.dstate);
-  const int b = blockIdx.x / H;
-  const int hd = blockIdx.x % H;
+  const int item = block_item();
+  const int b = item / H;
+  const int hd = item % H;
   const int64_t L = p.seqlen;
   const float a2 = p.A[hd] * kLog2e;
   const float bias = p.dt_bias ? p.dt_bias[hd] : 0.0f;
@@ -491,8 +502,9 @@ __global__ __launch_bounds__(64 * WV) void ssd_bf16_kernel(const SsdArgs p) {
   const int w = tid >> 6;
   const int lr = lane & 15, lk = lane >> 4;
   const int H = static_cast<int>(p.nheads), N = static_cast<int>(p.dstate);
-  const int b = blockIdx.x / H;
-  const int hd = blockIdx.x % H;
+  const int item = block_item();
+  const int b = item / H;
+  const int hd = item % H;
   const int64_t L = p.seqlen;
   const float a2 = p.A[hd] * kLog2e;
   const float bias = p.dt_bias ? p.dt_bias[hd] : 0.0f;
