@@ -165,28 +165,19 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// ---- cross-lane moves inside groups of 1, 2 or 4 consecutive lanes (DPP quad_perm)
+// ---- cross-lane moves (DPP): a lane reads another lane's value
 
+// Every control used here (quad permutes, row_ror) reads a valid lane, so
+// bound_ctrl changes no value; it is set because it lets the compiler fold
+// the move into the instruction that consumes it (an add with a DPP source).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
 
-// Value of lane K of this lane's group of G consecutive lanes.
-template <int G, int K>
-__device__ __forceinline__ float group_bcast(float v) {
-  static_assert(G == 1 || G == 2 || G == 4, "group of 1, 2 or 4 lanes");
-  if constexpr (G == 1) {
-    return v;
-  } else if constexpr (G == 2) {
-    return dpp_f<quad_perm(K, K, 2 + K, 2 + K)>(v);
-  } else {
-    return dpp_f<quad_perm(K, K, K, K)>(v);
-  }
-}
-
+// Value of lane (this lane xor MASK) inside its quad.
 template <int MASK>
 __device__ __forceinline__ float quad_xor(float v) {
   static_assert(MASK == 1 || MASK == 2, "xor 1 or 2 inside a quad");
@@ -194,33 +185,6 @@ __device__ __forceinline__ float quad_xor(float v) {
     return dpp_f<quad_perm(1, 0, 3, 2)>(v);
   } else {
     return dpp_f<quad_perm(2, 3, 0, 1)>(v);
-  }
-}
-
-// Transposed reduction over a group of G lanes: on entry lane j of the group
-// holds partial sums p[0..G-1] (one per time step of the group); on exit it
-// returns the group-wide sum of p[j]. Butterfly: at each level a lane keeps
-// the half of its vector whose index bit matches its own lane bit and adds
-// the partner's copy of that half.
-template <int G>
-__device__ __forceinline__ float group_transpose_sum(const float (&p)[G], int j) {
-  if constexpr (G == 1) {
-    return p[0];
-  } else if constexpr (G == 2) {
-    const bool hi = j & 1;
-    const float keep = hi ? p[1] : p[0];
-    const float send = hi ? p[0] : p[1];
-    return keep + quad_xor<1>(send);
-  } else {
-    static_assert(G == 4, "group of 1, 2 or 4 lanes");
-    const bool b1 = j & 2;
-    const float k0 = b1 ? p[2] : p[0], s0 = b1 ? p[0] : p[2];
-    const float k1 = b1 ? p[3] : p[1], s1 = b1 ? p[1] : p[3];
-    const float q0 = k0 + quad_xor<2>(s0);
-    const float q1 = k1 + quad_xor<2>(s1);
-    const bool b0 = j & 1;
-    const float k = b0 ? q1 : q0, s = b0 ? q0 : q1;
-    return k + quad_xor<1>(s);
   }
 }
 
