@@ -68,18 +68,23 @@ struct ScanBwd {
 
 __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
-// Value of lane (this lane xor M), M in {1, 2, 4, 8}, without a trip through
-// LDS addressing: DPP quad permutes for 1 and 2, a row rotate by 8 (which is
-// xor 8 inside a row of 16), and the swizzle unit's xor mode for 4.
+// Value of this lane's partner across lane bit M, M in {1, 2, 4, 8}, by DPP
+// (which the compiler folds into the add that consumes it): quad permutes
+// (lane xor 1, xor 2), a row rotate by 8 (xor 8 inside a row of 16), and for
+// M = 4 the half-row mirror, lane 7 - l inside each group of 8 (l xor 7).
+// The partner differs in bit M in every case, which is all the butterflies
+// below need: a stage adds, for the half a lane keeps, the copy held by a
+// lane of the other half, and the lanes summed at successive stages stay
+// disjoint, so every lane of the group is counted once.
 template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
-  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "xor distance 1, 2, 4 or 8");
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "partner across bit 0, 1, 2 or 3");
   if constexpr (M == 1 || M == 2) {
     return quad_xor<M>(v);
   } else if constexpr (M == 8) {
     return dpp_f<0x128>(v);  // row_ror:8
   } else {
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x101F));
+    return dpp_f<0x141>(v);  // row_half_mirror
   }
 }
 
